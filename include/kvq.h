@@ -1,0 +1,203 @@
+/*
+ * kvq.h -- quantized paged KV cache and decode attention for AMD MI355X (gfx950).
+ *
+ * C ABI.  Plain pointers and sizes only; every call returns a kvq_status and
+ * no C++ exception crosses the boundary.
+ *
+ * What the library computes comes from five web pages on KV-cache
+ * quantization:
+ *  - NInfer KV-cache quantization guide (m.xxqk.cn/news/579065): a paged KV
+ *    cache with 64-token pages and independent K/V encodings; the formats
+ *    BF16, INT8-G64, FP8-E4M3 row-256, NVFP4-G16 and the K8V4 profile, with
+ *    their per-token byte counts at head_dim 256, and the normalized
+ *    256-point Hadamard pre-rotation (section on the five formats); decode
+ *    reads the whole cache every step, so stored bytes set its speed
+ *    (section on why the cache is quantized).
+ *  - TokenSpeed quantization article (gsyq.cn/news/441801), section on the
+ *    --kv-cache-dtype options: fp8_e4m3 with unit scale, mxfp8 with one
+ *    UE8M0 scale per 32 head_dim elements and 128-token blocks.
+ *  - Qwen3.8-27B-NVFP4 FP8-KV article (lpnh.cn/news/1821634): per-tensor
+ *    symmetric FP8 (kv_cache_scheme) and multi-token prediction (MTP).
+ *
+ * Ownership: the caller owns every buffer (pool, inputs, outputs, tables,
+ * workspace).  The library never allocates or frees device memory and keeps
+ * no mutable global state.  All work is enqueued asynchronously on the
+ * caller's stream; nothing synchronizes.
+ *
+ * Errors: argument problems the host can see return KVQ_ERR_INVALID_ARGUMENT
+ * or KVQ_ERR_UNSUPPORTED and enqueue nothing.  A workspace that is too small
+ * returns KVQ_ERR_WORKSPACE_TOO_SMALL.  A failed kernel launch returns
+ * KVQ_ERR_HIP.  Device-side contents (slot numbers, page-table entries,
+ * sequence lengths) are preconditions the library does not check: they must
+ * be in range.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvq_status {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID_ARGUMENT = 1,
+  KVQ_ERR_UNSUPPORTED = 2,
+  KVQ_ERR_WORKSPACE_TOO_SMALL = 3,
+  KVQ_ERR_HIP = 4
+} kvq_status;
+
+/* KV formats.  "K | V" planes; "rot" = pre-rotated by H/16 (256-point
+ * Sylvester Hadamard) before quantization.  Bytes per token and kv head at
+ * D = 256 in brackets (NInfer guide table; FP8_TENSOR and MXFP8 derived).
+ *  KVQ_BF16        K: bf16 bits as given | V: IEEE fp16            [1024]
+ *  KVQ_INT8_G64    int8 + fp16 scale per 64 values, K rot | same, V not rot   [528]
+ *  KVQ_FP8_ROW     E4M3 + one fp16 scale per row | same            [516]
+ *  KVQ_NVFP4_G16   E2M1 + UE4M3 scale per 16, rot | same, rot      [288]
+ *  KVQ_K8V4        K as FP8_ROW | V as NVFP4_G16 (rot)             [402]
+ *  KVQ_MXFP8       E4M3 + UE8M0 scale per 32 | same                [528; 264 at D=128]
+ *  KVQ_FP8_TENSOR  E4M3 of x / k_scale | E4M3 of x / v_scale       [512]
+ * Scales are computed from the group's absolute maximum: fp16(amax/127),
+ * fp16(amax/448), UE4M3(amax/6), and the OCP MX exponent
+ * floor(log2 amax) - 8; every element is then rounded to nearest-even from
+ * x / scale computed in IEEE fp32 with the stored scale, saturating at the
+ * format maximum.  The encoding is bit-exact and deterministic. */
+typedef enum kvq_format {
+  KVQ_BF16 = 0,
+  KVQ_INT8_G64 = 1,
+  KVQ_FP8_ROW = 2,
+  KVQ_NVFP4_G16 = 3,
+  KVQ_K8V4 = 4,
+  KVQ_MXFP8 = 5,
+  KVQ_FP8_TENSOR = 6
+} kvq_format;
+
+/* One layer's KV cache.
+ *  format        kvq_format value.
+ *  head_dim      D: 128 or 256 for BF16, FP8_ROW, FP8_TENSOR, MXFP8;
+ *                256 for INT8_G64, NVFP4_G16, K8V4 (the rotation is 256-point).
+ *  page_size     tokens per page: 64 or 128 (the pages use 64, and 128 for mxfp8).
+ *  num_kv_heads  H_kv >= 1.
+ *  num_pages     pages in the pool (> 0).
+ *  k_scale, v_scale  FP8_TENSOR only: the per-tensor fp32 scales (> 0,
+ *                finite); 1.0 is the "unit scale".  Ignored otherwise.
+ */
+typedef struct kvq_cache_desc {
+  int32_t format;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t num_kv_heads;
+  int64_t num_pages;
+  float k_scale;
+  float v_scale;
+} kvq_cache_desc;
+
+/* Bytes of one page: H_kv head blocks of [K codes | K scales | V codes |
+ * V scales], each plane padded to 128 bytes (no padding at the supported
+ * shapes, so a page is exactly page_size x H_kv x the per-token bytes).
+ * The pool is num_pages consecutive pages; it must be 128-byte aligned.
+ * Inside each plane, tokens are grouped in blocks of 16 stored in the order
+ * the decode kernel's matrix-core lanes consume them; the index formulas are
+ * spelled out in decode_attention_quant_amd/csrc/kvq_format.hpp. */
+kvq_status kvq_page_bytes(const kvq_cache_desc* desc, size_t* bytes_per_page);
+
+/* Quantize and store K/V rows (the write path; NInfer guide: every format
+ * is written through its codec when a token enters the cache).
+ *  pool          device, num_pages * page_bytes bytes, written.
+ *  k_bf16, v_bf16  device, bf16 [num_tokens][num_kv_heads][head_dim].
+ *  slot_mapping  device int32 [num_tokens]: page * page_size + offset;
+ *                a negative entry skips that token.  Two tokens must not
+ *                share a slot in one call.
+ * Only the bytes of the written slots change.  num_tokens == 0 is a no-op. */
+kvq_status kvq_quantize_append(const kvq_cache_desc* desc, void* pool,
+                               const void* k_bf16, const void* v_bf16,
+                               int64_t num_tokens, const int32_t* slot_mapping,
+                               hipStream_t stream);
+
+/* Workspace bytes kvq_decode_attention / kvq_decode_split need for this
+ * problem.  pages_per_split = 0 selects the library's own plan (the one
+ * kvq_decode_attention uses); a positive value forces that split length. */
+kvq_status kvq_decode_workspace_size(const kvq_cache_desc* desc, int32_t batch, int32_t n_q,
+                                     int32_t num_q_heads, int32_t max_pages_per_seq,
+                                     int32_t pages_per_split, size_t* bytes);
+
+/* Decode attention over the compressed cache (NInfer guide: each generated
+ * token attends over every cached K/V; Qwen FP8-KV article: several query
+ * tokens per step with MTP).
+ *  q_bf16        device bf16 [batch][n_q][num_q_heads][head_dim].
+ *  block_table   device int32 [batch][max_pages_per_seq]: logical page ->
+ *                physical page; entries past a sequence's last page are not read.
+ *  seq_lens      device int32 [batch]: cached tokens of each sequence,
+ *                including its n_q newest ones (already appended).
+ *  softmax_scale scale applied to q.k (e.g. 1/sqrt(head_dim)).
+ *  out           device fp32 [batch][n_q][num_q_heads][head_dim], written.
+ *  lse           device fp32 [batch][n_q][num_q_heads] (natural log of the
+ *                softmax denominator plus the max score), or NULL.
+ *  workspace     device, >= kvq_decode_workspace_size(..., 0, ...) bytes.
+ * Query token i of sequence b sits at position seq_lens[b] - n_q + i and
+ * attends to positions 0..that one (causal among the new tokens); query
+ * head h reads kv head h / (num_q_heads / num_kv_heads).  A query with no
+ * visible key gets out = 0 and lse = -inf.  Results are deterministic for a
+ * given device. */
+kvq_status kvq_decode_attention(const kvq_cache_desc* desc, const void* pool,
+                                const void* q_bf16, int32_t batch, int32_t n_q,
+                                int32_t num_q_heads, const int32_t* block_table,
+                                int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                float softmax_scale, float* out, float* lse,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The two phases of kvq_decode_attention, for callers that combine partial
+ * results themselves (e.g. several devices each holding a range of a long
+ * sequence's pages) or time them apart.
+ * kvq_decode_split writes, for every (sequence b, kv head h, split s, row r)
+ * with r = i * G + j (query token i, j-th query head of the group), the
+ * partial maximum m (base-2 units of the scaled score), the partial
+ * denominator l and the unnormalized output o[head_dim], all fp32:
+ *   workspace = [units][splits][rows][2] (m, l) followed, at the next
+ *   256-byte boundary, by [units][splits][rows][head_dim] (o),
+ *   units = batch * num_kv_heads, splits = ceil(max_pages / pages_per_split)
+ *   with pages_per_split as planned (or forced), rows = G * n_q.
+ * Rotated V formats leave o in the rotated domain; kvq_decode_combine merges
+ * the valid splits of each row, normalizes, undoes the rotation, and writes
+ * out / lse exactly as kvq_decode_attention does. */
+kvq_status kvq_decode_split(const kvq_cache_desc* desc, const void* pool, const void* q_bf16,
+                            int32_t batch, int32_t n_q, int32_t num_q_heads,
+                            const int32_t* block_table, int32_t max_pages_per_seq,
+                            const int32_t* seq_lens, float softmax_scale, int32_t pages_per_split,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+kvq_status kvq_decode_combine(const kvq_cache_desc* desc, int32_t batch, int32_t n_q,
+                              int32_t num_q_heads, int32_t max_pages_per_seq,
+                              const int32_t* seq_lens, int32_t pages_per_split,
+                              const void* workspace, size_t workspace_bytes,
+                              float* out, float* lse, hipStream_t stream);
+
+/* The split plan kvq_decode_attention uses for this problem on the current
+ * device: pages per split and the number of splits of the longest sequence. */
+kvq_status kvq_decode_plan(const kvq_cache_desc* desc, int32_t batch, int32_t n_q,
+                           int32_t num_q_heads, int32_t max_pages_per_seq,
+                           int32_t* pages_per_split, int32_t* num_splits);
+
+#define KVQ_DEQUANT_STORED_DOMAIN 1
+
+/* Decode one physical page to fp32 (a portable view of the cache; no extra
+ * rounding: the llama.cpp FP8-KV article warns that quality depends on
+ * avoiding additional rounding when caches move).
+ *  k_out, v_out  device fp32 [num_kv_heads][page_size][head_dim], written.
+ * flags & KVQ_DEQUANT_STORED_DOMAIN: return code x scale as stored (exact
+ * in fp32 except FP8_TENSOR, which rounds the product once); otherwise
+ * rotated planes are rotated back (H y / 16 in fp32).  Slots never written
+ * decode whatever bytes they hold. */
+kvq_status kvq_dequant_page(const kvq_cache_desc* desc, const void* pool, int64_t page,
+                            int32_t flags, float* k_out, float* v_out, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* kvq_status_string(kvq_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -22,10 +22,9 @@ Sources (the five web pages on KV-cache quantization that define the method):
 * llama.cpp FP8 KV-cache article (zicq.com), section on why the KV cache is
   compressed: the M_KV size formula.
 
-Where the pages are silent the plainest reading is taken; every such
-reading is listed in DESIGN.md ("readings").  Parity status of each function
-is stated in its docstring: "pinned by ..." names the independent checks in
-``tests/test_oracle_*.py``.
+Where the pages are silent the plainest reading is taken and the docstring
+that relies on it says so.  The independent checks that pin each function
+live in ``tests/test_oracle_*.py``.
 """
 
 from . import scalar, hadamard, formats, layout, attention  # noqa: F401

@@ -1,0 +1,150 @@
+"""The C ABI: library loads, exports what include/kvq.h declares, and rejects
+bad arguments on the host before any HIP call (CPU only; no kernel runs)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import decode_attention_quant_amd as kvq
+from oracle import layout as Lo
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(kvq.LIB_PATH), reason="libkvq.so not built")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:kvq_status|const char\*)\s+(kvq_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    fns = header_functions()
+    for name in ("kvq_quantize_append", "kvq_decode_attention", "kvq_dequant_page"):
+        assert name in fns
+    assert set(fns) == set(kvq.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = kvq.library()
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    lib = kvq.library()
+    for s in range(5):
+        assert lib.kvq_status_string(s)
+    assert lib.kvq_status_string(99) == b"unknown status"
+
+
+@pytest.mark.parametrize("fmt", range(7))
+@pytest.mark.parametrize("D,P", [(128, 64), (256, 64), (256, 128), (128, 128)])
+def test_page_bytes_match_the_oracle_layout(fmt, D, P):
+    d = kvq.desc(fmt, D, P, 3, 10, 0.5, 0.5)
+    rotated = fmt in (1, 3, 4)
+    if rotated and D != 256:
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.page_bytes(d)
+        assert e.value.status == 2
+        return
+    assert kvq.page_bytes(d) == Lo.Geometry(fmt, D, P, 3).page_bytes
+
+
+def _status(fn, *args):
+    return getattr(kvq.library(), fn)(*args)
+
+
+def test_desc_validation():
+    out = ctypes.c_size_t()
+    bad = [
+        (kvq.desc(7, 256, 64, 2, 4), 1),       # unknown format
+        (kvq.desc(-1, 256, 64, 2, 4), 1),
+        (kvq.desc(0, 256, 64, 0, 4), 1),       # no kv heads
+        (kvq.desc(0, 256, 64, 2, 0), 1),       # no pages
+        (kvq.desc(0, 192, 64, 2, 4), 2),       # head_dim
+        (kvq.desc(0, 256, 32, 2, 4), 2),       # page size
+        (kvq.desc(3, 128, 64, 2, 4), 2),       # rotation needs 256
+        (kvq.desc(6, 256, 64, 2, 4, 0.0, 1.0), 1),            # tensor scale must be > 0
+        (kvq.desc(6, 256, 64, 2, 4, 1.0, float("inf")), 1),
+        (kvq.desc(6, 256, 64, 2, 4, float("nan"), 1.0), 1),
+    ]
+    for d, want in bad:
+        assert _status("kvq_page_bytes", ctypes.byref(d), ctypes.byref(out)) == want
+    assert _status("kvq_page_bytes", None, ctypes.byref(out)) == 1
+    d = kvq.desc(0, 256, 64, 2, 4)
+    assert _status("kvq_page_bytes", ctypes.byref(d), None) == 1
+
+
+def test_append_validation_enqueues_nothing():
+    d = kvq.desc(2, 256, 64, 2, 4)
+    P = ctypes.c_void_p
+    ok = P(0x10000)
+    # zero tokens is a no-op that succeeds without touching the GPU
+    assert _status("kvq_quantize_append", ctypes.byref(d), None, None, None, 0, None, None) == 0
+    assert _status("kvq_quantize_append", ctypes.byref(d), ok, ok, ok, -1, ok, None) == 1
+    assert _status("kvq_quantize_append", ctypes.byref(d), None, ok, ok, 5, ok, None) == 1
+    assert _status("kvq_quantize_append", ctypes.byref(d), ok, ok, ok, 5, None, None) == 1
+    assert _status("kvq_quantize_append", ctypes.byref(d), P(0x10040), ok, ok, 5, ok, None) == 1  # pool alignment
+    assert _status("kvq_quantize_append", ctypes.byref(d), ok, P(0x10008), ok, 5, ok, None) == 1  # k alignment
+
+
+def test_workspace_size_with_forced_split():
+    d = kvq.desc(1, 256, 64, 4, 100)
+    sz = ctypes.c_size_t()
+    assert _status("kvq_decode_workspace_size", ctypes.byref(d), 3, 1, 24, 10, 4, ctypes.byref(sz)) == 0
+    units, nsplit, R = 3 * 4, 3, 6
+    ml = (units * nsplit * R * 2 * 4 + 255) // 256 * 256
+    assert sz.value == ml + units * nsplit * R * 256 * 4
+    # pages_per_split larger than the table is clamped to one split
+    assert _status("kvq_decode_workspace_size", ctypes.byref(d), 3, 1, 24, 10, 50, ctypes.byref(sz)) == 0
+    assert sz.value == (units * R * 2 * 4 + 255) // 256 * 256 + units * R * 256 * 4
+    bad = [(3, 0, 24, 10, 4), (3, 1, 0, 10, 4), (3, 1, 25, 10, 4), (-1, 1, 24, 10, 4), (3, 1, 24, 0, 4),
+           (3, 1, 24, 10, -2)]
+    for args in bad:
+        assert _status("kvq_decode_workspace_size", ctypes.byref(d), *args, ctypes.byref(sz)) == 1, args
+    # too many rows per kv head
+    assert _status("kvq_decode_workspace_size", ctypes.byref(d), 1, 64, 4 * 32, 10, 4, ctypes.byref(sz)) == 2
+
+
+def test_decode_validation_enqueues_nothing():
+    d = kvq.desc(2, 256, 64, 4, 100)
+    P = ctypes.c_void_p
+    ok = P(0x100000)
+    lib = kvq.library()
+    args = dict(pool=ok, q=ok, B=2, nq=1, Hq=24, bt=ok, mp=10, sl=ok, scale=0.0625, out=ok, lse=None, ws=ok,
+                wsb=1 << 30)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return lib.kvq_decode_split(ctypes.byref(d), a["pool"], a["q"], a["B"], a["nq"], a["Hq"], a["bt"], a["mp"],
+                                    a["sl"], a["scale"], 4, a["ws"], a["wsb"], None)
+
+    assert call(B=0) == 0  # empty batch: nothing to do
+    assert call(pool=None) == 1
+    assert call(q=None) == 1
+    assert call(bt=None) == 1
+    assert call(sl=None) == 1
+    assert call(ws=None) == 1
+    assert call(q=P(0x100004)) == 1
+    assert call(ws=P(0x100080)) == 1   # workspace must be 256-byte aligned
+    assert call(scale=float("nan")) == 1
+    assert call(wsb=100) == 3
+    assert call(Hq=22) == 1            # not a multiple of H_kv
+    bad = kvq.desc(3, 128, 64, 4, 100)
+    assert lib.kvq_decode_split(ctypes.byref(bad), ok, ok, 2, 1, 24, ok, 10, ok, 0.1, 4, ok, 1 << 30, None) == 2
+
+
+def test_dequant_validation():
+    d = kvq.desc(0, 256, 64, 2, 4)
+    P = ctypes.c_void_p
+    ok = P(0x100000)
+    lib = kvq.library()
+    assert lib.kvq_dequant_page(ctypes.byref(d), ok, 4, 1, ok, ok, None) == 1    # page out of range
+    assert lib.kvq_dequant_page(ctypes.byref(d), ok, -1, 1, ok, ok, None) == 1
+    assert lib.kvq_dequant_page(ctypes.byref(d), ok, 0, 2, ok, ok, None) == 1    # unknown flag
+    assert lib.kvq_dequant_page(ctypes.byref(d), None, 0, 1, ok, ok, None) == 1
+    assert lib.kvq_dequant_page(ctypes.byref(d), ok, 0, 1, P(0x100004), ok, None) == 1

@@ -1,0 +1,147 @@
+"""GPU parity: quantize-append writes exactly the oracle's bytes, and
+dequant-page returns exactly the oracle's stored values (bit for bit)."""
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_quant_amd as kvq
+import workloads as W
+from oracle import attention as OA, layout as OL, formats as OF
+from _gpu_common import build, note, require_gpu, W_name
+
+pytestmark = pytest.mark.gpu
+
+# (format, config whose shapes it borrows, head_dim override)
+CASES = [
+    ("BF16", 1, None), ("FP8_ROW", 1, None), ("INT8_G64", 2, None), ("FP8_ROW", 2, None), ("FP8_TENSOR", 2, None),
+    ("NVFP4_G16", 3, None), ("K8V4", 4, None), ("MXFP8", 5, None),
+]
+
+
+def _mismatch(bl):
+    got = bl.pool_gpu.cpu().numpy()
+    ref = bl.pool_ref
+    diff = np.flatnonzero(got != ref)
+    return got, ref, diff
+
+
+@pytest.mark.parametrize("fmt,cfg,_", CASES)
+def test_append_bytes_bit_exact(fmt, cfg, _):
+    lens = [130, 65, 7, 1]
+    c = W.make_case(cfg, fmt, device="cpu", B=4, lengths=lens)
+    bl = build(c)
+    got, ref, diff = _mismatch(bl)
+    assert diff.size == 0, "%s: %d bytes differ, first at %s: got %s ref %s" % (
+        W_name(c), diff.size, diff[:8], got[diff[:8]], ref[diff[:8]])
+    # bytes of slots that were never written keep the pool's fill
+    mask = OL.written_byte_mask(bl.geo, c.num_pages, c.slot_mapping.numpy())
+    assert np.all(got[~mask] == 0xFF)
+
+
+@pytest.mark.parametrize("fmt", ["BF16", "FP8_ROW", "FP8_TENSOR", "MXFP8"])
+def test_append_head_dim_128(fmt):
+    # config 5's shapes: head_dim 128, 128-token pages, 32 kv heads
+    c = W.make_case(5, fmt, device="cpu", B=3, lengths=[200, 129, 3])
+    bl = build(c)
+    got, ref, diff = _mismatch(bl)
+    assert diff.size == 0, "%s: %d bytes differ" % (W_name(c), diff.size)
+
+
+def _adversarial_rows(D, rng):
+    """Rows built to hit ties, saturation, zeros, signed zeros and subnormals."""
+    rows = []
+    f32 = np.float32
+    # E4M3 grid midpoints scaled so that amax/448 is a power of two (exact scale)
+    grid = np.unique(np.abs(OF.S.e4m3_decode(np.arange(127))))
+    mids = (grid[:-1] + grid[1:]) / 2
+    r = np.zeros(D, f32)
+    r[: min(D, len(mids))] = mids[:D]
+    r[-1] = 448.0
+    rows.append(r)
+    rows.append(-r)
+    # E2M1 ties inside 16-groups whose amax is 6 (scale 1)
+    t = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 0.0, -0.0, -0.25, -2.5, -5.0, 0.5, 1.0, 6.0], f32)
+    rows.append(np.tile(t, D // 16))
+    # int8 ties: amax 127 with x.5 values
+    r = (np.arange(D) % 127 - 63).astype(f32) + 0.5
+    r[0] = 127.0
+    rows.append(r)
+    rows.append(np.zeros(D, f32))                         # all zero
+    r = np.zeros(D, f32)
+    r[5] = -0.0
+    r[7] = 1e-30
+    rows.append(r)                                        # tiny amax
+    rows.append((rng.standard_normal(D) * 1e-38).astype(f32))   # fp32 subnormal range
+    r = rng.standard_normal(D).astype(f32)
+    r[3] = 3.0e4
+    rows.append(r)                                        # huge outlier
+    rows.append((rng.standard_normal(D) * 6e4).astype(f32))     # near the fp16 limit
+    rows.append(np.full(D, 1.0, f32))                     # constant
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("fmt", ["INT8_G64", "FP8_ROW", "NVFP4_G16", "K8V4", "MXFP8", "FP8_TENSOR", "BF16"])
+def test_append_adversarial_rows_bit_exact(fmt):
+    require_gpu()
+    D, P, H = 256, 64, 2
+    rng = np.random.default_rng(77)
+    rows = _adversarial_rows(D, rng)
+    n = rows.shape[0]
+    x = np.stack([rows, rows[::-1] * np.float32(0.5)], axis=1)  # [n][H][D]
+    xt = torch.from_numpy(x).to(torch.bfloat16)
+    k_scale = v_scale = 0.37
+    d = kvq.desc(fmt, D, P, H, 1, k_scale, v_scale)
+    geo = OL.Geometry(W.FORMAT_IDS[fmt], D, P, H)
+    slots = torch.arange(n, dtype=torch.int32)
+    pool = kvq.alloc_pool(d)
+    note("append adversarial", fmt)
+    kvq.quantize_append(d, pool, xt.cuda(), xt.flip(0).contiguous().cuda(), slots.cuda())
+    torch.cuda.synchronize()
+    ref = np.full(geo.page_bytes, 0xFF, np.uint8)
+    OA.quantize_append(geo, ref, W.bf16_bits(xt), W.bf16_bits(xt.flip(0)), slots.numpy(), k_scale, v_scale)
+    got = pool.cpu().numpy()
+    diff = np.flatnonzero(got != ref)
+    assert diff.size == 0, "%s: %d bytes differ at %s: got %s ref %s" % (fmt, diff.size, diff[:8], got[diff[:8]],
+                                                                        ref[diff[:8]])
+
+
+def test_negative_slots_are_skipped():
+    c = W.make_case(2, "FP8_ROW", device="cpu", B=2, lengths=[70, 20])
+    c.slot_mapping[::3] = -1
+    bl = build(c)
+    got, ref, diff = _mismatch(bl)
+    assert diff.size == 0
+
+
+@pytest.mark.parametrize("fmt,cfg", [(f, c) for f, c, _ in CASES])
+def test_dequant_page_bit_exact_stored_domain(fmt, cfg):
+    c = W.make_case(cfg, fmt, device="cpu", B=2, lengths=[c_len(cfg), 17])
+    bl = build(c)
+    for page in range(c.num_pages):
+        note("dequant", fmt, "page", page)
+        k, v = kvq.dequant_page(bl.desc, bl.pool_gpu, page, stored_domain=True)
+        K, V = OA.dequant_page(bl.geo, bl.pool_ref, page, c.k_scale, c.v_scale, stored_domain=True)
+        kg, vg = k.cpu().numpy(), v.cpu().numpy()
+        # compare only written slots (others hold canary bytes, possibly NaN codes)
+        slots = set(c.slot_mapping.numpy().tolist())
+        rows = [s - page * c.P for s in range(page * c.P, (page + 1) * c.P) if s in slots]
+        for K_, kg_ in ((K, kg), (V, vg)):
+            a = K_[:, rows].astype(np.float32)
+            b = kg_[:, rows]
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), "%s page %d" % (fmt, page)
+
+
+def c_len(cfg):
+    return 200 if cfg != 5 else 300
+
+
+@pytest.mark.parametrize("fmt,cfg", [("INT8_G64", 2), ("NVFP4_G16", 3), ("K8V4", 4)])
+def test_dequant_page_original_domain(fmt, cfg):
+    c = W.make_case(cfg, fmt, device="cpu", B=1, lengths=[128])
+    bl = build(c)
+    for page in range(c.num_pages):
+        k, v = kvq.dequant_page(bl.desc, bl.pool_gpu, page, stored_domain=False)
+        K, V = OA.dequant_page(bl.geo, bl.pool_ref, page, stored_domain=False)
+        assert np.allclose(k.cpu().numpy(), K, atol=1e-5 * np.abs(K).max(), rtol=1e-5)
+        assert np.allclose(v.cpu().numpy(), V, atol=1e-5 * np.abs(V).max(), rtol=1e-5)

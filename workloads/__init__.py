@@ -4,7 +4,7 @@ This module only draws inputs (queries, keys, values, lengths, page tables);
 it holds none of the quantization or attention arithmetic.  Both the GPU
 library's callers and the CPU oracle are fed from it.
 
-Recipe (also stated in the design doc):
+Recipe:
 
 * host RNG ``numpy.random.default_rng(1000 + config)`` draws, in order, the
   4 special K channels, the sequence lengths, and one global permutation of
