@@ -54,9 +54,6 @@ WORKLOADS = {
                  label="tiny decode: 1 sequence x 1024 tokens, 4 q / 2 kv heads, head_dim 256"),
 }
 
-BYTES_PER_TOKEN = {}  # filled from the library's page size
-
-
 def kv_bytes_per_token(d):
     return kvq.page_bytes(d) // (d.page_size * d.num_kv_heads)
 
@@ -78,7 +75,7 @@ class Setup:
         self.v_new = c.v.index_select(0, idx).contiguous()
         self.slot_new = c.slot_mapping.index_select(0, idx).contiguous()
         self.q = c.q
-        self.pps, self.nsplit = kvq.decode_plan(self.desc, c.B, c.n_q, c.H_q, c.max_pages)
+        self.nwg, self.slots = kvq.decode_plan(self.desc, c.B, c.n_q, c.H_q, c.max_pages)
         self.ws = kvq.alloc_workspace(kvq.workspace_size(self.desc, c.B, c.n_q, c.H_q, c.max_pages))
         self.out = torch.empty((c.B, c.n_q, c.H_q, c.D), dtype=torch.float32, device="cuda")
         self.lse = torch.empty((c.B, c.n_q, c.H_q), dtype=torch.float32, device="cuda")
@@ -93,20 +90,15 @@ class Setup:
         kvq.quantize_append(self.desc, self.pool, self.k_new, self.v_new, self.slot_new, stream=stream)
         if ev is not None:
             ev[1].record(stream)
-        if self.nsplit == 1:
-            kvq.decode_attention(self.desc, self.pool, self.q, self.bt, self.sl, c.softmax_scale, out=self.out,
-                                 lse=self.lse, workspace=self.ws, stream=stream)
-            if ev is not None:
-                ev[2].record(stream)
-                ev[3].record(stream)
-        else:
-            kvq.decode_split(self.desc, self.pool, self.q, self.bt, self.sl, c.softmax_scale, self.ws, stream=stream)
-            if ev is not None:
-                ev[2].record(stream)
-            kvq.decode_combine(self.desc, c.B, c.n_q, c.H_q, c.max_pages, self.sl, self.ws, self.out, self.lse,
-                               stream=stream)
-            if ev is not None:
-                ev[3].record(stream)
+        # the two launches kvq_decode_attention makes, timed apart
+        kvq.decode_split(self.desc, self.pool, self.q, self.bt, self.sl, c.softmax_scale, self.ws,
+                         flags=kvq.SPLIT_WRITE_WHOLE_UNITS, out=self.out, lse=self.lse, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        kvq.decode_combine(self.desc, c.B, c.n_q, c.H_q, c.max_pages, self.sl, self.ws, self.out, self.lse,
+                           flags=kvq.SPLIT_WRITE_WHOLE_UNITS, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
 
 
 def time_steps(s, steps, warmup, stream):
@@ -124,7 +116,7 @@ def time_steps(s, steps, warmup, stream):
         torch.cuda.synchronize()
         total = t0.elapsed_time(t1)
         app = [e[0].elapsed_time(e[1]) for e in evs]
-        dec = [e[1].elapsed_time(e[2]) for e in evs]   # split kernel (or the single direct kernel)
+        dec = [e[1].elapsed_time(e[2]) for e in evs]   # split kernel
         comb = [e[2].elapsed_time(e[3]) for e in evs]
     return total / steps, float(np.mean(app)), float(np.mean(dec)), float(np.mean(comb)), \
         float(np.percentile(dec, 10)), float(np.percentile(dec, 90))
@@ -204,7 +196,7 @@ def main():
             "combine_ms": comb_ms,
             "append_ms": app_ms,
             "append_tok_per_s": c.B / (app_ms * 1e-3),
-            "pages_per_split": s.pps, "num_splits": s.nsplit,
+            "split_workgroups": s.nwg, "partial_slots": s.slots,
         }
         per[fmt] = res
         print("[bench] %s %s: %.1f GB/s (%.1f%% of peak), step %.3f ms, split %.3f ms, combine %.3f ms, "
@@ -234,7 +226,7 @@ def main():
         "config": {"workload": wl["label"], "kv_dtype": fmt, "batch": c.B, "n_q": c.n_q, "num_q_heads": c.H_q,
                    "num_kv_heads": c.H_kv, "head_dim": c.D, "page_size": c.P,
                    "cached_tokens": int(c.seq_lens.astype(np.int64).sum()),
-                   "pages_per_split": s.pps, "num_splits": s.nsplit},
+                   "split_workgroups": s.nwg},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                      "kernel": "decode_split_kernel<%s>" % fmt, "kernel_ms": res["split_kernel_ms"]},

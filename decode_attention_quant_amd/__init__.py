@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(HERE, "libkvq.so")
 FORMATS = {"BF16": 0, "INT8_G64": 1, "FP8_ROW": 2, "NVFP4_G16": 3, "K8V4": 4, "MXFP8": 5, "FP8_TENSOR": 6}
 FORMAT_NAMES = {v: k for k, v in FORMATS.items()}
 DEQUANT_STORED_DOMAIN = 1
+SPLIT_WRITE_WHOLE_UNITS = 1
 
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP runtime error"}
 
@@ -56,8 +57,8 @@ def library():
             "kvq_quantize_append": [D, P, P, P, I64, P, P],
             "kvq_decode_workspace_size": [D, I32, I32, I32, I32, I32, ctypes.POINTER(SZ)],
             "kvq_decode_attention": [D, P, P, I32, I32, I32, P, I32, P, F, P, P, P, SZ, P],
-            "kvq_decode_split": [D, P, P, I32, I32, I32, P, I32, P, F, I32, P, SZ, P],
-            "kvq_decode_combine": [D, I32, I32, I32, I32, P, I32, P, SZ, P, P, P],
+            "kvq_decode_split": [D, P, P, I32, I32, I32, P, I32, P, F, I32, I32, P, P, P, SZ, P],
+            "kvq_decode_combine": [D, I32, I32, I32, I32, P, I32, I32, P, SZ, P, P, P],
             "kvq_decode_plan": [D, I32, I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)],
             "kvq_dequant_page": [D, P, I64, I32, P, P, P],
         }
@@ -119,18 +120,19 @@ def quantize_append(d, pool, k, v, slot_mapping, stream=None):
                                          _stream(stream)), "kvq_quantize_append")
 
 
-def workspace_size(d, batch, n_q, num_q_heads, max_pages, pages_per_split=0):
+def workspace_size(d, batch, n_q, num_q_heads, max_pages, num_workgroups=0):
     out = ctypes.c_size_t()
     _check(library().kvq_decode_workspace_size(ctypes.byref(d), batch, n_q, num_q_heads, max_pages,
-                                               pages_per_split, ctypes.byref(out)), "kvq_decode_workspace_size")
+                                               num_workgroups, ctypes.byref(out)), "kvq_decode_workspace_size")
     return out.value
 
 
 def decode_plan(d, batch, n_q, num_q_heads, max_pages):
-    pps, ns = ctypes.c_int32(), ctypes.c_int32()
-    _check(library().kvq_decode_plan(ctypes.byref(d), batch, n_q, num_q_heads, max_pages, ctypes.byref(pps),
-                                     ctypes.byref(ns)), "kvq_decode_plan")
-    return pps.value, ns.value
+    """(split workgroups, partial slots) that decode_attention uses."""
+    nwg, slots = ctypes.c_int32(), ctypes.c_int32()
+    _check(library().kvq_decode_plan(ctypes.byref(d), batch, n_q, num_q_heads, max_pages, ctypes.byref(nwg),
+                                     ctypes.byref(slots)), "kvq_decode_plan")
+    return nwg.value, slots.value
 
 
 def alloc_workspace(nbytes, device="cuda"):
@@ -158,19 +160,20 @@ def decode_attention(d, pool, q, block_table, seq_lens, softmax_scale, out=None,
     return out
 
 
-def decode_split(d, pool, q, block_table, seq_lens, softmax_scale, workspace, pages_per_split=0, stream=None):
+def decode_split(d, pool, q, block_table, seq_lens, softmax_scale, workspace, num_workgroups=0, flags=0, out=None,
+                 lse=None, stream=None):
     B, n_q, H_q, D = q.shape
     _check(library().kvq_decode_split(
         ctypes.byref(d), _ptr(pool), _ptr(q), B, n_q, H_q, _ptr(block_table), block_table.shape[1],
-        _ptr(seq_lens), float(softmax_scale), pages_per_split, _ptr(workspace), workspace.numel(),
-        _stream(stream)), "kvq_decode_split")
+        _ptr(seq_lens), float(softmax_scale), num_workgroups, flags, _ptr(out), _ptr(lse), _ptr(workspace),
+        workspace.numel(), _stream(stream)), "kvq_decode_split")
 
 
-def decode_combine(d, batch, n_q, num_q_heads, max_pages, seq_lens, workspace, out, lse=None, pages_per_split=0,
-                   stream=None):
+def decode_combine(d, batch, n_q, num_q_heads, max_pages, seq_lens, workspace, out, lse=None, num_workgroups=0,
+                   flags=0, stream=None):
     _check(library().kvq_decode_combine(
-        ctypes.byref(d), batch, n_q, num_q_heads, max_pages, _ptr(seq_lens), pages_per_split, _ptr(workspace),
-        workspace.numel(), _ptr(out), _ptr(lse), _stream(stream)), "kvq_decode_combine")
+        ctypes.byref(d), batch, n_q, num_q_heads, max_pages, _ptr(seq_lens), num_workgroups, flags,
+        _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse), _stream(stream)), "kvq_decode_combine")
 
 
 def dequant_page(d, pool, page, stored_domain=True, stream=None):

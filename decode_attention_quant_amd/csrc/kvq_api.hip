@@ -30,12 +30,16 @@ Geometry geo_of(const kvq_cache_desc* d) { return make_geometry(d->format, d->he
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-constexpr int MAX_ROWS = 1024;  // G * n_q per kv head
+constexpr int MAX_ROWS = 1024;   // G * n_q per kv head
+constexpr int MAX_BATCH = 4096;  // the split kernel keeps a per-sequence prefix table in LDS
 
 struct Plan {
-  int32_t R, tiles, units, pps, nsplit;
-  size_t ml_bytes, o_bytes;
+  int32_t R, tiles, units, nwg, slots;
+  size_t cum_bytes, ml_bytes, o_bytes;
+  size_t total() const { return cum_bytes + ml_bytes + o_bytes; }
 };
+
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
 kvq_status check_decode_shape(const kvq_cache_desc* d, int32_t batch, int32_t n_q, int32_t H_q, int32_t max_pages) {
   kvq_status st = check_desc(d);
@@ -43,49 +47,62 @@ kvq_status check_decode_shape(const kvq_cache_desc* d, int32_t batch, int32_t n_
   if (batch < 0 || n_q < 1 || H_q < 1 || max_pages < 1) return KVQ_ERR_INVALID_ARGUMENT;
   if (H_q % d->num_kv_heads != 0) return KVQ_ERR_INVALID_ARGUMENT;
   if ((int64_t)(H_q / d->num_kv_heads) * n_q > MAX_ROWS) return KVQ_ERR_UNSUPPORTED;
-  if ((int64_t)batch * d->num_kv_heads > (1 << 24)) return KVQ_ERR_UNSUPPORTED;
+  if (batch > MAX_BATCH) return KVQ_ERR_UNSUPPORTED;
+  if ((int64_t)max_pages * d->page_size >= ((int64_t)1 << 31) / 16) return KVQ_ERR_UNSUPPORTED;
+  // the flat block range and the combine grid stay within int32
+  const int64_t units = (int64_t)batch * d->num_kv_heads;
+  if (units * ((int64_t)max_pages * d->page_size / 16) > INT32_MAX) return KVQ_ERR_UNSUPPORTED;
+  if (units * (H_q / d->num_kv_heads) * n_q > INT32_MAX) return KVQ_ERR_UNSUPPORTED;
   return KVQ_OK;
 }
 
-// pages_per_split = 0: choose so that the whole problem makes about eight
-// workgroups per compute unit (enough to fill 256 CUs and to even out
-// sequences of different lengths), never less than one page per split.
+// num_workgroups = 0: one split workgroup per ~256 token blocks (4096
+// tokens) of the largest problem the arguments allow, and at least as many
+// as fit on the device at once.  Sequences shorter than max_pages leave
+// the trailing workgroups empty (the kernel keeps >= 128 blocks per range).
+// A positive value forces that count.
 kvq_status make_plan(const kvq_cache_desc* d, int32_t batch, int32_t n_q, int32_t H_q, int32_t max_pages,
-                     int32_t pps_req, Plan* p) {
+                     int32_t nwg_req, Plan* p) {
   p->R = (H_q / d->num_kv_heads) * n_q;
   p->tiles = (p->R + 15) / 16;
   p->units = batch * d->num_kv_heads;
-  if (pps_req < 0) return KVQ_ERR_INVALID_ARGUMENT;
-  if (pps_req > 0) {
-    p->pps = pps_req < max_pages ? pps_req : max_pages;
+  if (nwg_req < 0) return KVQ_ERR_INVALID_ARGUMENT;
+  if (nwg_req > 0) {
+    p->nwg = nwg_req;
   } else {
-    int dev = 0, cus = 0;
+    int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess) return KVQ_ERR_HIP;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
       return KVQ_ERR_HIP;
-    const int64_t target = (int64_t)cus * 8;
-    const int64_t work = (int64_t)p->units * p->tiles * max_pages;
-    int64_t pps = (work + target - 1) / target;
-    if (pps < 1) pps = 1;
-    if (pps > max_pages) pps = max_pages;
-    p->pps = (int32_t)pps;
+    const Geometry geo = make_geometry(d->format, d->head_dim, d->page_size, d->num_kv_heads);
+    if (decode_split_occupancy(geo, batch, p->R, &per_cu) != hipSuccess || per_cu < 1) return KVQ_ERR_HIP;
+    const int64_t blocks_upper = (int64_t)p->units * (((int64_t)max_pages * d->page_size + 15) / 16);
+    int64_t nwg = (blocks_upper + 255) / 256;
+    const int64_t resident = (int64_t)cus * per_cu;
+    if (nwg < resident) nwg = resident;
+    if (nwg < 1) nwg = 1;
+    p->nwg = (int32_t)nwg;
   }
-  p->nsplit = (max_pages + p->pps - 1) / p->pps;
-  if ((int64_t)p->nsplit * p->units > INT32_MAX || p->tiles > 65535) return KVQ_ERR_UNSUPPORTED;
-  const size_t rows = (size_t)p->units * p->nsplit * p->R;
-  p->ml_bytes = (rows * 2 * sizeof(float) + 255) / 256 * 256;
-  p->o_bytes = rows * (size_t)d->head_dim * sizeof(float);
+  if (p->nwg > (1 << 24) || p->tiles > 65535) return KVQ_ERR_UNSUPPORTED;
+  p->slots = p->units + p->nwg;
+  p->cum_bytes = align256((size_t)(batch + 1) * sizeof(int32_t));
+  p->ml_bytes = align256((size_t)p->slots * p->R * 2 * sizeof(float));
+  p->o_bytes = (size_t)p->slots * p->R * (size_t)d->head_dim * sizeof(float);
   return KVQ_OK;
 }
 
 DecodeArgs base_args(const kvq_cache_desc* d, const Plan& p, int32_t batch, int32_t n_q, int32_t H_q,
-                     int32_t max_pages, const int32_t* seq_lens, float softmax_scale) {
+                     int32_t max_pages, const int32_t* seq_lens, float softmax_scale, void* workspace) {
   DecodeArgs a{};
   a.seq_lens = seq_lens;
   a.B = batch; a.n_q = n_q; a.H_q = H_q; a.G = H_q / d->num_kv_heads; a.R = p.R;
-  a.max_pages = max_pages; a.pps = p.pps; a.nsplit = p.nsplit;
+  a.max_pages = max_pages; a.nwg = p.nwg;
   a.qk_scale = softmax_scale * 1.4426950408889634f * (d->format == F_FP8_TENSOR ? d->k_scale : 1.0f);
   a.v_out_scale = d->format == F_FP8_TENSOR ? d->v_scale : 1.0f;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  a.ws_cum = reinterpret_cast<int32_t*>(ws);
+  a.ws_ml = reinterpret_cast<float*>(ws + p.cum_bytes);
+  a.ws_o = reinterpret_cast<float*>(ws + p.cum_bytes + p.ml_bytes);
   return a;
 }
 
@@ -131,68 +148,64 @@ kvq_status kvq_quantize_append(const kvq_cache_desc* desc, void* pool, const voi
 }
 
 kvq_status kvq_decode_plan(const kvq_cache_desc* desc, int32_t batch, int32_t n_q, int32_t num_q_heads,
-                           int32_t max_pages_per_seq, int32_t* pages_per_split, int32_t* num_splits) {
+                           int32_t max_pages_per_seq, int32_t* num_workgroups, int32_t* num_slots) {
   kvq_status st = check_decode_shape(desc, batch, n_q, num_q_heads, max_pages_per_seq);
   if (st != KVQ_OK) return st;
-  if (pages_per_split == nullptr || num_splits == nullptr) return KVQ_ERR_INVALID_ARGUMENT;
+  if (num_workgroups == nullptr || num_slots == nullptr) return KVQ_ERR_INVALID_ARGUMENT;
   Plan p;
   st = make_plan(desc, batch, n_q, num_q_heads, max_pages_per_seq, 0, &p);
   if (st != KVQ_OK) return st;
-  *pages_per_split = p.pps;
-  *num_splits = p.nsplit;
+  *num_workgroups = p.nwg;
+  *num_slots = p.slots;
   return KVQ_OK;
 }
 
 kvq_status kvq_decode_workspace_size(const kvq_cache_desc* desc, int32_t batch, int32_t n_q, int32_t num_q_heads,
-                                     int32_t max_pages_per_seq, int32_t pages_per_split, size_t* bytes) {
+                                     int32_t max_pages_per_seq, int32_t num_workgroups, size_t* bytes) {
   kvq_status st = check_decode_shape(desc, batch, n_q, num_q_heads, max_pages_per_seq);
   if (st != KVQ_OK) return st;
   if (bytes == nullptr) return KVQ_ERR_INVALID_ARGUMENT;
   Plan p;
-  st = make_plan(desc, batch, n_q, num_q_heads, max_pages_per_seq, pages_per_split, &p);
+  st = make_plan(desc, batch, n_q, num_q_heads, max_pages_per_seq, num_workgroups, &p);
   if (st != KVQ_OK) return st;
-  *bytes = p.ml_bytes + p.o_bytes;
+  *bytes = p.total();
   return KVQ_OK;
 }
 
-static kvq_status decode_common(const kvq_cache_desc* desc, const void* pool, const void* q_bf16, int32_t batch,
-                                int32_t n_q, int32_t H_q, const int32_t* block_table, int32_t max_pages,
-                                const int32_t* seq_lens, float softmax_scale, int32_t pps_req, bool allow_direct,
-                                float* out, float* lse, void* workspace, size_t workspace_bytes,
-                                hipStream_t stream, bool run_combine) {
+static kvq_status decode_run(const kvq_cache_desc* desc, const void* pool, const void* q_bf16, int32_t batch,
+                             int32_t n_q, int32_t H_q, const int32_t* block_table, int32_t max_pages,
+                             const int32_t* seq_lens, float softmax_scale, int32_t nwg_req, bool write_direct,
+                             bool run_split, bool run_combine, float* out, float* lse, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
   kvq_status st = check_decode_shape(desc, batch, n_q, H_q, max_pages);
   if (st != KVQ_OK) return st;
   if (!isfinite(softmax_scale)) return KVQ_ERR_INVALID_ARGUMENT;
-  if (pps_req < 0) return KVQ_ERR_INVALID_ARGUMENT;
+  if (nwg_req < 0) return KVQ_ERR_INVALID_ARGUMENT;
   if (batch == 0) return KVQ_OK;
-  if (pool == nullptr || q_bf16 == nullptr || block_table == nullptr || seq_lens == nullptr)
-    return KVQ_ERR_INVALID_ARGUMENT;
-  if (run_combine && out == nullptr) return KVQ_ERR_INVALID_ARGUMENT;
-  if (!aligned(pool, 128) || !aligned(q_bf16, 16) || (out != nullptr && !aligned(out, 16)))
-    return KVQ_ERR_INVALID_ARGUMENT;
-  Plan p;
-  st = make_plan(desc, batch, n_q, H_q, max_pages, pps_req, &p);
-  if (st != KVQ_OK) return st;
-  const bool direct = allow_direct && p.nsplit == 1;
-  if (!direct) {
-    if (workspace == nullptr || !aligned(workspace, 256)) return KVQ_ERR_INVALID_ARGUMENT;
-    if (workspace_bytes < p.ml_bytes + p.o_bytes) return KVQ_ERR_WORKSPACE_TOO_SMALL;
+  if (seq_lens == nullptr || workspace == nullptr || !aligned(workspace, 256)) return KVQ_ERR_INVALID_ARGUMENT;
+  if (run_split) {
+    if (pool == nullptr || q_bf16 == nullptr || block_table == nullptr) return KVQ_ERR_INVALID_ARGUMENT;
+    if (!aligned(pool, 128) || !aligned(q_bf16, 16)) return KVQ_ERR_INVALID_ARGUMENT;
   }
+  if (write_direct || run_combine) {
+    if (out == nullptr || !aligned(out, 16)) return KVQ_ERR_INVALID_ARGUMENT;
+  }
+  Plan p;
+  st = make_plan(desc, batch, n_q, H_q, max_pages, nwg_req, &p);
+  if (st != KVQ_OK) return st;
+  if (workspace_bytes < p.total()) return KVQ_ERR_WORKSPACE_TOO_SMALL;
   const Geometry geo = geo_of(desc);
-  DecodeArgs a = base_args(desc, p, batch, n_q, H_q, max_pages, seq_lens, softmax_scale);
+  DecodeArgs a = base_args(desc, p, batch, n_q, H_q, max_pages, seq_lens, softmax_scale, workspace);
   a.pool = static_cast<const uint8_t*>(pool);
   a.q = static_cast<const uint16_t*>(q_bf16);
   a.block_table = block_table;
-  a.direct = direct ? 1 : 0;
+  a.write_direct = write_direct ? 1 : 0;
   a.out = out;
   a.lse = lse;
-  if (!direct) {
-    a.ws_ml = static_cast<float*>(workspace);
-    a.ws_o = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + p.ml_bytes);
-  }
-  hipError_t e = launch_decode_split(geo, a, stream);
+  hipError_t e = hipSuccess;
+  if (run_split) e = launch_decode_split(geo, a, stream);
   if (e != hipSuccess) return KVQ_ERR_HIP;
-  if (!direct && run_combine) e = launch_decode_combine(geo, a, stream);
+  if (run_combine) e = launch_decode_combine(geo, a, stream);
   return hip_status(e);
 }
 
@@ -200,40 +213,30 @@ kvq_status kvq_decode_attention(const kvq_cache_desc* desc, const void* pool, co
                                 int32_t n_q, int32_t num_q_heads, const int32_t* block_table,
                                 int32_t max_pages_per_seq, const int32_t* seq_lens, float softmax_scale, float* out,
                                 float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return decode_common(desc, pool, q_bf16, batch, n_q, num_q_heads, block_table, max_pages_per_seq, seq_lens,
-                       softmax_scale, 0, true, out, lse, workspace, workspace_bytes, stream, true);
+  return decode_run(desc, pool, q_bf16, batch, n_q, num_q_heads, block_table, max_pages_per_seq, seq_lens,
+                    softmax_scale, 0, true, true, true, out, lse, workspace, workspace_bytes, stream);
 }
 
 kvq_status kvq_decode_split(const kvq_cache_desc* desc, const void* pool, const void* q_bf16, int32_t batch,
                             int32_t n_q, int32_t num_q_heads, const int32_t* block_table,
                             int32_t max_pages_per_seq, const int32_t* seq_lens, float softmax_scale,
-                            int32_t pages_per_split, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return decode_common(desc, pool, q_bf16, batch, n_q, num_q_heads, block_table, max_pages_per_seq, seq_lens,
-                       softmax_scale, pages_per_split, false, nullptr, nullptr, workspace, workspace_bytes, stream,
-                       false);
+                            int32_t num_workgroups, int32_t flags, float* out, float* lse, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  if ((flags & ~KVQ_SPLIT_WRITE_WHOLE_UNITS) != 0) return KVQ_ERR_INVALID_ARGUMENT;
+  const bool whole = (flags & KVQ_SPLIT_WRITE_WHOLE_UNITS) != 0;
+  return decode_run(desc, pool, q_bf16, batch, n_q, num_q_heads, block_table, max_pages_per_seq, seq_lens,
+                    softmax_scale, num_workgroups, whole, true, false, whole ? out : nullptr,
+                    whole ? lse : nullptr, workspace, workspace_bytes, stream);
 }
 
 kvq_status kvq_decode_combine(const kvq_cache_desc* desc, int32_t batch, int32_t n_q, int32_t num_q_heads,
-                              int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t pages_per_split,
-                              const void* workspace, size_t workspace_bytes, float* out, float* lse,
+                              int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t num_workgroups,
+                              int32_t flags, const void* workspace, size_t workspace_bytes, float* out, float* lse,
                               hipStream_t stream) {
-  kvq_status st = check_decode_shape(desc, batch, n_q, num_q_heads, max_pages_per_seq);
-  if (st != KVQ_OK) return st;
-  if (pages_per_split < 0) return KVQ_ERR_INVALID_ARGUMENT;
-  if (batch == 0) return KVQ_OK;
-  if (seq_lens == nullptr || out == nullptr || workspace == nullptr) return KVQ_ERR_INVALID_ARGUMENT;
-  if (!aligned(out, 16) || !aligned(workspace, 256)) return KVQ_ERR_INVALID_ARGUMENT;
-  Plan p;
-  st = make_plan(desc, batch, n_q, num_q_heads, max_pages_per_seq, pages_per_split, &p);
-  if (st != KVQ_OK) return st;
-  if (workspace_bytes < p.ml_bytes + p.o_bytes) return KVQ_ERR_WORKSPACE_TOO_SMALL;
-  const Geometry geo = geo_of(desc);
-  DecodeArgs a = base_args(desc, p, batch, n_q, num_q_heads, max_pages_per_seq, seq_lens, 1.0f);
-  a.ws_ml = const_cast<float*>(static_cast<const float*>(workspace));
-  a.ws_o = reinterpret_cast<float*>(const_cast<uint8_t*>(static_cast<const uint8_t*>(workspace)) + p.ml_bytes);
-  a.out = out;
-  a.lse = lse;
-  return hip_status(launch_decode_combine(geo, a, stream));
+  if ((flags & ~KVQ_SPLIT_WRITE_WHOLE_UNITS) != 0) return KVQ_ERR_INVALID_ARGUMENT;
+  return decode_run(desc, nullptr, nullptr, batch, n_q, num_q_heads, nullptr, max_pages_per_seq, seq_lens, 1.0f,
+                    num_workgroups, (flags & KVQ_SPLIT_WRITE_WHOLE_UNITS) != 0, false, true, out, lse,
+                    const_cast<void*>(workspace), workspace_bytes, stream);
 }
 
 kvq_status kvq_dequant_page(const kvq_cache_desc* desc, const void* pool, int64_t page, int32_t flags, float* k_out,

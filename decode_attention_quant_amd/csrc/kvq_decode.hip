@@ -37,9 +37,16 @@ template <int FMT, int D>
 struct DT {
   static constexpr int KC = k_codec(FMT), VC = v_codec(FMT);
   static constexpr int KBITS = codec_bits(KC), VBITS = codec_bits(VC);
-  static constexpr bool QF16 = k_rotated(FMT);  // rotated q -> f16 hi/lo
+  static constexpr bool QI8 = KC == C_I8G64;    // Q.K on the int8 matrix cores, q in two int8 pieces
+  static constexpr bool QF16 = KC == C_E2G16;   // Q.K in f16, q split into f16 hi + lo
+  static constexpr bool QROT = k_rotated(FMT);  // q is rotated first (K was)
   static constexpr bool VROT = v_rotated(FMT);
   static constexpr int KSTEPS = D / 32;
+  static constexpr int QSTEPS = QI8 ? D / 64 : D / 32;  // MFMA k-steps of Q.K
+  static constexpr int QPIECES = (QI8 || QF16) ? 2 : 1;
+  // Q operands kept in LDS (one ds_read_b128 per k-step) where registers
+  // would otherwise spill; in registers elsewhere.
+  static constexpr bool QLDS = true;
   static constexpr int NT = D / 16;
   static constexpr int KCH = D * KBITS / 512;                       // 16-B K chunks per lane per block
   static constexpr int VCH = (VBITS == 16 ? 2 : 1) * NT * 4 / 16;   // 16-B V chunks per lane per block
@@ -47,6 +54,13 @@ struct DT {
   static constexpr int VSW = VC == C_E4ROW ? 2 : VC == C_I8G64 ? 8 : VC == C_E4MX ? D / 32 : VC == C_E2G16 ? 16 : 0;
   static constexpr int G = n_groups(KC, D) > 0 ? n_groups(KC, D) : 1;
 };
+
+// Tables the kernel only reads (page table, sequence lengths) are read
+// through the constant address space, so uniform indexes become scalar
+// loads: a vector load here would be counted by vmcnt, and waiting for it
+// would also wait for every block prefetch issued before it.
+typedef const __attribute__((address_space(4))) int32_t cint32;
+__device__ __forceinline__ const cint32* as_const(const int32_t* p) { return (const cint32*)p; }
 
 template <int FMT, int D>
 struct Buf {
@@ -74,10 +88,10 @@ __device__ __forceinline__ void load_words(uint32_t (&w)[N], const uint8_t* p) {
 // Load token block j of this split into registers.
 template <int FMT, int D>
 __device__ __forceinline__ void load_block(Buf<FMT, D>& buf, const uint8_t* head0, const Geometry& geo,
-                                           const int32_t* bt_row, int page0, int j, int lane) {
+                                           const cint32* bt_row, int page0, int j, int lane) {
   using T = DT<FMT, D>;
   const int bpp = geo.P >> 4;
-  const int page = page0 + j / bpp;
+  const int page = __builtin_amdgcn_readfirstlane(page0 + j / bpp);
   const int bip = j - (j / bpp) * bpp;
   const int64_t phys = bt_row[page];
   const uint8_t* hb = head0 + phys * geo.page_bytes;
@@ -108,11 +122,12 @@ __device__ __forceinline__ void load_block(Buf<FMT, D>& buf, const uint8_t* head
 
 // 8 E4M3 codes (two dwords) -> bf16x8, exact
 __device__ __forceinline__ bf16x8 e4m3x8_bf16(uint32_t w0, uint32_t w1) {
-  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, false);
-  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, true);
-  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, false);
-  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, true);
-  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  uint4 r;
+  r.x = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, false));
+  r.y = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, true));
+  r.z = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, false));
+  r.w = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, true));
+  return bitcast<bf16x8>(r);
 }
 
 // 4 signed int8 codes -> 2 x f16x2, exact: the byte with its sign bit
@@ -128,16 +143,18 @@ __device__ __forceinline__ f16x8 i8x8_f16(uint32_t w0, uint32_t w1) {
   f16x2 a, b, c, d;
   i8x4_f16(w0, a, b);
   i8x4_f16(w1, c, d);
-  return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  return bitcast<f16x8>(make_uint4(bitcast<uint32_t>(a), bitcast<uint32_t>(b), bitcast<uint32_t>(c),
+                                   bitcast<uint32_t>(d)));
 }
 
 // 8 E2M1 codes (one dword, element e in nibble e) -> f16x8, exact
 __device__ __forceinline__ f16x8 e2m1x8_f16(uint32_t w) {
-  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
-  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
-  const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
-  const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
-  return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  uint4 r;
+  r.x = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0));
+  r.y = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1));
+  r.z = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2));
+  r.w = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3));
+  return bitcast<f16x8>(r);
 }
 
 __device__ __forceinline__ uint32_t word(const uint4& q, int i) {
@@ -148,9 +165,16 @@ __device__ __forceinline__ uint32_t word(const uint4& q, int i) {
 
 template <int FMT, int D>
 struct QOps {
-  // B operands of S = K . Q^T per k-step: bf16 (plain q) or f16 hi/lo (rotated q)
-  typename std::conditional<DT<FMT, D>::QF16, f16x8, bf16x8>::type hi[DT<FMT, D>::KSTEPS];
-  f16x8 lo[DT<FMT, D>::QF16 ? DT<FMT, D>::KSTEPS : 1];
+  // B operands of S = K . Q^T, k-step kk, piece p (bf16 q; f16 hi, lo; or
+  // int8 coarse, fine), as raw 16-byte lane values
+  using T = DT<FMT, D>;
+  uint4 reg[T::QLDS ? 1 : T::QSTEPS * T::QPIECES];
+  const uint4* lds;
+  int lane;
+  __device__ __forceinline__ uint4 get(int kk, int p) const {
+    if constexpr (T::QLDS) return lds[(kk * T::QPIECES + p) * 64 + lane];
+    else return reg[kk * T::QPIECES + p];
+  }
 };
 
 // ----------------------------------------------------------- S = K . Q^T
@@ -163,12 +187,12 @@ __device__ __forceinline__ f32x4 qk_block(const Buf<FMT, D>& buf, const QOps<FMT
   if constexpr (T::KC == C_BF16) {
 #pragma unroll
     for (int kk = 0; kk < T::KSTEPS; ++kk)
-      S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(buf.k[kk]), qo.hi[kk], S, 0, 0, 0);
+      S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(buf.k[kk]), bitcast<bf16x8>(qo.get(kk, 0)), S, 0, 0, 0);
   } else if constexpr (T::KC == C_E4ROW || T::KC == C_E4TEN) {
 #pragma unroll
     for (int i = 0; i < T::KCH; ++i) {
-      S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_bf16(buf.k[i].x, buf.k[i].y), qo.hi[2 * i], S, 0, 0, 0);
-      S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_bf16(buf.k[i].z, buf.k[i].w), qo.hi[2 * i + 1], S, 0, 0, 0);
+      S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_bf16(buf.k[i].x, buf.k[i].y), bitcast<bf16x8>(qo.get(2 * i, 0)), S, 0, 0, 0);
+      S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_bf16(buf.k[i].z, buf.k[i].w), bitcast<bf16x8>(qo.get(2 * i + 1, 0)), S, 0, 0, 0);
     }
     if constexpr (T::KC == C_E4ROW) {
       // one fp16 scale per token: tokens 4g..4g+3 in ks[0] (lo, hi), ks[1]
@@ -186,7 +210,8 @@ __device__ __forceinline__ f32x4 qk_block(const Buf<FMT, D>& buf, const QOps<FMT
       for (int hh = 0; hh < 2; ++hh) {
         const int kk = 2 * i + hh;
         const f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            e4m3x8_bf16(hh ? buf.k[i].z : buf.k[i].x, hh ? buf.k[i].w : buf.k[i].y), qo.hi[kk], zero, 0, 0, 0);
+            e4m3x8_bf16(hh ? buf.k[i].z : buf.k[i].x, hh ? buf.k[i].w : buf.k[i].y), bitcast<bf16x8>(qo.get(kk, 0)),
+            zero, 0, 0, 0);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int bi = e * G + kk;  // token 4g+e, group kk
@@ -196,19 +221,19 @@ __device__ __forceinline__ f32x4 qk_block(const Buf<FMT, D>& buf, const QOps<FMT
       }
     }
   } else if constexpr (T::KC == C_I8G64) {
-    // one fp16 scale per 64 values = two k-steps = one chunk
+    // one fp16 scale per 64 values = one 16-byte chunk = one int8 k-step:
+    // the raw codes are the A operand; q = coarse + fine / 254 (int8 each)
+    const i32x4 izero = {0, 0, 0, 0};
 #pragma unroll
     for (int grp = 0; grp < T::KCH; ++grp) {
-      const f16x8 a0 = i8x8_f16(buf.k[grp].x, buf.k[grp].y);
-      const f16x8 a1 = i8x8_f16(buf.k[grp].z, buf.k[grp].w);
-      f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, qo.hi[2 * grp], zero, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, qo.lo[2 * grp], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, qo.hi[2 * grp + 1], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, qo.lo[2 * grp + 1], acc, 0, 0, 0);
+      const i32x4 kc = bitcast<i32x4>(buf.k[grp]);
+      const i32x4 a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(kc, bitcast<i32x4>(qo.get(grp, 0)), izero, 0, 0, 0);
+      const i32x4 a2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(kc, bitcast<i32x4>(qo.get(grp, 1)), izero, 0, 0, 0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int hw = e * 4 + grp;  // halfword of token 4g+e, group grp
-        S[e] += acc[e] * f16_bits_to_f32((buf.ks[hw >> 1] >> (16 * (hw & 1))) & 0xFFFFu);
+        const float sc = f16_bits_to_f32((buf.ks[hw >> 1] >> (16 * (hw & 1))) & 0xFFFFu);
+        S[e] += (float)(a1[e] * 254 + a2[e]) * sc;  // |a1| <= 64*127*127: no int32 overflow
       }
     }
   } else if constexpr (T::KC == C_E2G16) {
@@ -225,8 +250,8 @@ __device__ __forceinline__ f32x4 qk_block(const Buf<FMT, D>& buf, const QOps<FMT
         const _Float16 s = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)sb, 1.0f, false)[0];
         f16x8 a = e2m1x8_f16(word(buf.k[i], hh));
         a *= s;
-        S = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qo.hi[kk], S, 0, 0, 0);
-        S = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qo.lo[kk], S, 0, 0, 0);
+        S = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bitcast<f16x8>(qo.get(kk, 0)), S, 0, 0, 0);
+        S = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bitcast<f16x8>(qo.get(kk, 1)), S, 0, 0, 0);
       }
     }
   }
@@ -319,313 +344,528 @@ __device__ __forceinline__ void fwht_wave(float (&x)[E], int lane) {
   }
 }
 
+// ----------------------------------------------------------- tail blocks
+
+// Zero the V codes and V scales of this lane's tokens 4g+e at or past
+// `nvalid` (slots past the sequence end may hold any bytes, NaN codes
+// included), so that tokens with zero probability add exactly zero.
+template <int FMT, int D>
+__device__ __forceinline__ void clear_tail(Buf<FMT, D>& buf, int nvalid, int g) {
+  using T = DT<FMT, D>;
+  const int nv = nvalid - 4 * g;  // valid tokens among this lane's four
+  uint32_t bmask = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) bmask |= (e < nv) ? (0xFFu << (8 * e)) : 0u;
+  const uint32_t h01 = (nv > 0 ? 0xFFFFu : 0u) | (nv > 1 ? 0xFFFF0000u : 0u);
+  const uint32_t h23 = (nv > 2 ? 0xFFFFu : 0u) | (nv > 3 ? 0xFFFF0000u : 0u);
+#pragma unroll
+  for (int q = 0; q < T::VCH; ++q) {
+    if constexpr (T::VBITS == 16) {
+      buf.v[q].x &= h01; buf.v[q].y &= h23; buf.v[q].z &= h01; buf.v[q].w &= h23;
+    } else {
+      buf.v[q].x &= bmask; buf.v[q].y &= bmask; buf.v[q].z &= bmask; buf.v[q].w &= bmask;
+    }
+  }
+  if constexpr (T::VC == C_E4ROW) {
+    buf.vs[0] &= h01;
+    buf.vs[1] &= h23;
+  } else if constexpr (T::VC == C_I8G64) {  // token e: words 2e, 2e+1
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (e >= nv) { buf.vs[2 * e] = 0u; buf.vs[2 * e + 1] = 0u; }
+  } else if constexpr (T::VC == C_E4MX) {  // token e: D/128 words
+    constexpr int WPT = D / 128;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int w = 0; w < WPT; ++w)
+        if (e >= nv) buf.vs[e * WPT + w] = 0u;
+  } else if constexpr (T::VC == C_E2G16) {
+#pragma unroll
+    for (int w = 0; w < T::VSW; ++w) buf.vs[w] &= bmask;
+  }
+}
+
 // ----------------------------------------------------------- the kernel
+
+// Blocks per split workgroup: an equal share of the T blocks, but at least
+// MIN_BLOCKS_PER_WG, so that when the sequences are shorter than the grid
+// was sized for, fewer workgroups get longer ranges (the rest find theirs
+// empty) instead of every range shrinking.
+constexpr int MIN_BLOCKS_PER_WG = 128;
+__device__ __forceinline__ int blocks_per_workgroup(int total, int nwg) {
+  const int per = (total + nwg - 1) / nwg;
+  return per > MIN_BLOCKS_PER_WG ? per : MIN_BLOCKS_PER_WG;
+}
+
+// LDS layout of the split kernel (floats): prefix table [B + 1] (rounded to
+// 16), merge area [4][Rt][D], m and l [4][16] each, 16 spare floats (q
+// maxima), then the Q operand store when it lives in LDS.
+template <int FMT, int D>
+__host__ __device__ constexpr size_t split_lds_bytes(int B, int R) {
+  using T = DT<FMT, D>;
+  const int rt = R < 16 ? R : 16;
+  const size_t cum = (size_t)((B + 1 + 15) / 16 * 16);
+  return (cum + 4 * (size_t)rt * D + 64 + 64 + 16) * sizeof(float) +
+         (T::QLDS ? (size_t)T::QSTEPS * T::QPIECES * 64 * 16 : 0);
+}
 
 template <int FMT, int D>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, DecodeArgs a) {
   using T = DT<FMT, D>;
   constexpr float NEG_INF = -__builtin_inff();
-  __shared__ float lds[4 * 16 * D + 2 * 64 + 16];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  extern __shared__ float lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, c16 = lane & 15;
-  const int s = (int)(blockIdx.x % (unsigned)a.nsplit), u = (int)(blockIdx.x / (unsigned)a.nsplit);
-  const int rt = blockIdx.y;
-  const int b = u / geo.H_kv, h = u - b * geo.H_kv;
-  const int L = a.seq_lens[b];
-  const int npages = (L + geo.P - 1) / geo.P;
-  const int page0 = s * a.pps;
-  if (page0 >= npages && !a.direct) return;
-  const int tok0 = page0 * geo.P;
-  const int tok1 = min(L, (page0 + a.pps) * geo.P);
-  const int nblk = tok1 > tok0 ? (tok1 - tok0 + 15) >> 4 : 0;
+  const int w = blockIdx.x, rt = blockIdx.y;
   const int Rt = min(16, a.R - 16 * rt);
+  int* cum = reinterpret_cast<int*>(lds);
+  float* sm_o = lds + (a.B + 1 + 15) / 16 * 16;
+  float* sm_m = sm_o + 4 * Rt * D;
+  float* sm_l = sm_m + 64;
+  float* qexp = sm_l + 64;
+  uint4* qst = reinterpret_cast<uint4*>(qexp + 16);
 
-  // ---- query rows of this tile: row r (= c16 in S layout) -> (i, head)
-  const int r = c16;
-  const int rr = 16 * rt + r;
-  const bool row_ok = r < Rt;
-  const int qi = rr / a.G, qh = h * a.G + (rr - qi * a.G);
-  const int limit = L - a.n_q + qi;  // last visible position of this row
-  float crow = a.qk_scale;
-
-  QOps<FMT, D> qo;
-  if constexpr (!T::QF16) {
-    const uint16_t* qp = a.q + (((int64_t)b * a.n_q + qi) * a.H_q + qh) * D;
-#pragma unroll
-    for (int kk = 0; kk < T::KSTEPS; ++kk) {
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (row_ok) w = *reinterpret_cast<const uint4*>(qp + 32 * kk + 8 * g);
-      qo.hi[kk] = bitcast<bf16x8>(w);
-    }
-  } else {
-    // q' = H q / 16 in fp32, scaled by 2^(8 - e) so that max|q'| lies in
-    // [128, 256), then split into f16 hi + lo (about 22 significant bits).
-    float* qrot = lds;              // [16][D]
-    float* qexp = lds + 16 * D;     // [16]
-    constexpr int E = D / 64;
-    for (int row = wave; row < Rt; row += 4) {
-      const int rr2 = 16 * rt + row;
-      const int i2 = rr2 / a.G, h2 = h * a.G + (rr2 - i2 * a.G);
-      const uint16_t* qp = a.q + (((int64_t)b * a.n_q + i2) * a.H_q + h2) * D + E * lane;
-      float x[E];
-      const uint2 w = *reinterpret_cast<const uint2*>(qp);
-      x[0] = bf16_to_f32(w.x & 0xFFFFu); x[1] = bf16_to_f32(w.x >> 16);
-      x[2] = bf16_to_f32(w.y & 0xFFFFu); x[3] = bf16_to_f32(w.y >> 16);
-      fwht_wave<E>(x, lane);
-      float am = 0.f;
-#pragma unroll
-      for (int i = 0; i < E; ++i) { x[i] *= 0.0625f; am = fmaxf(am, fabsf(x[i])); }
-#pragma unroll
-      for (int m = 1; m < 64; m <<= 1) am = fmaxf(am, __shfl_xor(am, m));
-      const int ex = am > 0.f ? __builtin_amdgcn_frexp_expf(am) : 0;
-#pragma unroll
-      for (int i = 0; i < E; ++i) qrot[row * D + E * lane + i] = ldexpf(x[i], 8 - ex);
-      if (lane == 0) qexp[row] = (float)ex;
-    }
-    __syncthreads();
-    if (row_ok) crow = a.qk_scale * ldexpf(1.0f, (int)qexp[r] - 8);
-#pragma unroll
-    for (int kk = 0; kk < T::KSTEPS; ++kk) {
-      f16x8 hi, lo;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float v = row_ok ? qrot[r * D + 32 * kk + 8 * g + e] : 0.f;
-        hi[e] = (_Float16)v;
-        lo[e] = (_Float16)(v - (float)hi[e]);
-      }
-      qo.hi[kk] = hi;
-      qo.lo[kk] = lo;
-    }
-    __syncthreads();
-  }
-
-  // ---- stream this wave's token blocks
-  const uint8_t* head0 = a.pool + (int64_t)h * geo.head_bytes;
-  const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
-  float m_run = NEG_INF, l_run = 0.f;
-  f32x4 O[T::NT];
-#pragma unroll
-  for (int nt = 0; nt < T::NT; ++nt) O[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto process = [&](const Buf<FMT, D>& buf, int j) {
-    const int t0 = tok0 + 16 * j;
-    const f32x4 S = qk_block<FMT, D>(buf, qo, lane);
-    float sc[4];
-    float bm = NEG_INF;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int t = t0 + 4 * g + e;
-      sc[e] = (row_ok && t <= limit) ? S[e] * crow : NEG_INF;
-      bm = fmaxf(bm, sc[e]);
-    }
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const float m_new = fmaxf(m_run, bm);
-    if (__any(m_new > m_run)) {
-      const float corr = (m_new > m_run) ? exp2f(m_run - m_new) : 1.0f;
-      l_run *= corr;
-      float ce[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ce[e] = __shfl(corr, 4 * g + e);
-#pragma unroll
-      for (int nt = 0; nt < T::NT; ++nt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) O[nt][e] *= ce[e];
-      m_run = m_new;
-    }
-    float p[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      p[e] = (sc[e] == NEG_INF) ? 0.f : exp2f(sc[e] - m_run);
-      l_run += p[e];
-    }
-    const f16x4 P = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
-    const bool tail = t0 + 16 > L;  // slots past the end may hold anything: zero their V
-#pragma unroll
-    for (int nt = 0; nt < T::NT; ++nt) {
-      f16x4 vb = v_operand<FMT, D>(buf, nt, lane);
-      if (tail) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (t0 + 4 * g + e >= L) vb[e] = (_Float16)0.0f;
-      }
-      O[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(P, vb, O[nt], 0, 0, 0);
-    }
-  };
-
+  // ---- cum[b] = H_kv * sum_{b' < b} ceil(L_b' / 16): the flat block index
+  //      of unit (b, 0).  Each thread scans a contiguous run, then the runs'
+  //      totals are scanned by wave 0.
   {
-    Buf<FMT, D> A, Bb;
-    int j = wave;
-    if (j < nblk) load_block<FMT, D>(A, head0, geo, bt_row, page0, j, lane);
-    while (j < nblk) {
-      if (j + 4 < nblk) load_block<FMT, D>(Bb, head0, geo, bt_row, page0, j + 4, lane);
-      process(A, j);
-      j += 4;
-      if (j >= nblk) break;
-      if (j + 4 < nblk) load_block<FMT, D>(A, head0, geo, bt_row, page0, j + 4, lane);
-      process(Bb, j);
-      j += 4;
+    const int per_t = (a.B + 255) / 256;
+    const int b0 = threadIdx.x * per_t;
+    int run = 0;
+    for (int i = 0; i < per_t; ++i) {
+      const int bb = b0 + i;
+      if (bb < a.B) run += ((a.seq_lens[bb] + 15) >> 4) * geo.H_kv;
     }
-  }
-
-  // ---- merge the 4 waves
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  float* sm_o = lds;                    // [4][16][D]
-  float* sm_m = lds + 4 * 16 * D;       // [4][16]
-  float* sm_l = sm_m + 64;              // [4][16]
-  if (lane < 16) {
-    sm_m[wave * 16 + lane] = m_run;
-    sm_l[wave * 16 + lane] = l_run;
-  }
-  __syncthreads();
+    float* tot = sm_o;  // scratch [257] before the merge area is used (it holds >= 512)
+    tot[threadIdx.x] = __int_as_float(run);
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      int v[4], sum = 0;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int row = 4 * g + e;
-    float M = NEG_INF;
+      for (int i = 0; i < 4; ++i) { v[i] = __float_as_int(tot[4 * threadIdx.x + i]); sum += v[i]; }
+      int incl = sum;  // inclusive scan of the lane sums
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w * 16 + row]);
-    const float mw = sm_m[wave * 16 + row];
-    const float f = (mw == NEG_INF) ? 0.f : exp2f(mw - M);
+      for (int m = 1; m < 64; m <<= 1) {
+        const int t = __shfl_up(incl, m);
+        if ((int)threadIdx.x >= m) incl += t;
+      }
+      int ex = incl - sum;
 #pragma unroll
-    for (int nt = 0; nt < T::NT; ++nt) sm_o[(wave * 16 + row) * D + 16 * nt + c16] = O[nt][e] * f;
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < Rt * D; idx += 256) {
-    const int row = idx / D, d = idx - row * D;
-    float o = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) o += sm_o[(w * 16 + row) * D + d];
-    sm_o[row * D + d] = o;  // wave-0 slot of this row; read by this thread only
-  }
-  __syncthreads();
-
-  // ---- write: one wave per row
-  constexpr int E = D / 64;
-  for (int row = wave; row < Rt; row += 4) {
-    float M = NEG_INF;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w * 16 + row]);
-    float l = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float mw = sm_m[w * 16 + row];
-      l += (mw == NEG_INF) ? 0.f : exp2f(mw - M) * sm_l[w * 16 + row];
+      for (int i = 0; i < 4; ++i) { tot[4 * threadIdx.x + i] = __int_as_float(ex); ex += v[i]; }
+      if (threadIdx.x == 63) tot[256] = __int_as_float(ex);  // grand total
     }
-    const int rr2 = 16 * rt + row;
-    float x[E];
+    __syncthreads();
+    int base = __float_as_int(tot[threadIdx.x]);
+    for (int i = 0; i < per_t; ++i) {
+      const int bb = b0 + i;
+      if (bb < a.B) {
+        cum[bb] = base;
+        base += ((a.seq_lens[bb] + 15) >> 4) * geo.H_kv;
+      }
+    }
+    if (threadIdx.x == 0) cum[a.B] = __float_as_int(tot[256]);
+    __syncthreads();
+  }
+  const int total = cum[a.B];
+  if (w == 0 && rt == 0)
+    for (int i = threadIdx.x; i <= a.B; i += 256) a.ws_cum[i] = cum[i];
+  const int per = blocks_per_workgroup(total, a.nwg);
+  int x = w * per;
+  const int x_end = min(total, x + per);
+
+  while (x < x_end) {
+    // ---- the unit that holds flat block x: b = last index with cum[b] <= x
+    int lo = 0, hi = a.B;  // cum[lo] <= x < cum[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (cum[mid] <= x) lo = mid; else hi = mid;
+    }
+    const int b = __builtin_amdgcn_readfirstlane(lo);
+    const int L = as_const(a.seq_lens)[b];
+    const int nb = (L + 15) >> 4;
+    const int within = x - cum[b];
+    const int h = __builtin_amdgcn_readfirstlane(within / nb);
+    const int blk0 = __builtin_amdgcn_readfirstlane(within - h * nb);
+    const int seg_end = min(x_end, cum[b] + (h + 1) * nb);
+    const int nblk = __builtin_amdgcn_readfirstlane(seg_end - x);
+    const bool whole = blk0 == 0 && nblk == nb;
+    const int u = b * geo.H_kv + h;
+
+    // ---- query rows of this tile: row r (= c16 in S layout) -> (i, head)
+    const int r = c16;
+    const int rr = 16 * rt + r;
+    const bool row_ok = r < Rt;
+    const int qi = rr / a.G, qh = h * a.G + (rr - qi * a.G);
+    const int limit = row_ok ? L - a.n_q + qi : -1;  // last visible position of this row
+    float crow = a.qk_scale;
+
+    QOps<FMT, D> qo;
+    qo.lane = lane;
+    qo.lds = qst;
+    uint4 qv[T::QSTEPS * T::QPIECES];
+    if constexpr (!T::QROT) {
+      const uint16_t* qp = a.q + (((int64_t)b * a.n_q + qi) * a.H_q + qh) * D;
 #pragma unroll
-    for (int i = 0; i < E; ++i) x[i] = sm_o[row * D + E * lane + i];
-    if (!a.direct) {
-      const int64_t prow = ((int64_t)u * a.nsplit + s) * a.R + rr2;
-      float* op = a.ws_o + prow * D + E * lane;
-#pragma unroll
-      for (int i = 0; i < E; ++i) op[i] = x[i];
-      if (lane == 0) {
-        a.ws_ml[prow * 2] = M;
-        a.ws_ml[prow * 2 + 1] = l;
+      for (int kk = 0; kk < T::QSTEPS; ++kk) {
+        uint4 q4 = make_uint4(0, 0, 0, 0);
+        if (row_ok) q4 = *reinterpret_cast<const uint4*>(qp + 32 * kk + 8 * g);
+        qv[kk] = q4;
       }
     } else {
-      const float inv = l > 0.f ? a.v_out_scale / l : 0.f;
+      // q' = H q / 16 in fp32 (rows spread over the waves, through LDS)
+      float* qrot = sm_o;  // [Rt][D]
+      constexpr int E = D / 64;
+      for (int row = wave; row < Rt; row += 4) {
+        const int rr2 = 16 * rt + row;
+        const int i2 = rr2 / a.G, h2 = h * a.G + (rr2 - i2 * a.G);
+        const uint16_t* qp = a.q + (((int64_t)b * a.n_q + i2) * a.H_q + h2) * D + E * lane;
+        float xq[E];
+        const uint2 q2 = *reinterpret_cast<const uint2*>(qp);
+        xq[0] = bf16_to_f32(q2.x & 0xFFFFu); xq[1] = bf16_to_f32(q2.x >> 16);
+        xq[2] = bf16_to_f32(q2.y & 0xFFFFu); xq[3] = bf16_to_f32(q2.y >> 16);
+        fwht_wave<E>(xq, lane);
+        float am = 0.f;
 #pragma unroll
-      for (int i = 0; i < E; ++i) x[i] *= inv;
-      if constexpr (T::VROT) {
-        fwht_wave<E>(x, lane);
+        for (int i = 0; i < E; ++i) { xq[i] *= 0.0625f; am = fmaxf(am, fabsf(xq[i])); }
 #pragma unroll
-        for (int i = 0; i < E; ++i) x[i] *= 0.0625f;
+        for (int m = 1; m < 64; m <<= 1) am = fmaxf(am, __shfl_xor(am, m));
+#pragma unroll
+        for (int i = 0; i < E; ++i) qrot[row * D + E * lane + i] = xq[i];
+        if (lane == 0) qexp[row] = am;
       }
-      const int i2 = rr2 / a.G, h2 = h * a.G + (rr2 - i2 * a.G);
-      const int64_t orow = ((int64_t)b * a.n_q + i2) * a.H_q + h2;
-      float* op = a.out + orow * D + E * lane;
+      __syncthreads();
+      const float am = row_ok ? qexp[r] : 0.f;
+      if constexpr (T::QI8) {
+        // q' ~ (c1 + c2 / 254) / inv, int8 c1 = RN(q' inv), c2 = RN(254 (q' inv - c1)),
+        // inv = 127 / max|q'|: error below max|q'| / 64516 per element
+        const float inv = am > 0.f ? 127.0f / am : 0.f;
+        crow = am > 0.f ? a.qk_scale * (am / (127.0f * 254.0f)) : 0.f;
 #pragma unroll
-      for (int i = 0; i < E; ++i) op[i] = x[i];
-      if (a.lse != nullptr && lane == 0)
-        a.lse[orow] = l > 0.f ? (M + __log2f(l)) * 0.69314718055994531f : NEG_INF;
+        for (int kk = 0; kk < T::QSTEPS; ++kk) {
+          uint32_t w1[4] = {0, 0, 0, 0}, w2[4] = {0, 0, 0, 0};
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            // k-slot 16g + j of int8 k-step kk <-> d as laid out in the K chunk
+            const int d = 64 * kk + (j < 8 ? 8 * g + j : 32 + 8 * g + (j - 8));
+            const float v = row_ok ? qrot[r * D + d] * inv : 0.f;
+            const float c1 = fmaxf(fminf(rintf(v), 127.f), -127.f);
+            const float c2 = fmaxf(fminf(rintf((v - c1) * 254.0f), 127.f), -127.f);
+            w1[j >> 2] |= ((uint32_t)(int)c1 & 0xFFu) << (8 * (j & 3));
+            w2[j >> 2] |= ((uint32_t)(int)c2 & 0xFFu) << (8 * (j & 3));
+          }
+          qv[2 * kk] = make_uint4(w1[0], w1[1], w1[2], w1[3]);
+          qv[2 * kk + 1] = make_uint4(w2[0], w2[1], w2[2], w2[3]);
+        }
+      } else {
+        // f16 hi + lo of q' * 2^(8 - e), e = exponent of max|q'|: max in
+        // [128, 256), about 22 significant bits kept
+        const int ex = am > 0.f ? __builtin_amdgcn_frexp_expf(am) : 0;
+        if (row_ok) crow = a.qk_scale * ldexpf(1.0f, ex - 8);
+#pragma unroll
+        for (int kk = 0; kk < T::QSTEPS; ++kk) {
+          f16x8 qh16, ql16;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float v = row_ok ? ldexpf(qrot[r * D + 32 * kk + 8 * g + e], 8 - ex) : 0.f;
+            qh16[e] = (_Float16)v;
+            ql16[e] = (_Float16)(v - (float)qh16[e]);
+          }
+          qv[2 * kk] = bitcast<uint4>(qh16);
+          qv[2 * kk + 1] = bitcast<uint4>(ql16);
+        }
+      }
     }
+    if constexpr (T::QLDS) {
+      __syncthreads();  // every wave has finished reading qrot / the previous segment's store
+      if (wave == 0) {
+#pragma unroll
+        for (int i = 0; i < T::QSTEPS * T::QPIECES; ++i) qst[i * 64 + lane] = qv[i];
+      }
+      __syncthreads();
+    } else {
+#pragma unroll
+      for (int i = 0; i < T::QSTEPS * T::QPIECES; ++i) qo.reg[i] = qv[i];
+      if constexpr (T::QROT) __syncthreads();  // qrot (the merge area) is free again
+    }
+
+    // ---- stream this wave's token blocks: blk0 + wave, blk0 + wave + 4, ...
+    const uint8_t* head0 = a.pool + (int64_t)h * geo.head_bytes;
+    const cint32* bt_row = as_const(a.block_table) + (int64_t)b * a.max_pages;
+    float m_run = NEG_INF, l_run = 0.f;
+    f32x4 O[T::NT];
+#pragma unroll
+    for (int nt = 0; nt < T::NT; ++nt) O[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto process = [&](Buf<FMT, D>& buf, int jb) {
+      const int t0 = 16 * jb;
+      if (t0 + 16 > L) clear_tail<FMT, D>(buf, L - t0, g);
+      __builtin_amdgcn_sched_barrier(0);
+      const f32x4 S = qk_block<FMT, D>(buf, qo, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      float sc[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sc[e] = (t0 + 4 * g + e <= limit) ? S[e] * crow : NEG_INF;
+      float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      bm = fmaxf(bm, __shfl_xor(bm, 16));
+      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      if (__any(bm > m_run)) {  // rare after the first blocks: rescale l and O
+        const float m_new = fmaxf(m_run, bm);
+        const float corr = (m_new > m_run) ? exp2f(m_run - m_new) : 1.0f;
+        l_run *= corr;
+        float ce[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ce[e] = __shfl(corr, 4 * g + e);
+#pragma unroll
+        for (int nt = 0; nt < T::NT; ++nt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) O[nt][e] *= ce[e];
+        m_run = m_new;
+      }
+      // a row that has seen no visible key yet has m_run = -inf and only
+      // -inf scores: subtract 0 instead so that exp2 gives 0, not NaN
+      const float m_use = (m_run == NEG_INF) ? 0.f : m_run;
+      float p[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        p[e] = exp2f(sc[e] - m_use);
+        l_run += p[e];
+      }
+      const f16x4 P = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+      // keep the compiler from hoisting every V conversion ahead of the
+      // products (it would hold all of them live and spill)
+#pragma unroll
+      for (int nt = 0; nt < T::NT; ++nt) {
+        if ((nt & 3) == 0) __builtin_amdgcn_sched_barrier(0);
+        O[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(P, v_operand<FMT, D>(buf, nt, lane), O[nt], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    {
+      Buf<FMT, D> A, Bb;
+      const int jend = blk0 + nblk;
+      int j = blk0 + wave;
+      if (j < jend) load_block<FMT, D>(A, head0, geo, bt_row, 0, j, lane);
+      while (j < jend) {
+        if (j + 4 < jend) load_block<FMT, D>(Bb, head0, geo, bt_row, 0, j + 4, lane);
+        process(A, j);
+        j += 4;
+        if (j >= jend) break;
+        if (j + 4 < jend) load_block<FMT, D>(A, head0, geo, bt_row, 0, j + 4, lane);
+        process(Bb, j);
+        j += 4;
+      }
+    }
+
+    // ---- merge the 4 waves
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    if (lane < 16) {
+      sm_m[wave * 16 + lane] = m_run;
+      sm_l[wave * 16 + lane] = l_run;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 4 * g + e;
+      if (row < Rt) {
+        float M = NEG_INF;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, sm_m[ww * 16 + row]);
+        const float mw = sm_m[wave * 16 + row];
+        const float f = (mw == NEG_INF) ? 0.f : exp2f(mw - M);
+#pragma unroll
+        for (int nt = 0; nt < T::NT; ++nt) sm_o[(wave * Rt + row) * D + 16 * nt + c16] = O[nt][e] * f;
+      }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < Rt * D; idx += 256) {
+      float o = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) o += sm_o[ww * Rt * D + idx];
+      sm_o[idx] = o;  // wave-0 slot of this element; read by this thread only
+    }
+    __syncthreads();
+
+    // ---- write: one wave per row
+    constexpr int E = D / 64;
+    const bool direct = whole && a.write_direct;
+    for (int row = wave; row < Rt; row += 4) {
+      float M = NEG_INF;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, sm_m[ww * 16 + row]);
+      float l = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) {
+        const float mw = sm_m[ww * 16 + row];
+        l += (mw == NEG_INF) ? 0.f : exp2f(mw - M) * sm_l[ww * 16 + row];
+      }
+      const int rr2 = 16 * rt + row;
+      float xo[E];
+#pragma unroll
+      for (int i = 0; i < E; ++i) xo[i] = sm_o[row * D + E * lane + i];
+      if (!direct) {
+        const int64_t prow = (int64_t)(u + w) * a.R + rr2;
+        float* op = a.ws_o + prow * D + E * lane;
+#pragma unroll
+        for (int i = 0; i < E; ++i) op[i] = xo[i];
+        if (lane == 0) {
+          a.ws_ml[prow * 2] = M;
+          a.ws_ml[prow * 2 + 1] = l;
+        }
+      } else {
+        const float inv = l > 0.f ? a.v_out_scale / l : 0.f;
+#pragma unroll
+        for (int i = 0; i < E; ++i) xo[i] *= inv;
+        if constexpr (T::VROT) {
+          fwht_wave<E>(xo, lane);
+#pragma unroll
+          for (int i = 0; i < E; ++i) xo[i] *= 0.0625f;
+        }
+        const int i2 = rr2 / a.G, h2 = h * a.G + (rr2 - i2 * a.G);
+        const int64_t orow = ((int64_t)b * a.n_q + i2) * a.H_q + h2;
+        float* op = a.out + orow * D + E * lane;
+#pragma unroll
+        for (int i = 0; i < E; ++i) op[i] = xo[i];
+        if (a.lse != nullptr && lane == 0)
+          a.lse[orow] = l > 0.f ? (M + __log2f(l)) * 0.69314718055994531f : NEG_INF;
+      }
+    }
+    x = seg_end;
+    __syncthreads();  // the next segment reuses the LDS areas
   }
 }
 
 // ----------------------------------------------------------- combine
+// One workgroup of D threads per (unit, row): thread t owns element t.
+// Units finished by the split kernel (one workgroup, write_direct) are
+// skipped; empty sequences get out = 0, lse = -inf.
 
 template <int D, bool VROT>
-__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a, int P, int H_kv) {
+__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a, int H_kv) {
   constexpr float NEG_INF = -__builtin_inff();
-  constexpr int E = D / 64;
-  const int lane = threadIdx.x & 63;
-  const int64_t rowid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t nrows = (int64_t)a.B * H_kv * a.R;
-  if (rowid >= nrows) return;
-  const int u = (int)(rowid / a.R), rr = (int)(rowid - (int64_t)u * a.R);
+  __shared__ float red[D];
+  const int t = threadIdx.x;
+  const int u = (int)(blockIdx.x / (unsigned)a.R), rr = (int)(blockIdx.x - (unsigned)u * a.R);
   const int b = u / H_kv, h = u - b * H_kv;
-  const int L = a.seq_lens[b];
-  const int npages = (L + P - 1) / P;
-  const int ns = (npages + a.pps - 1) / a.pps;
-  const float* ml = a.ws_ml + ((int64_t)u * a.nsplit * a.R + rr) * 2;
-  const float* po = a.ws_o + ((int64_t)u * a.nsplit * a.R + rr) * D + E * lane;
-  float M = NEG_INF;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[(int64_t)s * a.R * 2]);
-  float l = 0.f, x[E];
-#pragma unroll
-  for (int i = 0; i < E; ++i) x[i] = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float ms = ml[(int64_t)s * a.R * 2];
-    if (ms == NEG_INF) continue;
-    const float w = exp2f(ms - M);
-    l += w * ml[(int64_t)s * a.R * 2 + 1];
-    const float* os = po + (int64_t)s * a.R * D;
-#pragma unroll
-    for (int i = 0; i < E; ++i) x[i] += w * os[i];
-  }
-  const float inv = l > 0.f ? a.v_out_scale / l : 0.f;
-#pragma unroll
-  for (int i = 0; i < E; ++i) x[i] *= inv;
-  if constexpr (VROT) {
-    fwht_wave<E>(x, lane);
-#pragma unroll
-    for (int i = 0; i < E; ++i) x[i] *= 0.0625f;
-  }
   const int qi = rr / a.G, qh = h * a.G + (rr - qi * a.G);
   const int64_t orow = ((int64_t)b * a.n_q + qi) * a.H_q + qh;
-  float* op = a.out + orow * D + E * lane;
+  const int L = a.seq_lens[b];
+  const int nb = (L + 15) >> 4;
+  if (nb == 0) {
+    a.out[orow * D + t] = 0.f;
+    if (a.lse != nullptr && t == 0) a.lse[orow] = NEG_INF;
+    return;
+  }
+  const int total = a.ws_cum[a.B];
+  const int per = blocks_per_workgroup(total, a.nwg);
+  const int start = a.ws_cum[b] + h * nb;
+  const int wa = start / per, wb = (start + nb - 1) / per;
+  if (wa == wb && a.write_direct) return;
+  const float* ml = a.ws_ml + ((int64_t)(u + wa) * a.R + rr) * 2;
+  const float* po = a.ws_o + ((int64_t)(u + wa) * a.R + rr) * D + t;
+  const int nseg = wb - wa + 1;
+  const int64_t sml = (int64_t)a.R * 2, so = (int64_t)a.R * D;  // slot strides
+  // M = max over segments
+  float mloc = NEG_INF;
+  for (int s = t; s < nseg; s += D) mloc = fmaxf(mloc, ml[s * sml]);
+  red[t] = mloc;
+  __syncthreads();
+  for (int k = D / 2; k > 0; k >>= 1) {
+    if (t < k) red[t] = fmaxf(red[t], red[t + k]);
+    __syncthreads();
+  }
+  const float M = red[0];
+  __syncthreads();
+  float acc = 0.f, l = 0.f;
+  int s = 0;
+  for (; s + 4 <= nseg; s += 4) {
+    float ms[4], ls[4], os[4];
 #pragma unroll
-  for (int i = 0; i < E; ++i) op[i] = x[i];
-  if (a.lse != nullptr && lane == 0) a.lse[orow] = l > 0.f ? (M + __log2f(l)) * 0.69314718055994531f : NEG_INF;
+    for (int i = 0; i < 4; ++i) { ms[i] = ml[(s + i) * sml]; ls[i] = ml[(s + i) * sml + 1]; os[i] = po[(s + i) * so]; }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float wt = (ms[i] == NEG_INF) ? 0.f : exp2f(ms[i] - M);
+      l += wt * ls[i];
+      acc += wt * os[i];
+    }
+  }
+  for (; s < nseg; ++s) {
+    const float ms = ml[s * sml];
+    const float wt = (ms == NEG_INF) ? 0.f : exp2f(ms - M);
+    l += wt * ml[s * sml + 1];
+    acc += wt * po[s * so];
+  }
+  const float xo = l > 0.f ? acc * (a.v_out_scale / l) : 0.f;
+  if constexpr (VROT) {
+    red[t] = xo;
+    __syncthreads();
+    if (t < 64) {
+      constexpr int E = D / 64;
+      float xv[E];
+#pragma unroll
+      for (int i = 0; i < E; ++i) xv[i] = red[E * t + i];
+      fwht_wave<E>(xv, t);
+#pragma unroll
+      for (int i = 0; i < E; ++i) a.out[orow * D + E * t + i] = xv[i] * 0.0625f;
+    }
+  } else {
+    a.out[orow * D + t] = xo;
+  }
+  if (a.lse != nullptr && t == 0) a.lse[orow] = l > 0.f ? (M + __log2f(l)) * 0.69314718055994531f : NEG_INF;
 }
 
 // ----------------------------------------------------------- launchers
 
-template <int FMT, int D>
-static hipError_t launch_split_t(const Geometry& geo, const DecodeArgs& a, hipStream_t stream) {
-  const int units = a.B * geo.H_kv;
-  const int tiles = (a.R + 15) / 16;
-  hipLaunchKernelGGL((decode_split_kernel<FMT, D>), dim3((unsigned)a.nsplit * (unsigned)units, tiles), dim3(256), 0,
-                     stream, geo, a);
-  return hipGetLastError();
+#define KVQ_FOR_EACH_DECODE(X)                                                                     \
+  X(F_BF16, 128) X(F_BF16, 256) X(F_FP8_ROW, 128) X(F_FP8_ROW, 256) X(F_FP8_TENSOR, 128)          \
+  X(F_FP8_TENSOR, 256) X(F_MXFP8, 128) X(F_MXFP8, 256) X(F_INT8_G64, 256) X(F_NVFP4_G16, 256)   \
+  X(F_K8V4, 256)
+
+size_t decode_split_lds_bytes(const Geometry& geo, int B, int R) {
+#define KVQ_LDS_CASE(F, DD) \
+  if (geo.fmt == F && geo.D == DD) return split_lds_bytes<F, DD>(B, R);
+  KVQ_FOR_EACH_DECODE(KVQ_LDS_CASE)
+#undef KVQ_LDS_CASE
+  return 0;
+}
+
+hipError_t decode_split_occupancy(const Geometry& geo, int B, int R, int* blocks_per_cu) {
+  const size_t lds = decode_split_lds_bytes(geo, B, R);
+#define KVQ_OCC_CASE(F, DD)                                                                        \
+  if (geo.fmt == F && geo.D == DD)                                                                 \
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, decode_split_kernel<F, DD>, \
+                                                        256, lds);
+  KVQ_FOR_EACH_DECODE(KVQ_OCC_CASE)
+#undef KVQ_OCC_CASE
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode_split(const Geometry& geo, const DecodeArgs& a, hipStream_t stream) {
-#define KVQ_SPLIT_CASE(F, DD) \
-  if (geo.fmt == F && geo.D == DD) return launch_split_t<F, DD>(geo, a, stream);
-  KVQ_SPLIT_CASE(F_BF16, 128) KVQ_SPLIT_CASE(F_BF16, 256)
-  KVQ_SPLIT_CASE(F_FP8_ROW, 128) KVQ_SPLIT_CASE(F_FP8_ROW, 256)
-  KVQ_SPLIT_CASE(F_FP8_TENSOR, 128) KVQ_SPLIT_CASE(F_FP8_TENSOR, 256)
-  KVQ_SPLIT_CASE(F_MXFP8, 128) KVQ_SPLIT_CASE(F_MXFP8, 256)
-  KVQ_SPLIT_CASE(F_INT8_G64, 256) KVQ_SPLIT_CASE(F_NVFP4_G16, 256) KVQ_SPLIT_CASE(F_K8V4, 256)
+  const int tiles = (a.R + 15) / 16;
+  const size_t lds = decode_split_lds_bytes(geo, a.B, a.R);
+#define KVQ_SPLIT_CASE(F, DD)                                                                    \
+  if (geo.fmt == F && geo.D == DD) {                                                             \
+    hipLaunchKernelGGL((decode_split_kernel<F, DD>), dim3(a.nwg, tiles), dim3(256), lds, stream, geo, a); \
+    return hipGetLastError();                                                                    \
+  }
+  KVQ_FOR_EACH_DECODE(KVQ_SPLIT_CASE)
 #undef KVQ_SPLIT_CASE
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode_combine(const Geometry& geo, const DecodeArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.B * geo.H_kv * a.R;
-  const unsigned blocks = (unsigned)((rows + 3) / 4);
-  if (blocks == 0) return hipSuccess;
+  if (rows == 0) return hipSuccess;
   const bool vrot = v_rotated(geo.fmt);
   if (geo.D == 256 && vrot)
-    hipLaunchKernelGGL((decode_combine_kernel<256, true>), dim3(blocks), dim3(256), 0, stream, a, geo.P, geo.H_kv);
+    hipLaunchKernelGGL((decode_combine_kernel<256, true>), dim3((unsigned)rows), dim3(256), 0, stream, a, geo.H_kv);
   else if (geo.D == 256)
-    hipLaunchKernelGGL((decode_combine_kernel<256, false>), dim3(blocks), dim3(256), 0, stream, a, geo.P, geo.H_kv);
+    hipLaunchKernelGGL((decode_combine_kernel<256, false>), dim3((unsigned)rows), dim3(256), 0, stream, a, geo.H_kv);
   else if (geo.D == 128 && !vrot)
-    hipLaunchKernelGGL((decode_combine_kernel<128, false>), dim3(blocks), dim3(256), 0, stream, a, geo.P, geo.H_kv);
+    hipLaunchKernelGGL((decode_combine_kernel<128, false>), dim3((unsigned)rows), dim3(128), 0, stream, a, geo.H_kv);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -7,22 +7,38 @@
 
 namespace kvq {
 
-// Arguments of one decode launch (split or direct mode).
+// Arguments of one decode launch.
+//
+// Work is scheduled stream-K style: the token blocks (16 tokens) of every
+// (sequence b, kv head h) unit, units in order u = b * H_kv + h, form one
+// flat range of T blocks; workgroup w of the split kernel takes blocks
+// [w * per, (w + 1) * per), per = ceil(T / nwg).  A unit wholly inside one
+// workgroup's range can be finished there; a unit spread over workgroups
+// w_a..w_b leaves one partial (m, l, o) per workgroup, in slot u + w (the
+// pairs (u, w) visited form a monotone staircase, so u + w is unique), and
+// the combine kernel merges them.
 struct DecodeArgs {
   const uint8_t* pool;
   const uint16_t* q;          // [B][n_q][H_q][D] bf16
   const int32_t* block_table; // [B][max_pages]
   const int32_t* seq_lens;    // [B]
   int32_t B, n_q, H_q, G, R;  // G = H_q / H_kv, R = G * n_q rows per kv head
-  int32_t max_pages, pps, nsplit;
+  int32_t max_pages;
+  int32_t nwg;                // workgroups of the split kernel
   float qk_scale;             // softmax_scale * log2(e) (* k_scale for FP8_TENSOR)
   float v_out_scale;          // v_scale for FP8_TENSOR, else 1
-  float* ws_ml;               // split mode: [units][nsplit][R][2]
-  float* ws_o;                // split mode: [units][nsplit][R][D]
-  float* out;                 // direct mode: [B][n_q][H_q][D]
-  float* lse;                 // direct mode, nullable
-  int32_t direct;             // 1: one split per sequence, write out/lse directly
+  int32_t* ws_cum;            // [B + 1]: H_kv * (blocks of sequences 0..b-1), written by workgroup 0
+  float* ws_ml;               // [slots][R][2]: m (base 2), l
+  float* ws_o;                // [slots][R][D]: unnormalized o
+  float* out;                 // [B][n_q][H_q][D]
+  float* lse;                 // [B][n_q][H_q], nullable
+  int32_t write_direct;       // 1: finish units held by one workgroup in the split kernel
 };
+
+// LDS bytes of the split kernel for a batch of B sequences and R rows.
+size_t decode_split_lds_bytes(const Geometry& geo, int B, int R);
+// Workgroups of the split kernel that fit on one CU at once.
+hipError_t decode_split_occupancy(const Geometry& geo, int B, int R, int* blocks_per_cu);
 
 hipError_t launch_append(uint8_t* pool, const uint16_t* k, const uint16_t* v, int64_t T, const int32_t* slots,
                          const Geometry& geo, float k_scale, float v_scale, hipStream_t stream);

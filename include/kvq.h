@@ -118,11 +118,13 @@ kvq_status kvq_quantize_append(const kvq_cache_desc* desc, void* pool,
                                hipStream_t stream);
 
 /* Workspace bytes kvq_decode_attention / kvq_decode_split need for this
- * problem.  pages_per_split = 0 selects the library's own plan (the one
- * kvq_decode_attention uses); a positive value forces that split length. */
+ * problem.  num_workgroups = 0 selects the library's own plan (the one
+ * kvq_decode_attention uses: as many split workgroups as fit on the device
+ * at once, fewer for small problems); a positive value forces that count.
+ * Limits: batch <= 4096; (num_q_heads / num_kv_heads) * n_q <= 1024. */
 kvq_status kvq_decode_workspace_size(const kvq_cache_desc* desc, int32_t batch, int32_t n_q,
                                      int32_t num_q_heads, int32_t max_pages_per_seq,
-                                     int32_t pages_per_split, size_t* bytes);
+                                     int32_t num_workgroups, size_t* bytes);
 
 /* Decode attention over the compressed cache (NInfer guide: each generated
  * token attends over every cached K/V; Qwen FP8-KV article: several query
@@ -136,7 +138,8 @@ kvq_status kvq_decode_workspace_size(const kvq_cache_desc* desc, int32_t batch, 
  *  out           device fp32 [batch][n_q][num_q_heads][head_dim], written.
  *  lse           device fp32 [batch][n_q][num_q_heads] (natural log of the
  *                softmax denominator plus the max score), or NULL.
- *  workspace     device, >= kvq_decode_workspace_size(..., 0, ...) bytes.
+ *  workspace     device, 256-byte aligned, >= kvq_decode_workspace_size(..., 0, ...)
+ *                bytes; its contents on entry do not matter.
  * Query token i of sequence b sits at position seq_lens[b] - n_q + i and
  * attends to positions 0..that one (causal among the new tokens); query
  * head h reads kv head h / (num_q_heads / num_kv_heads).  A query with no
@@ -149,36 +152,49 @@ kvq_status kvq_decode_attention(const kvq_cache_desc* desc, const void* pool,
                                 float softmax_scale, float* out, float* lse,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* The two phases of kvq_decode_attention, for callers that combine partial
+/* The two phases of kvq_decode_attention, for callers that merge partial
  * results themselves (e.g. several devices each holding a range of a long
  * sequence's pages) or time them apart.
- * kvq_decode_split writes, for every (sequence b, kv head h, split s, row r)
- * with r = i * G + j (query token i, j-th query head of the group), the
- * partial maximum m (base-2 units of the scaled score), the partial
- * denominator l and the unnormalized output o[head_dim], all fp32:
- *   workspace = [units][splits][rows][2] (m, l) followed, at the next
- *   256-byte boundary, by [units][splits][rows][head_dim] (o),
- *   units = batch * num_kv_heads, splits = ceil(max_pages / pages_per_split)
- *   with pages_per_split as planned (or forced), rows = G * n_q.
- * Rotated V formats leave o in the rotated domain; kvq_decode_combine merges
- * the valid splits of each row, normalizes, undoes the rotation, and writes
- * out / lse exactly as kvq_decode_attention does. */
+ *
+ * Schedule: the 16-token blocks of all (sequence b, kv head h) units, in
+ * unit order u = b * num_kv_heads + h, form one range of T blocks;
+ * split workgroup w takes blocks [w * per, (w + 1) * per),
+ * per = max(ceil(T / num_workgroups), 128).  kvq_decode_split writes, for every unit u and every
+ * workgroup w that covers part of it, one partial per row r = i * G + j
+ * (query token i, j-th query head of the group) into slot u + w:
+ *   workspace = cum int32 [batch + 1] (cum[b] = num_kv_heads x blocks of
+ *   sequences before b), then at the next 256-byte boundary (m, l) fp32
+ *   [slots][rows][2], then at the next 256-byte boundary o fp32
+ *   [slots][rows][head_dim]; slots = batch * num_kv_heads + num_workgroups,
+ *   rows = G * n_q.  m is the running maximum in base-2 units of the scaled
+ *   score, l the softmax denominator relative to it, o the unnormalized
+ *   output (still rotated for NVFP4_G16 and K8V4).
+ * kvq_decode_combine merges each unit's partials, normalizes, undoes the
+ * rotation and writes out / lse exactly as kvq_decode_attention does; pass
+ * the same num_workgroups (0 = planned) and flags to both.
+ * flags & KVQ_SPLIT_WRITE_WHOLE_UNITS: a unit held entirely by one split
+ * workgroup is finished by the split phase (written to out / lse, which
+ * kvq_decode_split then needs) and the combine skips it; this is what
+ * kvq_decode_attention does.  Without it every unit leaves partials.
+ * kvq_decode_split takes out / lse only for that flag (NULL otherwise). */
+#define KVQ_SPLIT_WRITE_WHOLE_UNITS 1
 kvq_status kvq_decode_split(const kvq_cache_desc* desc, const void* pool, const void* q_bf16,
                             int32_t batch, int32_t n_q, int32_t num_q_heads,
                             const int32_t* block_table, int32_t max_pages_per_seq,
-                            const int32_t* seq_lens, float softmax_scale, int32_t pages_per_split,
+                            const int32_t* seq_lens, float softmax_scale, int32_t num_workgroups,
+                            int32_t flags, float* out, float* lse,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 kvq_status kvq_decode_combine(const kvq_cache_desc* desc, int32_t batch, int32_t n_q,
                               int32_t num_q_heads, int32_t max_pages_per_seq,
-                              const int32_t* seq_lens, int32_t pages_per_split,
+                              const int32_t* seq_lens, int32_t num_workgroups, int32_t flags,
                               const void* workspace, size_t workspace_bytes,
                               float* out, float* lse, hipStream_t stream);
 
-/* The split plan kvq_decode_attention uses for this problem on the current
- * device: pages per split and the number of splits of the longest sequence. */
+/* The plan kvq_decode_attention uses for this problem on the current device:
+ * split workgroups and partial slots. */
 kvq_status kvq_decode_plan(const kvq_cache_desc* desc, int32_t batch, int32_t n_q,
                            int32_t num_q_heads, int32_t max_pages_per_seq,
-                           int32_t* pages_per_split, int32_t* num_splits);
+                           int32_t* num_workgroups, int32_t* num_slots);
 
 #define KVQ_DEQUANT_STORED_DOMAIN 1
 

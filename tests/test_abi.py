@@ -92,22 +92,21 @@ def test_append_validation_enqueues_nothing():
     assert _status("kvq_quantize_append", ctypes.byref(d), ok, P(0x10008), ok, 5, ok, None) == 1  # k alignment
 
 
-def test_workspace_size_with_forced_split():
+def test_workspace_size_with_forced_workgroups():
     d = kvq.desc(1, 256, 64, 4, 100)
     sz = ctypes.c_size_t()
-    assert _status("kvq_decode_workspace_size", ctypes.byref(d), 3, 1, 24, 10, 4, ctypes.byref(sz)) == 0
-    units, nsplit, R = 3 * 4, 3, 6
-    ml = (units * nsplit * R * 2 * 4 + 255) // 256 * 256
-    assert sz.value == ml + units * nsplit * R * 256 * 4
-    # pages_per_split larger than the table is clamped to one split
-    assert _status("kvq_decode_workspace_size", ctypes.byref(d), 3, 1, 24, 10, 50, ctypes.byref(sz)) == 0
-    assert sz.value == (units * R * 2 * 4 + 255) // 256 * 256 + units * R * 256 * 4
+    assert _status("kvq_decode_workspace_size", ctypes.byref(d), 3, 1, 24, 10, 7, ctypes.byref(sz)) == 0
+    units, nwg, R = 3 * 4, 7, 6
+    slots = units + nwg
+    a256 = lambda n: (n + 255) // 256 * 256
+    assert sz.value == a256(4 * 4) + a256(slots * R * 2 * 4) + slots * R * 256 * 4
     bad = [(3, 0, 24, 10, 4), (3, 1, 0, 10, 4), (3, 1, 25, 10, 4), (-1, 1, 24, 10, 4), (3, 1, 24, 0, 4),
            (3, 1, 24, 10, -2)]
     for args in bad:
         assert _status("kvq_decode_workspace_size", ctypes.byref(d), *args, ctypes.byref(sz)) == 1, args
-    # too many rows per kv head
+    # too many rows per kv head, or too large a batch
     assert _status("kvq_decode_workspace_size", ctypes.byref(d), 1, 64, 4 * 32, 10, 4, ctypes.byref(sz)) == 2
+    assert _status("kvq_decode_workspace_size", ctypes.byref(d), 5000, 1, 24, 10, 4, ctypes.byref(sz)) == 2
 
 
 def test_decode_validation_enqueues_nothing():
@@ -121,7 +120,8 @@ def test_decode_validation_enqueues_nothing():
     def call(**kw):
         a = dict(args, **kw)
         return lib.kvq_decode_split(ctypes.byref(d), a["pool"], a["q"], a["B"], a["nq"], a["Hq"], a["bt"], a["mp"],
-                                    a["sl"], a["scale"], 4, a["ws"], a["wsb"], None)
+                                    a["sl"], a["scale"], 4, a.get("flags", 0), a["out"], a["lse"], a["ws"],
+                                    a["wsb"], None)
 
     assert call(B=0) == 0  # empty batch: nothing to do
     assert call(pool=None) == 1
@@ -131,11 +131,15 @@ def test_decode_validation_enqueues_nothing():
     assert call(ws=None) == 1
     assert call(q=P(0x100004)) == 1
     assert call(ws=P(0x100080)) == 1   # workspace must be 256-byte aligned
+    assert call(pool=P(0x100040)) == 1  # pool must be 128-byte aligned
     assert call(scale=float("nan")) == 1
     assert call(wsb=100) == 3
     assert call(Hq=22) == 1            # not a multiple of H_kv
+    assert call(flags=2) == 1          # unknown flag
+    assert call(flags=1, out=None) == 1  # finishing whole units needs out
     bad = kvq.desc(3, 128, 64, 4, 100)
-    assert lib.kvq_decode_split(ctypes.byref(bad), ok, ok, 2, 1, 24, ok, 10, ok, 0.1, 4, ok, 1 << 30, None) == 2
+    assert lib.kvq_decode_split(ctypes.byref(bad), ok, ok, 2, 1, 24, ok, 10, ok, 0.1, 4, 0, None, None, ok,
+                                1 << 30, None) == 2
 
 
 def test_dequant_validation():

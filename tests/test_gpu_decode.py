@@ -83,22 +83,29 @@ def test_mtp_short_sequences():
     assert np.all(out[0, :2] == 0)
 
 
-@pytest.mark.parametrize("fmt,cfg", [("INT8_G64", 2), ("NVFP4_G16", 3), ("MXFP8", 5)])
-def test_split_count_sweep_and_phases(fmt, cfg):
+@pytest.mark.parametrize("fmt,cfg", [("INT8_G64", 2), ("NVFP4_G16", 3), ("MXFP8", 5), ("K8V4", 4)])
+def test_workgroup_sweep_and_phases(fmt, cfg):
+    """Any number of split workgroups (ranges that cut units anywhere, one
+    workgroup holding many units, empty workgroups) gives the same answer,
+    through the two-phase API as through the one-call one."""
     c = W.make_case(cfg, fmt, device="cpu", B=3, lengths=[900, 450, 77] if cfg != 5 else [1100, 450, 77])
     bl = build(c)
     ref, ref_lse = oracle_attention(bl)
     q = c.q.cuda()
-    for pps in (1, 2, 3, 5, c.max_pages):
-        ws = kvq.alloc_workspace(kvq.workspace_size(bl.desc, c.B, c.n_q, c.H_q, c.max_pages, pps))
-        out = torch.full((c.B, c.n_q, c.H_q, c.D), float("nan"), device="cuda")
-        lse = torch.full((c.B, c.n_q, c.H_q), float("nan"), device="cuda")
-        note("split sweep", fmt, "pps", pps)
-        kvq.decode_split(bl.desc, bl.pool_gpu, q, bl.bt, bl.sl, c.softmax_scale, ws, pages_per_split=pps)
-        kvq.decode_combine(bl.desc, c.B, c.n_q, c.H_q, c.max_pages, bl.sl, ws, out, lse, pages_per_split=pps)
-        torch.cuda.synchronize()
-        assert_close(out.cpu().numpy(), ref, "%s pps=%d" % (fmt, pps))
-        assert_lse_close(lse.cpu().numpy(), ref_lse, "%s pps=%d" % (fmt, pps))
+    for nwg in (1, 2, 3, 7, 64, 333, 0):
+        for flags in (0, kvq.SPLIT_WRITE_WHOLE_UNITS):
+            ws = kvq.alloc_workspace(kvq.workspace_size(bl.desc, c.B, c.n_q, c.H_q, c.max_pages, nwg))
+            ws.fill_(0xFF)  # workspace contents on entry must not matter
+            out = torch.full((c.B, c.n_q, c.H_q, c.D), float("nan"), device="cuda")
+            lse = torch.full((c.B, c.n_q, c.H_q), float("nan"), device="cuda")
+            note("workgroup sweep", fmt, "nwg", nwg, "flags", flags)
+            kvq.decode_split(bl.desc, bl.pool_gpu, q, bl.bt, bl.sl, c.softmax_scale, ws, num_workgroups=nwg,
+                             flags=flags, out=out, lse=lse)
+            kvq.decode_combine(bl.desc, c.B, c.n_q, c.H_q, c.max_pages, bl.sl, ws, out, lse, num_workgroups=nwg,
+                               flags=flags)
+            torch.cuda.synchronize()
+            assert_close(out.cpu().numpy(), ref, "%s nwg=%d flags=%d" % (fmt, nwg, flags))
+            assert_lse_close(lse.cpu().numpy(), ref_lse, "%s nwg=%d flags=%d" % (fmt, nwg, flags))
 
 
 @pytest.mark.parametrize("fmt,cfg", [("K8V4", 4), ("FP8_ROW", 2)])
