@@ -47,6 +47,10 @@ struct DT {
   // Q operands kept in LDS (one ds_read_b128 per k-step) where registers
   // would otherwise spill; in registers elsewhere.
   static constexpr bool QLDS = true;
+  // Prefetch whole blocks into a second register buffer where it fits next
+  // to the O accumulators; otherwise reuse one buffer, loading the next
+  // block's K as soon as Q.K is done and its V as soon as P.V is done.
+  static constexpr bool DOUBLE_BUF = D == 128 || FMT == F_FP8_ROW || FMT == F_FP8_TENSOR;
   static constexpr int NT = D / 16;
   static constexpr int KCH = D * KBITS / 512;                       // 16-B K chunks per lane per block
   static constexpr int VCH = (VBITS == 16 ? 2 : 1) * NT * 4 / 16;   // 16-B V chunks per lane per block
@@ -85,21 +89,46 @@ __device__ __forceinline__ void load_words(uint32_t (&w)[N], const uint8_t* p) {
   }
 }
 
-// Load token block j of this split into registers.
+// Addresses of token block j (absolute block index within the unit).
+struct BlockAddr {
+  const uint8_t* hb;  // head block of the page holding block j
+  int bip;            // block index inside the page
+};
+__device__ __forceinline__ BlockAddr block_addr(const uint8_t* head0, const Geometry& geo, const cint32* bt_row,
+                                                int j) {
+  const int bpp_log2 = geo.P == 128 ? 3 : 2;  // 16-token blocks per page: 8 or 4
+  const int page = __builtin_amdgcn_readfirstlane(j >> bpp_log2);
+  BlockAddr r;
+  r.bip = j & ((1 << bpp_log2) - 1);
+  r.hb = head0 + (int64_t)bt_row[page] * geo.page_bytes;
+  return r;
+}
+
+// Load the K codes (and K scales) of token block j into registers.
 template <int FMT, int D>
-__device__ __forceinline__ void load_block(Buf<FMT, D>& buf, const uint8_t* head0, const Geometry& geo,
-                                           const cint32* bt_row, int page0, int j, int lane) {
+__device__ __forceinline__ void load_k(Buf<FMT, D>& buf, const uint8_t* head0, const Geometry& geo,
+                                       const cint32* bt_row, int j, int lane) {
   using T = DT<FMT, D>;
-  const int bpp = geo.P >> 4;
-  const int page = __builtin_amdgcn_readfirstlane(page0 + j / bpp);
-  const int bip = j - (j / bpp) * bpp;
-  const int64_t phys = bt_row[page];
-  const uint8_t* hb = head0 + phys * geo.page_bytes;
+  const BlockAddr ba = block_addr(head0, geo, bt_row, j);
   const int g = lane >> 4, c16 = lane & 15;
-  const uint8_t* kc = hb + geo.off_kc + (int64_t)bip * geo.kcode_blk;
-  const uint8_t* vc = hb + geo.off_vc + (int64_t)bip * geo.vcode_blk;
+  const uint8_t* kc = ba.hb + geo.off_kc + (int64_t)ba.bip * geo.kcode_blk;
 #pragma unroll
   for (int i = 0; i < T::KCH; ++i) buf.k[i] = *reinterpret_cast<const uint4*>(kc + i * 1024 + lane * 16);
+  if constexpr (T::KSW > 0) {
+    const uint8_t* ks = ba.hb + geo.off_ks + (int64_t)ba.bip * geo.kscale_blk;
+    const int off = T::KC == C_E2G16 ? c16 * 16 : g * (4 * T::KSW);
+    load_words(buf.ks, ks + off);
+  }
+}
+
+// Load the V codes (and V scales) of token block j into registers.
+template <int FMT, int D>
+__device__ __forceinline__ void load_v(Buf<FMT, D>& buf, const uint8_t* head0, const Geometry& geo,
+                                       const cint32* bt_row, int j, int lane) {
+  using T = DT<FMT, D>;
+  const BlockAddr ba = block_addr(head0, geo, bt_row, j);
+  const int g = lane >> 4, c16 = lane & 15;
+  const uint8_t* vc = ba.hb + geo.off_vc + (int64_t)ba.bip * geo.vcode_blk;
 #pragma unroll
   for (int q = 0; q < T::VCH; ++q) {
     if constexpr (T::VBITS == 4)
@@ -107,15 +136,17 @@ __device__ __forceinline__ void load_block(Buf<FMT, D>& buf, const uint8_t* head
     else
       buf.v[q] = *reinterpret_cast<const uint4*>(vc + q * 1024 + lane * 16);
   }
-  if constexpr (T::KSW > 0) {
-    const uint8_t* ks = hb + geo.off_ks + (int64_t)bip * geo.kscale_blk;
-    const int off = T::KC == C_E2G16 ? c16 * 16 : g * (4 * T::KSW);
-    load_words(buf.ks, ks + off);
-  }
   if constexpr (T::VSW > 0) {
-    const uint8_t* vs = hb + geo.off_vs + (int64_t)bip * geo.vscale_blk;
+    const uint8_t* vs = ba.hb + geo.off_vs + (int64_t)ba.bip * geo.vscale_blk;
     load_words(buf.vs, vs + g * (4 * T::VSW));
   }
+}
+
+template <int FMT, int D>
+__device__ __forceinline__ void load_block(Buf<FMT, D>& buf, const uint8_t* head0, const Geometry& geo,
+                                           const cint32* bt_row, int j, int lane) {
+  load_k<FMT, D>(buf, head0, geo, bt_row, j, lane);
+  load_v<FMT, D>(buf, head0, geo, bt_row, j, lane);
 }
 
 // ----------------------------------------------------------- operand expanders
@@ -185,15 +216,23 @@ __device__ __forceinline__ f32x4 qk_block(const Buf<FMT, D>& buf, const QOps<FMT
   f32x4 S = {0.f, 0.f, 0.f, 0.f};
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   if constexpr (T::KC == C_BF16) {
+    // two independent accumulator chains (even / odd k-steps)
+    f32x4 S1 = zero;
 #pragma unroll
-    for (int kk = 0; kk < T::KSTEPS; ++kk)
+    for (int kk = 0; kk < T::KSTEPS; kk += 2) {
       S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(buf.k[kk]), bitcast<bf16x8>(qo.get(kk, 0)), S, 0, 0, 0);
+      S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(buf.k[kk + 1]), bitcast<bf16x8>(qo.get(kk + 1, 0)), S1,
+                                                   0, 0, 0);
+    }
+    S += S1;
   } else if constexpr (T::KC == C_E4ROW || T::KC == C_E4TEN) {
+    f32x4 S1 = zero;
 #pragma unroll
     for (int i = 0; i < T::KCH; ++i) {
       S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_bf16(buf.k[i].x, buf.k[i].y), bitcast<bf16x8>(qo.get(2 * i, 0)), S, 0, 0, 0);
-      S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_bf16(buf.k[i].z, buf.k[i].w), bitcast<bf16x8>(qo.get(2 * i + 1, 0)), S, 0, 0, 0);
+      S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_bf16(buf.k[i].z, buf.k[i].w), bitcast<bf16x8>(qo.get(2 * i + 1, 0)), S1, 0, 0, 0);
     }
+    S += S1;
     if constexpr (T::KC == C_E4ROW) {
       // one fp16 scale per token: tokens 4g..4g+3 in ks[0] (lo, hi), ks[1]
       S[0] *= f16_bits_to_f32(buf.ks[0] & 0xFFFFu);
@@ -240,6 +279,7 @@ __device__ __forceinline__ f32x4 qk_block(const Buf<FMT, D>& buf, const QOps<FMT
     // E2M1 x UE4M3 is exact in f16: fold the group scale into the operand.
     // lane (g, t): k-step kk covers d in [32kk + 8g, +8) -> group 2kk + g/2
     const int gb = (lane >> 5) & 1;
+    f32x4 Slo = zero;
 #pragma unroll
     for (int i = 0; i < T::KCH; ++i) {
 #pragma unroll
@@ -250,10 +290,12 @@ __device__ __forceinline__ f32x4 qk_block(const Buf<FMT, D>& buf, const QOps<FMT
         const _Float16 s = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)sb, 1.0f, false)[0];
         f16x8 a = e2m1x8_f16(word(buf.k[i], hh));
         a *= s;
+        // hi and lo parts of q in separate chains
         S = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bitcast<f16x8>(qo.get(kk, 0)), S, 0, 0, 0);
-        S = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bitcast<f16x8>(qo.get(kk, 1)), S, 0, 0, 0);
+        Slo = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bitcast<f16x8>(qo.get(kk, 1)), Slo, 0, 0, 0);
       }
     }
+    S += Slo;
   }
   return S;
 }
@@ -343,6 +385,10 @@ __device__ __forceinline__ void fwht_wave(float (&x)[E], int lane) {
     }
   }
 }
+
+// 2^x with the hardware exp: results below 2^-126 flush to zero, which only
+// drops probabilities far below anything that can change an fp32 sum
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ----------------------------------------------------------- tail blocks
 
@@ -598,21 +644,22 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
 #pragma unroll
     for (int nt = 0; nt < T::NT; ++nt) O[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto process = [&](Buf<FMT, D>& buf, int jb) {
+    auto qk_phase = [&](const Buf<FMT, D>& buf, int jb, float (&sc)[4]) {
       const int t0 = 16 * jb;
-      if (t0 + 16 > L) clear_tail<FMT, D>(buf, L - t0, g);
       __builtin_amdgcn_sched_barrier(0);
       const f32x4 S = qk_block<FMT, D>(buf, qo, lane);
       __builtin_amdgcn_sched_barrier(0);
-      float sc[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) sc[e] = (t0 + 4 * g + e <= limit) ? S[e] * crow : NEG_INF;
+    };
+    auto pv_phase = [&](Buf<FMT, D>& buf, int jb, const float (&sc)[4]) {
+      const int t0 = 16 * jb;
       float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
       bm = fmaxf(bm, __shfl_xor(bm, 16));
       bm = fmaxf(bm, __shfl_xor(bm, 32));
       if (__any(bm > m_run)) {  // rare after the first blocks: rescale l and O
         const float m_new = fmaxf(m_run, bm);
-        const float corr = (m_new > m_run) ? exp2f(m_run - m_new) : 1.0f;
+        const float corr = (m_new > m_run) ? fast_exp2(m_run - m_new) : 1.0f;
         l_run *= corr;
         float ce[4];
 #pragma unroll
@@ -629,10 +676,11 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
       float p[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        p[e] = exp2f(sc[e] - m_use);
+        p[e] = fast_exp2(sc[e] - m_use);
         l_run += p[e];
       }
       const f16x4 P = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+      if (t0 + 16 > L) clear_tail<FMT, D>(buf, L - t0, g);
       // keep the compiler from hoisting every V conversion ahead of the
       // products (it would hold all of them live and spill)
 #pragma unroll
@@ -644,18 +692,35 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
     };
 
     {
-      Buf<FMT, D> A, Bb;
       const int jend = blk0 + nblk;
       int j = blk0 + wave;
-      if (j < jend) load_block<FMT, D>(A, head0, geo, bt_row, 0, j, lane);
-      while (j < jend) {
-        if (j + 4 < jend) load_block<FMT, D>(Bb, head0, geo, bt_row, 0, j + 4, lane);
-        process(A, j);
-        j += 4;
-        if (j >= jend) break;
-        if (j + 4 < jend) load_block<FMT, D>(A, head0, geo, bt_row, 0, j + 4, lane);
-        process(Bb, j);
-        j += 4;
+      if constexpr (T::DOUBLE_BUF) {
+        Buf<FMT, D> A, Bb;
+        float sc[4];
+        if (j < jend) load_block<FMT, D>(A, head0, geo, bt_row, j, lane);
+        while (j < jend) {
+          if (j + 4 < jend) load_block<FMT, D>(Bb, head0, geo, bt_row, j + 4, lane);
+          qk_phase(A, j, sc);
+          pv_phase(A, j, sc);
+          j += 4;
+          if (j >= jend) break;
+          if (j + 4 < jend) load_block<FMT, D>(A, head0, geo, bt_row, j + 4, lane);
+          qk_phase(Bb, j, sc);
+          pv_phase(Bb, j, sc);
+          j += 4;
+        }
+      } else {
+        Buf<FMT, D> A;
+        float sc[4];
+        if (j < jend) load_block<FMT, D>(A, head0, geo, bt_row, j, lane);
+        while (j < jend) {
+          const int jn = j + 4;
+          qk_phase(A, j, sc);
+          if (jn < jend) load_k<FMT, D>(A, head0, geo, bt_row, jn, lane);
+          pv_phase(A, j, sc);
+          if (jn < jend) load_v<FMT, D>(A, head0, geo, bt_row, jn, lane);
+          j = jn;
+        }
       }
     }
 
