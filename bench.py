@@ -4,21 +4,40 @@ A step is the whole hot path over one batch: quantize-append of each
 sequence's newest token (K and V of every kv head, through the codec and the
 Hadamard rotation where the format has it), then split-K decode attention
 over every cached page and the cross-split combine.  Inputs are resident in
-HBM before timing starts.  The default workload is the batched decode:
+HBM before timing starts, and before every timed step a 1 GiB read evicts
+the L2 caches and the 256 MB MALL, so each step streams the cache from HBM
+as it would between two layers of a model (``--no-flush`` times the steps
+back to back instead).  The default workload is the batched decode:
 32 sequences with contexts drawn uniformly from 8K-32K tokens, 24 query /
 4 KV heads, head_dim 256, 64-token pages, for each of INT8-G64, FP8 row-256
 and per-tensor FP8 (the headline value is INT8-G64).
+
+The write path is measured on its own workload: one 2048-token prefill chunk
+for each of 64 mixed-length sequences (log-uniform 1K-128K cached tokens,
+chunks starting mid-page), K8V4 first, then the other formats at that shape.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload batched]
 
 Prints one JSON line.  ``value`` is effective compressed-KV bandwidth:
 sum_b H_kv * L_b * bytes_per_token / ms_per_step.  ``roofline`` prices the
 dominant kernel (the split kernel) against the 8 TB/s HBM peak with its
-average duration measured by HIP events on its own stream; ``cpu_baseline``
-times the CPU oracle on a bounded sample of the same workload.
+average duration measured by HIP events on its own stream, next to the read
+rate a plain streaming kernel reaches on the same device; its ``traffic``
+comes from committed HBM byte counters, only while the kernel sources still
+hash to what was profiled.  ``cpu_baseline`` times the CPU oracle on a
+bounded sample of the same workload.
+
+    python bench.py --summarize-counters FETCH_DIR WRITE_DIR --bench-json FILE
+
+turns two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE)
+into that traffic record: per-dispatch KiB of the split kernel, scaled by
+what the same counters read for the probe's copy kernel of known size.
 """
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
@@ -35,6 +54,13 @@ import decode_attention_quant_amd as kvq  # noqa: E402
 import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+FLUSH_BYTES = 1 << 30          # read before each timed step: 4x the 256 MB MALL
+RATE_BYTES = 4 << 30           # buffer of the streaming-rate measurement
+COPY_BYTES = RATE_BYTES // 2   # bytes each way of the probe's copy
+APPEND_CHUNK = 2048
+APPEND_FORMATS = ["K8V4", "BF16", "INT8_G64", "FP8_ROW", "NVFP4_G16", "FP8_TENSOR"]
+CSRC = os.path.join(ROOT, "decode_attention_quant_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_traffic.json")
 METRIC = "decode-attn effective KV GB/s (% of HBM peak) per kv-dtype; quant-append tok/s"
 
 WORKLOADS = {
@@ -101,9 +127,56 @@ class Setup:
             ev[3].record(stream)
 
 
-def time_steps(s, steps, warmup, stream):
+class Probe:
+    """The streaming kernels of libkvq_probe.so; a 1 GiB buffer to flush with."""
+
+    def __init__(self):
+        from decode_attention_quant_amd import probe
+        self.p = probe
+        probe.library()
+        self.buf = torch.ones(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        self.sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+
+    def flush(self, stream):
+        self.p.read(self.buf, self.sink, stream)
+
+    def rates(self, stream, reps=10):
+        """Median GB/s of the read scan over 4 GiB and of a 2 GiB copy (read
+        + write counted), on a buffer freed afterwards."""
+        buf = torch.ones(RATE_BYTES, dtype=torch.uint8, device="cuda")
+        rd, cp = [], []
+        with torch.cuda.stream(stream):
+            for i in range(reps + 2):
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                e[0].record(stream)
+                self.p.read(buf, self.sink, stream)
+                e[1].record(stream)
+                self.p.copy(buf[COPY_BYTES:], buf[:COPY_BYTES], stream)
+                e[2].record(stream)
+                torch.cuda.synchronize()
+                if i >= 2:
+                    rd.append(RATE_BYTES / (e[0].elapsed_time(e[1]) * 1e-3) / 1e9)
+                    cp.append(2 * COPY_BYTES / (e[1].elapsed_time(e[2]) * 1e-3) / 1e9)
+        del buf
+        torch.cuda.empty_cache()
+        return float(np.median(rd)), float(np.median(cp))
+
+
+def _stats(x):
+    return {"mean": float(np.mean(x)), "median": float(np.median(x)), "p10": float(np.percentile(x, 10)),
+            "p90": float(np.percentile(x, 90))}
+
+
+def time_steps(s, steps, warmup, stream, probe=None):
+    """Per-step HIP-event times (ms) of the step and of its three launches.
+
+    With a probe, its cache-evicting read runs before each step, outside
+    the step's events; the wall time between the first and last step then
+    includes those reads."""
     with torch.cuda.stream(stream):
         for _ in range(warmup):
+            if probe is not None:
+                probe.flush(stream)
             s.step(stream)
         torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
@@ -111,15 +184,132 @@ def time_steps(s, steps, warmup, stream):
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
         t0.record(stream)
         for i in range(steps):
+            if probe is not None:
+                probe.flush(stream)
             s.step(stream, evs[i])
         t1.record(stream)
         torch.cuda.synchronize()
-        total = t0.elapsed_time(t1)
-        app = [e[0].elapsed_time(e[1]) for e in evs]
-        dec = [e[1].elapsed_time(e[2]) for e in evs]   # split kernel
-        comb = [e[2].elapsed_time(e[3]) for e in evs]
-    return total / steps, float(np.mean(app)), float(np.mean(dec)), float(np.mean(comb)), \
-        float(np.percentile(dec, 10)), float(np.percentile(dec, 90))
+    return {
+        "wall": t0.elapsed_time(t1) / steps,
+        "step": _stats([e[0].elapsed_time(e[3]) for e in evs]),
+        "append": _stats([e[0].elapsed_time(e[1]) for e in evs]),
+        "split": _stats([e[1].elapsed_time(e[2]) for e in evs]),
+        "combine": _stats([e[2].elapsed_time(e[3]) for e in evs]),
+    }
+
+
+def append_chunk_bench(formats, stream, probe, reps=10):
+    """Quantize-append of one 2048-token chunk per sequence of the mixed-length
+    workload (64 sequences, chunks starting mid-page): tok/s and GB/s moved,
+    against the HBM roof T * H_kv * (4 D + bytes_per_token) / 8 TB/s."""
+    res = {}
+    for fmt in formats:
+        c = W.make_case(4, fmt, device="cuda", reserve=APPEND_CHUNK)
+        c.k = c.v = None  # only the new chunk is written
+        d = kvq.desc(c.fmt, c.D, c.P, c.H_kv, c.num_pages, 1.0, 1.0)
+        if fmt == "FP8_TENSOR":  # the cached tensors' calibrated scales
+            d = kvq.desc(c.fmt, c.D, c.P, c.H_kv, c.num_pages, c.k_scale, c.v_scale)
+        pool = kvq.alloc_pool(d)
+        k, v, slots = W.append_chunk(c, APPEND_CHUNK, device="cuda")
+        T = k.shape[0]
+        bpt = kv_bytes_per_token(d)
+        moved = T * c.H_kv * (4 * c.D + bpt)
+        ts = []
+        with torch.cuda.stream(stream):
+            for i in range(reps + 2):
+                probe.flush(stream)
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                e[0].record(stream)
+                kvq.quantize_append(d, pool, k, v, slots, stream=stream)
+                e[1].record(stream)
+                if i >= 2:
+                    ts.append(e)
+            torch.cuda.synchronize()
+        ms = float(np.median([e[0].elapsed_time(e[1]) for e in ts]))
+        roof = HBM_PEAK_GBS * 1e9 / (c.H_kv * (4 * c.D + bpt))
+        res[fmt] = {"tokens": T, "ms": ms, "tok_per_s": T / (ms * 1e-3), "GB_per_s": moved / (ms * 1e-3) / 1e9,
+                    "roof_tok_per_s": roof, "frac_of_roof": T / (ms * 1e-3) / roof}
+        print("[bench] append %s: %d tokens in %.3f ms, %.1f M tok/s (%.1f%% of the HBM roof), %.0f GB/s" % (
+            fmt, T, ms, T / ms / 1e3, 100 * res[fmt]["frac_of_roof"], res[fmt]["GB_per_s"]),
+            file=sys.stderr, flush=True)
+        del pool, k, v, slots, c
+        torch.cuda.empty_cache()
+    return res
+
+
+def kernel_sources_sha():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        h.update(f.encode())
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload, fmt):
+    """HBM bytes per split-kernel launch from the committed counter summary,
+    or None when it is for another workload or the kernels changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as fh:
+        t = json.load(fh)
+    if t.get("sources_sha256") != kernel_sources_sha() or t.get("workload") != workload or t.get("kv_dtype") != fmt:
+        return None
+    return t["traffic_bytes_per_launch"]
+
+
+def _counter_means(folder, counter):
+    """Mean per-dispatch value of ``counter`` by kernel name, from rocprofv3 CSVs."""
+    vals = {}
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under %s" % folder)
+    for f in files:
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                if row.get("Counter_Name") != counter:
+                    continue
+                key = (row["Kernel_Name"], row.get("Dispatch_Id", len(vals)))
+                vals[key] = vals.get(key, 0.0) + float(row["Counter_Value"])
+    by_kernel = {}
+    for (name, _), v in vals.items():
+        by_kernel.setdefault(name, []).append(v)
+    return {k: (float(np.mean(v)), len(v)) for k, v in by_kernel.items()}
+
+
+def summarize_counters(fetch_dir, write_dir, bench_json):
+    with open(bench_json) as fh:
+        line = json.loads([ln for ln in fh if ln.startswith("{")][-1])
+    fmt = line["config"]["kv_dtype"]
+    fetch = _counter_means(fetch_dir, "FETCH_SIZE")
+    write = _counter_means(write_dir, "WRITE_SIZE")
+
+    def pick(table, needle):
+        hits = [(k, v) for k, v in table.items() if needle in k]
+        if len(hits) != 1:
+            raise SystemExit("expected one kernel matching %r, found %s" % (needle, [k for k, _ in hits]))
+        return hits[0]
+
+    split_name = "decode_split_kernel<%d, %d>" % (kvq.FORMATS[fmt], line["config"]["head_dim"])
+    kname, (f_kib, n_f) = pick(fetch, split_name)
+    _, (w_kib, n_w) = pick(write, split_name)
+    _, (cf_kib, _) = pick(fetch, "kvq_probe::copy_kernel")
+    _, (cw_kib, _) = pick(write, "kvq_probe::copy_kernel")
+    copy_bytes = COPY_BYTES
+    rf, wf = copy_bytes / 1024.0 / cf_kib, copy_bytes / 1024.0 / cw_kib
+    traffic = (f_kib * rf + w_kib * wf) * 1024.0
+    kv = line["per_kv_dtype"][fmt]["kv_bytes"]
+    return {
+        "kernel": kname, "workload": line["config"]["workload_name"], "kv_dtype": fmt,
+        "sources_sha256": kernel_sources_sha(),
+        "split_dispatches": [n_f, n_w],
+        "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib,
+        "copy_kernel_bytes_each_way": copy_bytes, "copy_fetch_kib": cf_kib, "copy_write_kib": cw_kib,
+        "read_scale": rf, "write_scale": wf,
+        "traffic_bytes_per_launch": traffic,
+        "algorithmic_kv_bytes_per_launch": kv,
+        "traffic_over_algorithmic": traffic / kv,
+    }
 
 
 def cpu_baseline(s, budget_s=10.0):
@@ -165,9 +355,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="batched", choices=sorted(WORKLOADS))
     ap.add_argument("--formats", default=None, help="comma-separated subset of the workload's formats")
+    ap.add_argument("--append-formats", default=",".join(APPEND_FORMATS),
+                    help="formats of the prefill-chunk append measurement, or 'none'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true", help="time steps back to back, caches warm")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--bench-json")
     args = ap.parse_args()
+    if args.summarize_counters:
+        print(json.dumps(summarize_counters(*args.summarize_counters, args.bench_json), indent=1))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build runs the hot path on a single device and has no "
               "multi-GPU mode; run with --gpus 1", file=sys.stderr)
@@ -179,29 +377,36 @@ def main():
     wl = WORKLOADS[args.workload]
     formats = args.formats.split(",") if args.formats else wl["formats"]
     stream = torch.cuda.Stream()
+    probe = Probe()
+    read_gbs, copy_gbs = probe.rates(stream)
+    print("[bench] streaming read %.0f GB/s, copy %.0f GB/s (read + write)" % (read_gbs, copy_gbs),
+          file=sys.stderr, flush=True)
+    flush = None if args.no_flush else probe
     per = {}
     primary = None
     for fmt in formats:
         print("[bench] %s %s: building the cache" % (args.workload, fmt), file=sys.stderr, flush=True)
         s = Setup(wl["config"], fmt)
-        ms, app_ms, split_ms, comb_ms, p10, p90 = time_steps(s, args.steps, args.warmup, stream)
+        t = time_steps(s, args.steps, args.warmup, stream, flush)
+        ms = t["step"]["mean"] if flush is not None else t["wall"]
         c = s.case
         res = {
             "GB_per_s": s.kv_bytes / (ms * 1e-3) / 1e9,
             "pct_of_hbm_peak": 100.0 * s.kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "ms_per_step": ms,
+            "step_ms": t["step"], "wall_ms_per_step": t["wall"],
             "kv_bytes": s.kv_bytes,
             "bytes_per_token": s.bpt,
-            "split_kernel_ms": split_ms, "split_kernel_ms_p10": p10, "split_kernel_ms_p90": p90,
-            "combine_ms": comb_ms,
-            "append_ms": app_ms,
-            "append_tok_per_s": c.B / (app_ms * 1e-3),
+            "split_kernel_ms": t["split"], "combine_ms": t["combine"], "step_append_ms": t["append"],
+            "step_append_tok_per_s": c.B / (t["append"]["mean"] * 1e-3),
             "split_workgroups": s.nwg, "partial_slots": s.slots,
         }
         per[fmt] = res
-        print("[bench] %s %s: %.1f GB/s (%.1f%% of peak), step %.3f ms, split %.3f ms, combine %.3f ms, "
-              "append %.3f ms" % (args.workload, fmt, res["GB_per_s"], res["pct_of_hbm_peak"], ms, split_ms,
-                                  comb_ms, app_ms), file=sys.stderr, flush=True)
+        print("[bench] %s %s: %.1f GB/s (%.1f%% of peak), step %.3f ms, split %.3f ms (p10 %.3f p90 %.3f), "
+              "combine %.3f ms, append %.3f ms" % (
+                  args.workload, fmt, res["GB_per_s"], res["pct_of_hbm_peak"], ms, t["split"]["mean"],
+                  t["split"]["p10"], t["split"]["p90"], t["combine"]["mean"], t["append"]["mean"]),
+              file=sys.stderr, flush=True)
         if primary is None:
             primary = (fmt, s, res)
         else:
@@ -209,7 +414,10 @@ def main():
             torch.cuda.empty_cache()
     fmt, s, res = primary
     c = s.case
-    achieved = s.kv_bytes / (res["split_kernel_ms"] * 1e-3) / 1e9
+    split_ms = res["split_kernel_ms"]["mean"]
+    achieved = s.kv_bytes / (split_ms * 1e-3) / 1e9
+    append_formats = [] if args.append_formats == "none" else args.append_formats.split(",")
+    appends = append_chunk_bench(append_formats, stream, probe) if append_formats else {}
     line = {
         "metric": METRIC,
         "value": res["GB_per_s"],
@@ -223,17 +431,22 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": wl["label"], "kv_dtype": fmt, "batch": c.B, "n_q": c.n_q, "num_q_heads": c.H_q,
-                   "num_kv_heads": c.H_kv, "head_dim": c.D, "page_size": c.P,
-                   "cached_tokens": int(c.seq_lens.astype(np.int64).sum()),
-                   "split_workgroups": s.nwg},
+        "config": {"workload": wl["label"], "workload_name": args.workload, "kv_dtype": fmt, "batch": c.B,
+                   "n_q": c.n_q, "num_q_heads": c.H_q, "num_kv_heads": c.H_kv, "head_dim": c.D,
+                   "page_size": c.P, "cached_tokens": int(c.seq_lens.astype(np.int64).sum()),
+                   "split_workgroups": s.nwg, "cache_flush_between_steps": flush is not None},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "decode_split_kernel<%s>" % fmt, "kernel_ms": res["split_kernel_ms"]},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(args.workload, fmt),
+                     "kernel": "decode_split_kernel<%s>" % fmt, "kernel_ms": split_ms,
+                     "algorithmic_bytes_per_launch": s.kv_bytes,
+                     "measured_streaming_read_GBs": read_gbs, "frac_of_measured_read": achieved / read_gbs,
+                     "measured_copy_GBs": copy_gbs},
         "pct_of_hbm_peak": res["pct_of_hbm_peak"],
-        "quant_append": {"tokens_per_step": c.B, "tok_per_s": res["append_tok_per_s"], "ms": res["append_ms"]},
-        "per_kv_dtype": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
-                         for k, v in per.items()},
+        "quant_append": ({"workload": "64 sequences x one %d-token prefill chunk (mixed lengths 1K-128K, "
+                                      "chunks start mid-page), 4 kv heads, head_dim 256" % APPEND_CHUNK,
+                          "kv_dtype": append_formats[0], **appends[append_formats[0]],
+                          "per_kv_dtype": appends} if appends else None),
+        "per_kv_dtype": per,
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) on %s" % fmt, file=sys.stderr, flush=True)

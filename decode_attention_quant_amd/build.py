@@ -1,11 +1,12 @@
-"""Build the HIP library libkvq.so in place (gfx950).
+"""Build the HIP libraries in place (gfx950).
 
     python -m decode_attention_quant_amd.build
 
-Every source in csrc/ is compiled by hipcc for gfx950 and linked into one
-shared library next to this file.  Packed fp32 VALU instructions are turned
-off (``-packed-fp32-ops``); fp32 denormals and IEEE division stay at the
-HIP defaults, which the bit-exact encoders rely on.
+Every source in csrc/ is compiled by hipcc for gfx950 and linked into
+libkvq.so next to this file; probe/ (streaming kernels that calibrate
+measurements, not part of the kvq ABI) becomes libkvq_probe.so.  Packed fp32
+VALU instructions are turned off (``-packed-fp32-ops``); fp32 denormals and
+IEEE division stay at the HIP defaults, which the bit-exact encoders rely on.
 """
 
 import os
@@ -15,11 +16,13 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvq.so")
+PROBE_SRC = os.path.join(HERE, "probe")
+PROBE_LIB = os.path.join(HERE, "libkvq_probe.so")
 ARCH = os.environ.get("KVQ_OFFLOAD_ARCH", "gfx950")
 
 
-def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+def sources(folder=CSRC):
+    return sorted(os.path.join(folder, f) for f in os.listdir(folder) if f.endswith(".hip"))
 
 
 def hipcc():
@@ -29,7 +32,14 @@ def hipcc():
 
 
 def build(verbose=False, jobs=8):
-    """Compile every csrc/*.hip to an object, then link libkvq.so."""
+    """Compile and link libkvq.so and libkvq_probe.so; returns libkvq.so's path."""
+    _build_lib(sources(CSRC), LIB, verbose, jobs)
+    _build_lib(sources(PROBE_SRC), PROBE_LIB, verbose, jobs)
+    return LIB
+
+
+def _build_lib(srcs, lib, verbose, jobs):
+    """Compile each source to an object under _build/, then link ``lib``."""
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     common = [
@@ -39,7 +49,7 @@ def build(verbose=False, jobs=8):
         "-I" + os.path.join(HERE, "..", "include"), "-I" + CSRC,
     ]
     procs, objs = [], []
-    for src in sources():
+    for src in srcs:
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
         objs.append(obj)
         cmd = [hipcc()] + common + ["-c", src, "-o", obj]
@@ -59,13 +69,13 @@ def build(verbose=False, jobs=8):
         for src, out in failed:
             sys.stderr.write("---- %s\n%s\n" % (src, out))
         raise RuntimeError("hipcc failed for %s" % ", ".join(os.path.basename(s) for s, _ in failed))
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -152,3 +152,31 @@ def test_dequant_validation():
     assert lib.kvq_dequant_page(ctypes.byref(d), ok, 0, 2, ok, ok, None) == 1    # unknown flag
     assert lib.kvq_dequant_page(ctypes.byref(d), None, 0, 1, ok, ok, None) == 1
     assert lib.kvq_dequant_page(ctypes.byref(d), ok, 0, 1, P(0x100004), ok, None) == 1
+
+
+# ---- libkvq_probe.so: the measurement kernels' C ABI (kvq_probe.h)
+
+PROBE_HEADER = os.path.join(ROOT, "include", "kvq_probe.h")
+
+
+def test_probe_header_matches_exports():
+    from decode_attention_quant_amd import probe
+    fns = sorted(set(re.findall(r"^int\s+(kvq_probe_\w+)\s*\(", open(PROBE_HEADER).read(), re.M)))
+    assert fns == sorted(probe.EXPORTS)
+    lib = probe.library()
+    for name in fns:
+        assert hasattr(lib, name), name
+
+
+def test_probe_rejects_bad_arguments_on_the_host():
+    from decode_attention_quant_amd import probe
+    lib = probe.library()
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
+    assert lib.kvq_probe_read(None, 1024, fake, None) == 1
+    assert lib.kvq_probe_read(fake, 1000, fake, None) == 1          # not whole 1 KB chunks
+    assert lib.kvq_probe_read(ctypes.c_void_p((1 << 20) + 8), 1024, fake, None) == 1  # misaligned
+    assert lib.kvq_probe_read(fake, 1024, None, None) == 1
+    assert lib.kvq_probe_copy(fake, fake, 24, None) == 1            # not whole 16 B words
+    assert lib.kvq_probe_copy(None, fake, 32, None) == 1
+    assert lib.kvq_probe_read(fake, 0, fake, None) == 0             # empty: nothing to do
+    assert lib.kvq_probe_copy(fake, fake, 0, None) == 0
