@@ -4,26 +4,34 @@
 // stored per token set the speed (NInfer KV-cache guide, section on why the
 // cache is quantized; Qwen FP8-KV article, bandwidth section).  This kernel
 // therefore streams each page plane exactly once with 16-byte loads and does
-// the rest in registers:
+// the rest in registers.
 //
-//  grid (split s + nsplit * unit u, row tile), u = b * H_kv + h: one workgroup of 4 waves
-//  walks pages [s*pps, (s+1)*pps) of sequence b, kv head h.  The rows of the
-//  workgroup are the R = G * n_q query rows sharing that kv head (GQA group
-//  times MTP tokens, up to 16 per tile).  Wave w takes token blocks
-//  w, w+4, ... (16 tokens each) and keeps its own online-softmax state.
+// Schedule (stream-K): the 16-token blocks of every (sequence b, kv head h)
+// unit, u = b * H_kv + h, form one flat range; workgroup x of the grid
+// (x, row tile) takes an equal slice of it (at least 128 blocks), so every
+// workgroup streams the same number of bytes whatever the length mix.  A
+// unit wholly inside one slice is finished in place (normalized, V rotated
+// back, lse written); a unit cut by slice ends leaves one partial (m, l, o)
+// per slice for decode_combine_kernel.  The rows of a workgroup are the
+// R = G * n_q query rows sharing one kv head (GQA group times MTP tokens,
+// 16 per row tile).  Of its 4 waves, wave w takes blocks w, w + 4, ... and
+// keeps its own online-softmax state; the waves merge through LDS.
 //
-//  per token block (one wave):
-//    S (16 tokens x 16 rows) = K_blk . Q^T with v_mfma_f32_16x16x32_{bf16,f16}:
-//      K codes are expanded to bf16 / f16 exactly (E4M3, int8 and
-//      E2M1 x UE4M3 values are exact there); row / group scales multiply
-//      the fp32 partial sums; rotated formats use Q' = H q / 16 split into
-//      f16 hi + lo parts (two MFMAs) so q keeps ~22 bits.
-//    online softmax in base 2 (exp2), masking t >= L and the MTP causal rule.
-//    O (16 rows x D) += P . V_blk with v_mfma_f32_16x16x16_f16; V codes are
-//      expanded to f16 with their scale folded in (one rounding).
-//  The 4 waves merge through LDS; the workgroup writes either partial
-//  (m, l, o) for the combine kernel, or, with one split per sequence, the
-//  normalized output directly (un-rotating V for NVFP4 / K8V4).
+// Per token block (one wave, 16 tokens x 16 rows):
+//   S = K_blk . Q^T on the matrix cores, K codes expanded exactly:
+//     BF16            bf16 K x bf16 q               (16x16x32 bf16)
+//     FP8 row/tensor  E4M3 -> bf16 (exact) x bf16 q; row scale on S
+//     MXFP8           E4M3 -> bf16 x bf16 q per 32-wide k-step, scaled by
+//                     2^e of that group before summing
+//     INT8-G64        int8 K x rotated q in two int8 digits (16x16x64 i8),
+//                     group scale on each 64-wide integer partial sum
+//     NVFP4 (K)       E2M1 x UE4M3 -> f16 (exact) x rotated q as f16 hi + lo
+//   online softmax in base 2, masking t >= L and the MTP causal rule;
+//   O (16 rows x D) += P . V_blk (16x16x16 f16), P rounded to f16 and V
+//   expanded to f16 with its scale folded in: exact for fp16 V and for
+//   E2M1 x UE4M3; one f16 rounding of code x scale for int8 and E4M3 with
+//   an fp16 scale and for E4M3 x 2^e; the per-tensor V scale multiplies the
+//   output instead.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
