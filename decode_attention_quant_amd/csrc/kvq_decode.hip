@@ -52,12 +52,30 @@ struct DT {
   static constexpr int KSTEPS = D / 32;
   static constexpr int QSTEPS = QI8 ? D / 64 : D / 32;  // MFMA k-steps of Q.K
   static constexpr int QPIECES = (QI8 || QF16) ? 2 : 1;
-  // Q operands kept in LDS (one ds_read_b128 per k-step) where registers
-  // would otherwise spill; in registers elsewhere.
-  static constexpr bool QLDS = true;
-  // Prefetch whole blocks into a second register buffer where it fits next
-  // to the O accumulators; otherwise reuse one buffer, loading the next
-  // block's K as soon as Q.K is done and its V as soon as P.V is done.
+  // Bytes of one 16-token block in each plane, and their place in an LDS
+  // stage (the four plane regions back to back).
+  static constexpr int KB = code_block_bytes(KC, D), KSB = scale_block_bytes(KC, D);
+  static constexpr int VB = code_block_bytes(VC, D), VSB = scale_block_bytes(VC, D);
+  static constexpr int SK = 0, SKS = KB, SV = KB + KSB, SVS = KB + KSB + VB;
+  static constexpr int STAGE = KB + KSB + VB + VSB;
+  // Direct global->LDS loads (16 bytes per lane) that copy one block.
+  static constexpr int NDMA = (KB + 1023) / 1024 + (KSB + 1023) / 1024 + (VB + 1023) / 1024 + (VSB + 1023) / 1024;
+  // Blocks are staged through a per-wave ring of RING_S blocks in LDS,
+  // RING_S - 1 of them in flight while one is consumed, where that fits in
+  // RING_LDS bytes per workgroup (two workgroups per CU).  INT8-G64 keeps
+  // its register pipeline: with q in two int8 pieces its loop is shorter
+  // than the ring's extra LDS reads and waits cost (measured).
+  static constexpr int RING_LDS = 72 * 1024;
+  static constexpr int RING_FIT = RING_LDS / (4 * STAGE);
+  static constexpr int RING_S = RING_FIT > 4 ? 4 : RING_FIT;
+  static constexpr bool RING = RING_S >= 2 && FMT != F_INT8_G64;
+  // Without the ring: Q operands in LDS (one ds_read_b128 per k-step) where
+  // registers would otherwise spill.
+  static constexpr bool QLDS = !RING;
+  // Without the ring: prefetch whole blocks into a second register buffer
+  // where it fits next to the O accumulators; otherwise reuse one buffer,
+  // loading the next block's K as soon as Q.K is done and its V as soon as
+  // P.V is done.
   static constexpr bool DOUBLE_BUF = D == 128 || FMT == F_FP8_ROW || FMT == F_FP8_TENSOR;
   static constexpr int NT = D / 16;
   static constexpr int KCH = D * KBITS / 512;                       // 16-B K chunks per lane per block
@@ -155,6 +173,161 @@ __device__ __forceinline__ void load_block(Buf<FMT, D>& buf, const uint8_t* head
                                            const cint32* bt_row, int j, int lane) {
   load_k<FMT, D>(buf, head0, geo, bt_row, j, lane);
   load_v<FMT, D>(buf, head0, geo, bt_row, j, lane);
+}
+
+// ----------------------------------------------------------- LDS ring
+// A wave copies each 16-token block into a stage of its own LDS ring with
+// direct global->LDS loads (global_load_lds_dwordx4: lane l's 16 bytes land
+// at the stage address + 16 l), which hold no registers while in flight.
+// Completion is tracked with explicit vmcnt waits: inside the block loop
+// these copies are the only vector-memory instructions, and they complete in
+// order.  Stages are read back with ds_read_b128 in inline asm that waits for
+// its own results, so the compiler's conservative wait for every
+// outstanding copy before an LDS read never enters the loop.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef const __attribute__((address_space(1))) void gbl_void_t;
+
+template <int BYTES>
+__device__ __forceinline__ void copy_plane(uint32_t dst, const uint8_t* src, int lane) {
+#pragma unroll
+  for (int c = 0; c < BYTES / 1024; ++c)
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)(src + c * 1024 + lane * 16),
+                                     (lds_void_t*)(uintptr_t)(dst + c * 1024), 16, 0, 0);
+  constexpr int REM = BYTES % 1024;
+  if constexpr (REM > 0) {
+    if (lane < REM / 16)
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(src + (BYTES / 1024) * 1024 + lane * 16),
+                                       (lds_void_t*)(uintptr_t)(dst + (BYTES / 1024) * 1024), 16, 0, 0);
+  }
+}
+
+// Start copying token block j into the stage at LDS byte address `stage`.
+template <int FMT, int D>
+__device__ __forceinline__ void stage_block(uint32_t stage, const uint8_t* head0, const Geometry& geo,
+                                            const cint32* bt_row, int j, int lane) {
+  using T = DT<FMT, D>;
+  const BlockAddr ba = block_addr(head0, geo, bt_row, j);
+  copy_plane<T::KB>(stage + T::SK, ba.hb + geo.off_kc + (int64_t)ba.bip * T::KB, lane);
+  if constexpr (T::KSB > 0) copy_plane<T::KSB>(stage + T::SKS, ba.hb + geo.off_ks + (int64_t)ba.bip * T::KSB, lane);
+  copy_plane<T::VB>(stage + T::SV, ba.hb + geo.off_vc + (int64_t)ba.bip * T::VB, lane);
+  if constexpr (T::VSB > 0) copy_plane<T::VSB>(stage + T::SVS, ba.hb + geo.off_vs + (int64_t)ba.bip * T::VSB, lane);
+}
+
+// s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt fields at "no wait").
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Wait until every copy of a block is done when `after` blocks (wave-
+// uniform, < S) were staged behind it.
+template <int NDMA, int S>
+__device__ __forceinline__ void wait_staged(int after) {
+  if constexpr (S > 3) {
+    if (after >= 3) { wait_vmcnt<3 * NDMA>(); return; }
+  }
+  if constexpr (S > 2) {
+    if (after >= 2) { wait_vmcnt<2 * NDMA>(); return; }
+  }
+  if (after >= 1) { wait_vmcnt<NDMA>(); return; }
+  wait_vmcnt<0>();
+}
+
+// NC 16-byte code chunks at c + i * CS (i < NC) and SW scale words at s
+// (consecutive), read from LDS in one asm block that waits for them.
+template <int NC, int CS, int SW>
+__device__ __forceinline__ void lds_read_part(uint4 (&c)[NC], uint32_t (&w)[SW > 0 ? SW : 1], uint32_t ca,
+                                              uint32_t sa) {
+  static_assert(NC == 2 || NC == 4, "");
+  static_assert(SW == 0 || SW == 2 || SW == 4 || SW == 8 || SW == 16, "");
+#define KVQ_R(o, a, off) "ds_read_b128 %" #o ", %" #a " offset:%" #off "\n\t"
+#define KVQ_W "s_waitcnt lgkmcnt(0)"
+  if constexpr (NC == 2) {
+    if constexpr (SW == 0) {
+      asm volatile(KVQ_R(0, 2, 3) KVQ_R(1, 2, 4) KVQ_W
+                   : "=&v"(c[0]), "=&v"(c[1]) : "v"(ca), "i"(0), "i"(CS) : "memory");
+    } else if constexpr (SW == 2) {
+      uint2 s0;
+      asm volatile(KVQ_R(0, 3, 5) KVQ_R(1, 3, 6) "ds_read_b64 %2, %4\n\t" KVQ_W
+                   : "=&v"(c[0]), "=&v"(c[1]), "=&v"(s0) : "v"(ca), "v"(sa), "i"(0), "i"(CS) : "memory");
+      w[0] = s0.x; w[1] = s0.y;
+    } else if constexpr (SW == 4) {
+      uint4 s0;
+      asm volatile(KVQ_R(0, 3, 5) KVQ_R(1, 3, 6) KVQ_R(2, 4, 5) KVQ_W
+                   : "=&v"(c[0]), "=&v"(c[1]), "=&v"(s0) : "v"(ca), "v"(sa), "i"(0), "i"(CS) : "memory");
+      w[0] = s0.x; w[1] = s0.y; w[2] = s0.z; w[3] = s0.w;
+    } else if constexpr (SW == 8) {
+      uint4 s0, s1;
+      asm volatile(KVQ_R(0, 4, 6) KVQ_R(1, 4, 7) KVQ_R(2, 5, 6) KVQ_R(3, 5, 8) KVQ_W
+                   : "=&v"(c[0]), "=&v"(c[1]), "=&v"(s0), "=&v"(s1) : "v"(ca), "v"(sa), "i"(0), "i"(CS), "i"(16)
+                   : "memory");
+      w[0] = s0.x; w[1] = s0.y; w[2] = s0.z; w[3] = s0.w; w[4] = s1.x; w[5] = s1.y; w[6] = s1.z; w[7] = s1.w;
+    } else {
+      uint4 s0, s1, s2, s3;
+      asm volatile(KVQ_R(0, 6, 8) KVQ_R(1, 6, 9) KVQ_R(2, 7, 8) KVQ_R(3, 7, 10) KVQ_R(4, 7, 11) KVQ_R(5, 7, 12) KVQ_W
+                   : "=&v"(c[0]), "=&v"(c[1]), "=&v"(s0), "=&v"(s1), "=&v"(s2), "=&v"(s3)
+                   : "v"(ca), "v"(sa), "i"(0), "i"(CS), "i"(16), "i"(32), "i"(48) : "memory");
+      const uint4 ss[4] = {s0, s1, s2, s3};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { w[4 * i] = ss[i].x; w[4 * i + 1] = ss[i].y; w[4 * i + 2] = ss[i].z; w[4 * i + 3] = ss[i].w; }
+    }
+  } else {
+    if constexpr (SW == 0) {
+      asm volatile(KVQ_R(0, 4, 5) KVQ_R(1, 4, 6) KVQ_R(2, 4, 7) KVQ_R(3, 4, 8) KVQ_W
+                   : "=&v"(c[0]), "=&v"(c[1]), "=&v"(c[2]), "=&v"(c[3])
+                   : "v"(ca), "i"(0), "i"(CS), "i"(2 * CS), "i"(3 * CS) : "memory");
+    } else if constexpr (SW == 2) {
+      uint2 s0;
+      asm volatile(KVQ_R(0, 5, 7) KVQ_R(1, 5, 8) KVQ_R(2, 5, 9) KVQ_R(3, 5, 10) "ds_read_b64 %4, %6\n\t" KVQ_W
+                   : "=&v"(c[0]), "=&v"(c[1]), "=&v"(c[2]), "=&v"(c[3]), "=&v"(s0)
+                   : "v"(ca), "v"(sa), "i"(0), "i"(CS), "i"(2 * CS), "i"(3 * CS) : "memory");
+      w[0] = s0.x; w[1] = s0.y;
+    } else if constexpr (SW == 4) {
+      uint4 s0;
+      asm volatile(KVQ_R(0, 5, 7) KVQ_R(1, 5, 8) KVQ_R(2, 5, 9) KVQ_R(3, 5, 10) KVQ_R(4, 6, 7) KVQ_W
+                   : "=&v"(c[0]), "=&v"(c[1]), "=&v"(c[2]), "=&v"(c[3]), "=&v"(s0)
+                   : "v"(ca), "v"(sa), "i"(0), "i"(CS), "i"(2 * CS), "i"(3 * CS) : "memory");
+      w[0] = s0.x; w[1] = s0.y; w[2] = s0.z; w[3] = s0.w;
+    } else if constexpr (SW == 8) {
+      uint4 s0, s1;
+      asm volatile(KVQ_R(0, 6, 8) KVQ_R(1, 6, 9) KVQ_R(2, 6, 10) KVQ_R(3, 6, 11) KVQ_R(4, 7, 8) KVQ_R(5, 7, 12) KVQ_W
+                   : "=&v"(c[0]), "=&v"(c[1]), "=&v"(c[2]), "=&v"(c[3]), "=&v"(s0), "=&v"(s1)
+                   : "v"(ca), "v"(sa), "i"(0), "i"(CS), "i"(2 * CS), "i"(3 * CS), "i"(16) : "memory");
+      w[0] = s0.x; w[1] = s0.y; w[2] = s0.z; w[3] = s0.w; w[4] = s1.x; w[5] = s1.y; w[6] = s1.z; w[7] = s1.w;
+    } else {
+      uint4 s0, s1, s2, s3;
+      asm volatile(KVQ_R(0, 8, 10) KVQ_R(1, 8, 11) KVQ_R(2, 8, 12) KVQ_R(3, 8, 13)
+                   KVQ_R(4, 9, 10) KVQ_R(5, 9, 14) KVQ_R(6, 9, 15) KVQ_R(7, 9, 16) KVQ_W
+                   : "=&v"(c[0]), "=&v"(c[1]), "=&v"(c[2]), "=&v"(c[3]), "=&v"(s0), "=&v"(s1), "=&v"(s2), "=&v"(s3)
+                   : "v"(ca), "v"(sa), "i"(0), "i"(CS), "i"(2 * CS), "i"(3 * CS), "i"(16), "i"(32), "i"(48)
+                   : "memory");
+      const uint4 ss[4] = {s0, s1, s2, s3};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { w[4 * i] = ss[i].x; w[4 * i + 1] = ss[i].y; w[4 * i + 2] = ss[i].z; w[4 * i + 3] = ss[i].w; }
+    }
+  }
+#undef KVQ_R
+#undef KVQ_W
+}
+
+// The K codes and scales of the block in `stage`, in the registers and lane
+// order load_k would give.
+template <int FMT, int D>
+__device__ __forceinline__ void read_stage_k(Buf<FMT, D>& buf, uint32_t stage, int lane) {
+  using T = DT<FMT, D>;
+  const int g = lane >> 4, c16 = lane & 15;
+  const uint32_t sa = stage + T::SKS + (T::KC == C_E2G16 ? c16 * 16 : g * (4 * T::KSW));
+  lds_read_part<T::KCH, 1024, T::KSW>(buf.k, buf.ks, stage + T::SK + lane * 16, sa);
+}
+
+// The V codes and scales of the block in `stage`, as load_v would give them.
+template <int FMT, int D>
+__device__ __forceinline__ void read_stage_v(Buf<FMT, D>& buf, uint32_t stage, int lane) {
+  using T = DT<FMT, D>;
+  const int g = lane >> 4, c16 = lane & 15;
+  const uint32_t ca = stage + T::SV + (T::VBITS == 4 ? (g * 8 + (c16 & 7)) * 16 : lane * 16);
+  lds_read_part<T::VCH, T::VBITS == 4 ? 512 : 1024, T::VSW>(buf.v, buf.vs, ca, stage + T::SVS + g * (4 * T::VSW));
 }
 
 // ----------------------------------------------------------- operand expanders
@@ -452,16 +625,19 @@ __device__ __forceinline__ int blocks_per_workgroup(int total, int nwg) {
   return per > MIN_BLOCKS_PER_WG ? per : MIN_BLOCKS_PER_WG;
 }
 
-// LDS layout of the split kernel (floats): prefix table [B + 1] (rounded to
-// 16), merge area [4][Rt][D], m and l [4][16] each, 16 spare floats (q
-// maxima), then the Q operand store when it lives in LDS.
+// LDS layout of the split kernel: prefix table int [B + 1] (rounded to 16),
+// m and l float [4][16] each, 16 spare floats (q maxima), the Q operand
+// store when it lives in LDS, then one area that holds the 4 waves' block
+// rings during the block loop and the merge area float [4][Rt][D] after it.
 template <int FMT, int D>
 __host__ __device__ constexpr size_t split_lds_bytes(int B, int R) {
   using T = DT<FMT, D>;
   const int rt = R < 16 ? R : 16;
   const size_t cum = (size_t)((B + 1 + 15) / 16 * 16);
-  return (cum + 4 * (size_t)rt * D + 64 + 64 + 16) * sizeof(float) +
-         (T::QLDS ? (size_t)T::QSTEPS * T::QPIECES * 64 * 16 : 0);
+  const size_t merge = 4 * (size_t)rt * D * sizeof(float);
+  const size_t ring = T::RING ? (size_t)4 * T::RING_S * T::STAGE : 0;
+  return (cum + 64 + 64 + 16) * sizeof(float) + (T::QLDS ? (size_t)T::QSTEPS * T::QPIECES * 64 * 16 : 0) +
+         (merge > ring ? merge : ring);
 }
 
 template <int FMT, int D>
@@ -475,11 +651,14 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
   const int w = blockIdx.x, rt = blockIdx.y;
   const int Rt = min(16, a.R - 16 * rt);
   int* cum = reinterpret_cast<int*>(lds);
-  float* sm_o = lds + (a.B + 1 + 15) / 16 * 16;
-  float* sm_m = sm_o + 4 * Rt * D;
+  float* sm_m = lds + (a.B + 1 + 15) / 16 * 16;
   float* sm_l = sm_m + 64;
   float* qexp = sm_l + 64;
   uint4* qst = reinterpret_cast<uint4*>(qexp + 16);
+  float* sm_o = reinterpret_cast<float*>(qst + (T::QLDS ? T::QSTEPS * T::QPIECES * 64 : 0));
+  // LDS byte address of this wave's ring (the low 32 bits of a generic
+  // pointer into LDS are its LDS offset)
+  const uint32_t ring0 = (uint32_t)(uintptr_t)(void*)sm_o + (uint32_t)(wave * T::RING_S * T::STAGE);
 
   // ---- cum[b] = H_kv * sum_{b' < b} ceil(L_b' / 16): the flat block index
   //      of unit (b, 0).  Each thread scans a contiguous run, then the runs'
@@ -702,7 +881,33 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
     {
       const int jend = blk0 + nblk;
       int j = blk0 + wave;
-      if constexpr (T::DOUBLE_BUF) {
+      if constexpr (T::RING) {
+        // this wave's blocks j_k = blk0 + wave + 4 k, k < nk; block k sits in
+        // stage k % S, and blocks k + 1 .. k + S - 1 are in flight meanwhile
+        constexpr int S = T::RING_S;
+        const int nk = nblk > wave ? (nblk - wave + 3) >> 2 : 0;
+#pragma unroll
+        for (int k = 0; k < S - 1; ++k)
+          if (k < nk) stage_block<FMT, D>(ring0 + k * T::STAGE, head0, geo, bt_row, j + 4 * k, lane);
+        Buf<FMT, D> A;
+        float sc[4];
+        int st = 0;
+        for (int k = 0; k < nk; ++k) {
+          // stage st - 1 (block k - 1) has been read: refill it with block k + S - 1
+          if (k + S - 1 < nk) {
+            const int sn = st == 0 ? S - 1 : st - 1;
+            stage_block<FMT, D>(ring0 + sn * T::STAGE, head0, geo, bt_row, j + 4 * (S - 1), lane);
+          }
+          wait_staged<T::NDMA, S>(min(S - 1, nk - 1 - k));
+          const uint32_t stg = ring0 + st * T::STAGE;
+          read_stage_k<FMT, D>(A, stg, lane);
+          qk_phase(A, j, sc);
+          read_stage_v<FMT, D>(A, stg, lane);
+          pv_phase(A, j, sc);
+          j += 4;
+          st = st + 1 == S ? 0 : st + 1;
+        }
+      } else if constexpr (T::DOUBLE_BUF) {
         Buf<FMT, D> A, Bb;
         float sc[4];
         if (j < jend) load_block<FMT, D>(A, head0, geo, bt_row, j, lane);
