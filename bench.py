@@ -237,9 +237,13 @@ def append_chunk_bench(formats, stream, probe, reps=10):
     return res
 
 
+# the sources the split kernel is compiled from
+SPLIT_SOURCES = ["kvq_decode.hip", "kvq_device.hpp", "kvq_format.hpp", "kvq_internal.hpp"]
+
+
 def kernel_sources_sha():
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
+    for f in SPLIT_SOURCES:
         h.update(f.encode())
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
@@ -248,7 +252,8 @@ def kernel_sources_sha():
 
 def recorded_traffic(workload, fmt):
     """HBM bytes per split-kernel launch from the committed counter summary,
-    or None when it is for another workload or the kernels changed since."""
+    or None when it is for another workload or the split kernel's sources
+    changed since."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as fh:

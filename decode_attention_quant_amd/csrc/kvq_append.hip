@@ -468,9 +468,10 @@ __device__ __forceinline__ void v_row_group(uint8_t* __restrict__ pool, const ui
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int64_t tok = t0 + e;
-    slot[e] = (tok >= tlo && tok < thi) ? slots[tok] : -1;
+    const bool in = tok >= tlo && tok < thi;
+    slot[e] = in ? slots[tok] : -1;
     ok[e] = slot[e] >= 0;
-    if (ok[e]) {
+    if (in) {  // loaded whatever the slot says, so the two loads overlap
       const uint16_t* src = v + (tok * geo.H_kv + head) * D + j * F;
 #pragma unroll
       for (int i = 0; i < F / 8; ++i) {
@@ -727,20 +728,22 @@ __device__ __forceinline__ void append_v_wave(uint8_t* __restrict__ pool, const 
   int a = 0;
   bool shifted = false, tail_here = false;
   if constexpr (D == 256) {
-    // does the window of 16 tokens from tw have slots sw, sw + 1, ...?  (wave-uniform)
-    auto runs_on = [&](int64_t tw, int sw) -> bool {
-      const int64_t tok = tw + j;
-      const bool okj = tw >= 0 && tw + 16 <= T && sw >= 0 && slots[tok] == sw + j;
-      return __all(okj);
+    // lane l holds the slot of token b0 - 3 + l (l < 35; -1 outside [0, T)):
+    // both windows are decided from these values with lane votes
+    const int64_t tl = b0 - 3 + lane;
+    const int sl = (lane < 35 && tl >= 0 && tl < T) ? slots[tl] : -1;
+    // do the 16 tokens from lane l0 on have slots s, s + 1, ...?  (s = slot at lane l0 + a)
+    auto runs_on = [&](int l0, int s) -> bool {
+      const bool in = lane >= l0 && lane < l0 + 16;
+      return __all(!in || (s >= 0 && sl == s + (lane - l0)));
     };
-    const int s0 = b0 < T ? slots[b0] : -1;
+    const int s0 = __shfl(sl, 3);
     if (s0 >= 0) {
       a = s0 & 3;
-      shifted = runs_on(b0 - a, s0 - a);
+      shifted = runs_on(3 - a, s0 - a);
       if (shifted && a > 0) {
-        const int64_t b1 = b0 + 16;
-        const int s1 = b1 < T ? slots[b1] : -1;
-        tail_here = !(s1 >= 0 && (s1 & 3) == a && runs_on(b1 - a, s1 - a));
+        const int s1 = __shfl(sl, 19);
+        tail_here = !(s1 >= 0 && (s1 & 3) == a && runs_on(19 - a, s1 - a));
       }
     }
   }
@@ -765,6 +768,13 @@ __device__ __forceinline__ void append_k_wave(uint8_t* __restrict__ pool, const 
   const int64_t token = tg * 16 + (lane >> 2);  // a whole quad shares it
   if (token >= T) return;
   const int64_t row = token * geo.H_kv + head;
+  const uint16_t* src = k + row * D + q * E;
+  uint32_t raw[E / 2];
+#pragma unroll
+  for (int i = 0; i < E / 8; ++i) {  // issued before the slot is known, so the loads overlap
+    const uint4 w = *reinterpret_cast<const uint4*>(src + 8 * i);
+    raw[4 * i] = w.x; raw[4 * i + 1] = w.y; raw[4 * i + 2] = w.z; raw[4 * i + 3] = w.w;
+  }
   const int slot = slots[token];
   if (slot < 0) return;
   const int64_t page = slot / geo.P;
@@ -773,14 +783,6 @@ __device__ __forceinline__ void append_k_wave(uint8_t* __restrict__ pool, const 
   uint8_t* head_base = pool + page * geo.page_bytes + (int64_t)head * geo.head_bytes;
   uint8_t* codes = head_base + geo.off_kc + (int64_t)blk * geo.kcode_blk;
   uint8_t* scales = head_base + geo.off_ks + (int64_t)blk * geo.kscale_blk;
-
-  const uint16_t* src = k + row * D + q * E;
-  uint32_t raw[E / 2];
-#pragma unroll
-  for (int i = 0; i < E / 8; ++i) {
-    const uint4 w = *reinterpret_cast<const uint4*>(src + 8 * i);
-    raw[4 * i] = w.x; raw[4 * i + 1] = w.y; raw[4 * i + 2] = w.z; raw[4 * i + 3] = w.w;
-  }
   constexpr int KC = k_codec(FMT);
   if constexpr (KC == C_BF16) {
     store_k_codes<16, D>(codes, raw, q, t);  // K of BF16 is stored bit for bit
