@@ -1017,15 +1017,20 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
 }
 
 // ----------------------------------------------------------- combine
-// One workgroup of D threads per (unit, row): thread t owns element t.
-// Units finished by the split kernel (one workgroup, write_direct) are
-// skipped; empty sequences get out = 0, lse = -inf.
+// One workgroup of NT = SG D / 4 threads per (unit, row); thread (g, c) owns
+// elements 4c .. 4c + 3 and merges partials g, g + SG, ...
+// with a running maximum, rescaling what it holds when the maximum grows
+// (the same log-sum-exp merge as the split kernel's); the groups then merge
+// through LDS.  Units finished by the split kernel (one workgroup,
+// write_direct) are skipped; empty sequences get out = 0, lse = -inf.
 
-template <int D, bool VROT>
-__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a, int H_kv) {
+template <int D, bool VROT, int SG>
+__global__ __launch_bounds__(SG * D / 4) void decode_combine_kernel(DecodeArgs a, int H_kv) {
   constexpr float NEG_INF = -__builtin_inff();
-  __shared__ float red[D];
-  const int t = threadIdx.x;
+  constexpr int DL = D / 4;       // threads per partial row (4 elements each)
+  __shared__ float4 sacc[SG][DL];
+  __shared__ float sm[SG], sl[SG];
+  const int tid = threadIdx.x, c = tid % DL, g = tid / DL;
   const int u = (int)(blockIdx.x / (unsigned)a.R), rr = (int)(blockIdx.x - (unsigned)u * a.R);
   const int b = u / H_kv, h = u - b * H_kv;
   const int qi = rr / a.G, qh = h * a.G + (rr - qi * a.G);
@@ -1033,8 +1038,8 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a, int H_k
   const int L = a.seq_lens[b];
   const int nb = (L + 15) >> 4;
   if (nb == 0) {
-    a.out[orow * D + t] = 0.f;
-    if (a.lse != nullptr && t == 0) a.lse[orow] = NEG_INF;
+    if (tid < DL) *reinterpret_cast<float4*>(a.out + orow * D + 4 * c) = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (a.lse != nullptr && tid == 0) a.lse[orow] = NEG_INF;
     return;
   }
   const int total = a.ws_cum[a.B];
@@ -1043,56 +1048,61 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a, int H_k
   const int wa = start / per, wb = (start + nb - 1) / per;
   if (wa == wb && a.write_direct) return;
   const float* ml = a.ws_ml + ((int64_t)(u + wa) * a.R + rr) * 2;
-  const float* po = a.ws_o + ((int64_t)(u + wa) * a.R + rr) * D + t;
+  const float* po = a.ws_o + ((int64_t)(u + wa) * a.R + rr) * D + 4 * c;
   const int nseg = wb - wa + 1;
   const int64_t sml = (int64_t)a.R * 2, so = (int64_t)a.R * D;  // slot strides
-  // M = max over segments
-  float mloc = NEG_INF;
-  for (int s = t; s < nseg; s += D) mloc = fmaxf(mloc, ml[s * sml]);
-  red[t] = mloc;
-  __syncthreads();
-  for (int k = D / 2; k > 0; k >>= 1) {
-    if (t < k) red[t] = fmaxf(red[t], red[t + k]);
-    __syncthreads();
-  }
-  const float M = red[0];
-  __syncthreads();
-  float acc = 0.f, l = 0.f;
-  int s = 0;
-  for (; s + 4 <= nseg; s += 4) {
-    float ms[4], ls[4], os[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { ms[i] = ml[(s + i) * sml]; ls[i] = ml[(s + i) * sml + 1]; os[i] = po[(s + i) * so]; }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float wt = (ms[i] == NEG_INF) ? 0.f : exp2f(ms[i] - M);
-      l += wt * ls[i];
-      acc += wt * os[i];
+
+  float m = NEG_INF, l = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto take = [&](float ms, float ls, float4 o) {
+    if (ms == NEG_INF) return;  // a partial that saw no visible key
+    if (ms > m) {
+      const float f = m == NEG_INF ? 0.f : exp2f(m - ms);
+      l *= f;
+      acc.x *= f; acc.y *= f; acc.z *= f; acc.w *= f;
+      m = ms;
     }
+    const float w = exp2f(ms - m);
+    l += w * ls;
+    acc.x += w * o.x; acc.y += w * o.y; acc.z += w * o.z; acc.w += w * o.w;
+  };
+  int s = g;
+  for (; s + SG < nseg; s += 2 * SG) {  // two partials in flight per thread
+    const float m0 = ml[s * sml], l0 = ml[s * sml + 1];
+    const float m1 = ml[(s + SG) * sml], l1 = ml[(s + SG) * sml + 1];
+    const float4 o0 = *reinterpret_cast<const float4*>(po + s * so);
+    const float4 o1 = *reinterpret_cast<const float4*>(po + (s + SG) * so);
+    take(m0, l0, o0);
+    take(m1, l1, o1);
   }
-  for (; s < nseg; ++s) {
-    const float ms = ml[s * sml];
-    const float wt = (ms == NEG_INF) ? 0.f : exp2f(ms - M);
-    l += wt * ml[s * sml + 1];
-    acc += wt * po[s * so];
+  if (s < nseg) take(ml[s * sml], ml[s * sml + 1], *reinterpret_cast<const float4*>(po + s * so));
+
+  sacc[g][c] = acc;
+  if (c == 0) { sm[g] = m; sl[g] = l; }
+  __syncthreads();
+  if (g != 0) return;
+  float M = NEG_INF;
+#pragma unroll
+  for (int k = 0; k < SG; ++k) M = fmaxf(M, sm[k]);
+  float Lt = 0.f;
+  float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int k = 0; k < SG; ++k) {
+    const float w = sm[k] == NEG_INF ? 0.f : exp2f(sm[k] - M);
+    const float4 v = sacc[k][c];
+    Lt += w * sl[k];
+    A.x += w * v.x; A.y += w * v.y; A.z += w * v.z; A.w += w * v.w;
   }
-  const float xo = l > 0.f ? acc * (a.v_out_scale / l) : 0.f;
+  const float inv = Lt > 0.f ? a.v_out_scale / Lt : 0.f;
+  float xv[4] = {A.x * inv, A.y * inv, A.z * inv, A.w * inv};
   if constexpr (VROT) {
-    red[t] = xo;
-    __syncthreads();
-    if (t < 64) {
-      constexpr int E = D / 64;
-      float xv[E];
+    static_assert(D == 256, "the rotation is 256-point");
+    fwht_wave<4>(xv, c);  // the 64 threads of group 0 are one wave holding the row
 #pragma unroll
-      for (int i = 0; i < E; ++i) xv[i] = red[E * t + i];
-      fwht_wave<E>(xv, t);
-#pragma unroll
-      for (int i = 0; i < E; ++i) a.out[orow * D + E * t + i] = xv[i] * 0.0625f;
-    }
-  } else {
-    a.out[orow * D + t] = xo;
+    for (int i = 0; i < 4; ++i) xv[i] *= 0.0625f;
   }
-  if (a.lse != nullptr && t == 0) a.lse[orow] = l > 0.f ? (M + __log2f(l)) * 0.69314718055994531f : NEG_INF;
+  *reinterpret_cast<float4*>(a.out + orow * D + 4 * c) = make_float4(xv[0], xv[1], xv[2], xv[3]);
+  if (a.lse != nullptr && tid == 0) a.lse[orow] = Lt > 0.f ? (M + __log2f(Lt)) * 0.69314718055994531f : NEG_INF;
 }
 
 // ----------------------------------------------------------- launchers
@@ -1135,17 +1145,26 @@ hipError_t launch_decode_split(const Geometry& geo, const DecodeArgs& a, hipStre
 }
 
 hipError_t launch_decode_combine(const Geometry& geo, const DecodeArgs& a, hipStream_t stream) {
-  const int64_t rows = (int64_t)a.B * geo.H_kv * a.R;
+  const int64_t units = (int64_t)a.B * geo.H_kv;
+  const int64_t rows = units * a.R;
   if (rows == 0) return hipSuccess;
   const bool vrot = v_rotated(geo.fmt);
-  if (geo.D == 256 && vrot)
-    hipLaunchKernelGGL((decode_combine_kernel<256, true>), dim3((unsigned)rows), dim3(256), 0, stream, a, geo.H_kv);
-  else if (geo.D == 256)
-    hipLaunchKernelGGL((decode_combine_kernel<256, false>), dim3((unsigned)rows), dim3(256), 0, stream, a, geo.H_kv);
-  else if (geo.D == 128 && !vrot)
-    hipLaunchKernelGGL((decode_combine_kernel<128, false>), dim3((unsigned)rows), dim3(128), 0, stream, a, geo.H_kv);
-  else
-    return hipErrorInvalidValue;
+  // partials merged side by side: about the partials per unit, 1 .. 16
+  const int64_t expect = a.nwg / units + 1;
+  const int sg = expect >= 16 ? 16 : expect >= 8 ? 8 : expect >= 4 ? 4 : expect >= 2 ? 2 : 1;
+#define KVQ_COMBINE(DD, VR)                                                                               \
+  switch (sg) {                                                                                           \
+    case 16: hipLaunchKernelGGL((decode_combine_kernel<DD, VR, 16>), dim3((unsigned)rows), dim3(4 * DD), 0, stream, a, geo.H_kv); break; \
+    case 8: hipLaunchKernelGGL((decode_combine_kernel<DD, VR, 8>), dim3((unsigned)rows), dim3(2 * DD), 0, stream, a, geo.H_kv); break; \
+    case 4: hipLaunchKernelGGL((decode_combine_kernel<DD, VR, 4>), dim3((unsigned)rows), dim3(DD), 0, stream, a, geo.H_kv); break; \
+    case 2: hipLaunchKernelGGL((decode_combine_kernel<DD, VR, 2>), dim3((unsigned)rows), dim3(DD / 2), 0, stream, a, geo.H_kv); break; \
+    default: hipLaunchKernelGGL((decode_combine_kernel<DD, VR, 1>), dim3((unsigned)rows), dim3(DD / 4), 0, stream, a, geo.H_kv); break; \
+  }
+  if (geo.D == 256 && vrot) KVQ_COMBINE(256, true)
+  else if (geo.D == 256) KVQ_COMBINE(256, false)
+  else if (geo.D == 128 && !vrot) KVQ_COMBINE(128, false)
+  else return hipErrorInvalidValue;
+#undef KVQ_COMBINE
   return hipGetLastError();
 }
 

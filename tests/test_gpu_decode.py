@@ -138,3 +138,25 @@ def test_slack_slots_hold_garbage(fill):
     ref, ref_lse = oracle_attention(bl)
     assert np.all(np.isfinite(out))
     assert_close(out, ref, "fill %#x" % fill)
+
+
+@pytest.mark.parametrize("nwg", [300, 64])
+def test_many_partials_per_unit_head_dim_128(nwg):
+    """head_dim 128 (MXFP8, 32 kv heads) with one sequence split over many
+    workgroups: the combine merges tens of partials per unit side by side."""
+    c = W.make_case(5, "MXFP8", device="cpu", B=1, lengths=[3000])
+    bl = build(c)
+    ref, ref_lse = oracle_attention(bl)
+    q = c.q.cuda()
+    ws = kvq.alloc_workspace(kvq.workspace_size(bl.desc, c.B, c.n_q, c.H_q, c.max_pages, nwg))
+    ws.fill_(0xFF)
+    out = torch.full((c.B, c.n_q, c.H_q, c.D), float("nan"), device="cuda")
+    lse = torch.full((c.B, c.n_q, c.H_q), float("nan"), device="cuda")
+    note("combine d128", "nwg", nwg)
+    kvq.decode_split(bl.desc, bl.pool_gpu, q, bl.bt, bl.sl, c.softmax_scale, ws, num_workgroups=nwg,
+                     flags=kvq.SPLIT_WRITE_WHOLE_UNITS, out=out, lse=lse)
+    kvq.decode_combine(bl.desc, c.B, c.n_q, c.H_q, c.max_pages, bl.sl, ws, out, lse, num_workgroups=nwg,
+                       flags=kvq.SPLIT_WRITE_WHOLE_UNITS)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), ref, "mxfp8 nwg=%d" % nwg)
+    assert_lse_close(lse.cpu().numpy(), ref_lse, "mxfp8 nwg=%d" % nwg)
