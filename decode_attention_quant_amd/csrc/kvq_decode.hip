@@ -616,13 +616,15 @@ __device__ __forceinline__ void clear_tail(Buf<FMT, D>& buf, int nvalid, int g) 
 // ----------------------------------------------------------- the kernel
 
 // Blocks per split workgroup: an equal share of the T blocks, but at least
-// MIN_BLOCKS_PER_WG, so that when the sequences are shorter than the grid
-// was sized for, fewer workgroups get longer ranges (the rest find theirs
-// empty) instead of every range shrinking.
-constexpr int MIN_BLOCKS_PER_WG = 128;
-__device__ __forceinline__ int blocks_per_workgroup(int total, int nwg) {
+// ceil(T / 256) clamped to [16, 128], so that when the sequences are shorter
+// than the grid was sized for, about 256 workgroups (one per CU) get longer
+// ranges and the rest find theirs empty, instead of every range shrinking
+// to a few blocks that each leave a partial result.
+__host__ __device__ __forceinline__ int blocks_per_workgroup(int total, int nwg) {
   const int per = (total + nwg - 1) / nwg;
-  return per > MIN_BLOCKS_PER_WG ? per : MIN_BLOCKS_PER_WG;
+  int lo = (total + 255) / 256;
+  lo = lo < 16 ? 16 : (lo > 128 ? 128 : lo);
+  return per > lo ? per : lo;
 }
 
 // LDS layout of the split kernel: prefix table int [B + 1] (rounded to 16),

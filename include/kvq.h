@@ -159,8 +159,9 @@ kvq_status kvq_decode_attention(const kvq_cache_desc* desc, const void* pool,
  * Schedule: the 16-token blocks of all (sequence b, kv head h) units, in
  * unit order u = b * num_kv_heads + h, form one range of T blocks;
  * split workgroup w takes blocks [w * per, (w + 1) * per),
- * per = max(ceil(T / num_workgroups), 128).  kvq_decode_split writes, for every unit u and every
- * workgroup w that covers part of it, one partial per row r = i * G + j
+ * per = max(ceil(T / num_workgroups), min(max(ceil(T / 256), 16), 128)).
+ * kvq_decode_split writes, for every unit u and every workgroup w that
+ * covers part of it, one partial per row r = i * G + j
  * (query token i, j-th query head of the group) into slot u + w:
  *   workspace = cum int32 [batch + 1] (cum[b] = num_kv_heads x blocks of
  *   sequences before b), then at the next 256-byte boundary (m, l) fp32
