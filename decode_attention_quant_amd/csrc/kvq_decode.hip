@@ -531,8 +531,10 @@ __device__ __forceinline__ f16x4 v_operand(const Buf<FMT, D>& buf, int nt, int l
     return f16x4{a[0], a[1], b[0], b[1]};
   } else {  // C_E2G16: byte e holds (token 4g+e, n) low and (token 4g+e, n+8) high
     const uint32_t w = word(buf.v[nt >> 2], nt & 3);
-    const uint32_t x = (w >> (((lane & 15) >= 8) ? 4 : 0)) & 0x0F0F0F0Fu;
-    const uint32_t y = x | (x >> 4);  // byte 0: t0 | t1 << 4, byte 2: t2 | t3 << 4
+    const uint32_t x = w >> (((lane & 15) >= 8) ? 4 : 0);  // this lane's nibble of each byte in bits 0-3
+    // byte 0: t0 | t1 << 4, byte 2: t2 | t3 << 4 (bytes 1, 3 unused)
+    uint32_t y;  // (x & 0x0F0F0F0F) | ((x >> 4) & 0xF0F0F0F0) in one bitfield insert
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(y) : "v"(0x0F0F0F0Fu), "v"(x), "v"(x >> 4));
     f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y, 1.0f, 0);
     f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y, 1.0f, 2);
     const uint32_t sw = buf.vs[nt];  // UE4M3 of tokens 4g..4g+3, group nt
