@@ -569,6 +569,19 @@ __device__ __forceinline__ void fwht_wave(float (&x)[E], int lane) {
   }
 }
 
+// Maximum over the four lanes 16 g + c (g = 0..3) that share c, without an
+// LDS round trip: each swap leaves x of this lane and of its partner at
+// distance 16 (then 32) in the two results.
+__device__ __forceinline__ float max_over_g(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(bitcast<uint32_t>(x), bitcast<uint32_t>(x), false, false);
+  x = fmaxf(bitcast<float>((uint32_t)a[0]), bitcast<float>((uint32_t)a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(bitcast<uint32_t>(x), bitcast<uint32_t>(x), false, false);
+  return fmaxf(bitcast<float>((uint32_t)b[0]), bitcast<float>((uint32_t)b[1]));
+}
+
+// Slack of the running maximum, in log2 units (see pv_phase).
+constexpr float RESCALE_SLACK = 8.0f;
+
 // 2^x with the hardware exp: results below 2^-126 flush to zero, which only
 // drops probabilities far below anything that can change an fp32 sum
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -845,10 +858,13 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
     };
     auto pv_phase = [&](Buf<FMT, D>& buf, int jb, const float (&sc)[4]) {
       const int t0 = 16 * jb;
-      float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-      bm = fmaxf(bm, __shfl_xor(bm, 16));
-      bm = fmaxf(bm, __shfl_xor(bm, 32));
-      if (__any(bm > m_run)) {  // rare after the first blocks: rescale l and O
+      const float bm = max_over_g(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+      // The running maximum only has to bound the scores loosely: with it up
+      // to RESCALE_SLACK below the true one, p <= 2^RESCALE_SLACK, which f16 P
+      // and the fp32 sums hold as well as p <= 1; (m, l, O) stay consistent
+      // for whatever m is used.  So l and O are rescaled only on a jump past
+      // the slack (and on the first visible block, from m = -inf).
+      if (__any(bm > m_run + RESCALE_SLACK)) {
         const float m_new = fmaxf(m_run, bm);
         const float corr = (m_new > m_run) ? fast_exp2(m_run - m_new) : 1.0f;
         l_run *= corr;

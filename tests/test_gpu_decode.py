@@ -160,3 +160,24 @@ def test_many_partials_per_unit_head_dim_128(nwg):
     torch.cuda.synchronize()
     assert_close(out.cpu().numpy(), ref, "mxfp8 nwg=%d" % nwg)
     assert_lse_close(lse.cpu().numpy(), ref_lse, "mxfp8 nwg=%d" % nwg)
+
+
+@pytest.mark.parametrize("fmt,cfg", [("NVFP4_G16", 3), ("FP8_ROW", 2), ("INT8_G64", 2), ("K8V4", 4), ("MXFP8", 5),
+                                     ("BF16", 1)])
+def test_scores_that_climb_and_jump(fmt, cfg):
+    """Keys scaled up along each sequence (up to 6x at the end) with a few
+    6x spikes late on: the running maximum climbs block after block and
+    jumps by far more than the rescale slack mid-stream, so the kernel both
+    runs with probabilities above 1 and rescales l and O part-way."""
+    c = W.make_case(cfg, fmt, device="cpu", B=2, lengths=[1500, 700])
+    pos = torch.as_tensor(c.token_pos, dtype=torch.float32)
+    L = torch.as_tensor(c.seq_lens[c.token_seq].astype(np.float32))
+    factor = 1.0 + 5.0 * pos / L
+    late = np.flatnonzero(c.token_pos > 0.6 * c.seq_lens[c.token_seq])
+    factor[np.random.default_rng(11).choice(late, size=6, replace=False)] *= 6.0
+    c.k = (c.k.float() * factor[:, None, None]).to(torch.bfloat16)
+    bl = build(c)
+    out, lse = run_decode(bl)
+    ref, ref_lse = oracle_attention(bl)
+    assert_close(out, ref, "climbing scores " + W_name(c))
+    assert_lse_close(lse, ref_lse, "climbing scores " + W_name(c))
