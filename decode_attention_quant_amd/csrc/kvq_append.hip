@@ -16,11 +16,16 @@
 //
 // V waves: each row of 16 lanes holds 4 consecutive tokens, lane j holding
 // elements [j F, (j + 1) F), F = D / 16, of all 4.  The V tile interleaves
-// 4 consecutive slots inside every 32-bit word, so when the 4 tokens fill
-// one such slab (consecutive slots, the first a multiple of 4) each lane
-// writes whole words; consecutive slots that straddle two slabs take two
-// partial writes per word, and other slot patterns each token's bytes.  The rotation runs stages h = 1 .. 8 inside a
-// lane and h = 16 .. 128 across lanes (xor 1, 2, 4, 8).
+// 4 consecutive slots (a slab) inside every 32-bit word, so when the 4
+// tokens fill one slab (consecutive slots, the first a multiple of 4) each
+// lane writes whole words: 8-bit codes after a 4 x 4 word transpose across
+// the quad, 4-bit codes (one column of a token pair per byte) after an
+// 8 x 8 word transpose across 8 lanes.  Otherwise 8- and 16-bit codes are
+// written token by token (two partial writes per word for consecutive
+// slots that straddle two slabs), and 4-bit codes nibble by nibble with
+// atomic and/or, which keeps the other token of the pair intact.  The
+// rotation runs stages h = 1 .. 8 inside a lane and h = 16 .. 128 across
+// lanes (xor 1, 2, 4, 8).
 //
 // Every cross-lane step is a DPP permutation, and every rotation stage
 // rounds exactly like the fixed butterfly order of the format.
@@ -83,6 +88,28 @@ __device__ __forceinline__ void quad_transpose(uint32_t (&W)[4], int c) {
     W[2] = hi ? W[2] : r0;
     W[3] = hi ? W[3] : r1;
   }
+}
+
+// Lanes c = 0 .. 7 of a group of 8 hold W[0 .. 7]; afterwards lane c holds
+// element c of every lane of the group: W[k] = (W of lane k)[c].  Stage M
+// (1, 2, 4) swaps element i + M of the lower lane of each pair with element
+// i of the upper one (bit M of i clear).
+template <int M>
+__device__ __forceinline__ void oct_stage(uint32_t (&W)[8], int c) {
+  const bool up = (c & M) != 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (i & M) continue;
+    const uint32_t r = lane_xor_u32<M>(up ? W[i] : W[i + M]);
+    if (up) W[i] = r;
+    else W[i + M] = r;
+  }
+}
+
+__device__ __forceinline__ void oct_transpose(uint32_t (&W)[8], int c) {
+  oct_stage<1>(W, c);
+  oct_stage<2>(W, c);
+  oct_stage<4>(W, c);
 }
 
 // Max over the L lanes (L a power of two <= 16) whose index differs only in
@@ -279,41 +306,6 @@ __device__ __forceinline__ void store_k_codes(uint8_t* codes, const uint32_t* w,
   }
 }
 
-// V codes, t = 4 gv + e, d = 16 jt + n:
-//   8-bit  (jt/4)*1024 + (gv*16 + n)*16 + (jt%4)*4 + e
-//   16-bit (jt/2)*1024 + (gv*16 + n)*16 + (jt%2)*8 + 2e
-//   4-bit  (jt/4)*512 + (gv*8 + n%8)*16 + (jt%4)*4 + e, high nibble n >= 8
-template <int BITS, int D>
-__device__ __forceinline__ void store_v_codes(uint8_t* codes, const uint32_t* w, int q, int t) {
-  constexpr int E = D / 4;
-  const int gv = t >> 2, e = t & 3;
-  if constexpr (BITS == 8) {
-#pragma unroll
-    for (int l = 0; l < E; ++l) {
-      const int d = q * E + l, jt = d >> 4, n = d & 15;
-      codes[(jt >> 2) * 1024 + (gv * 16 + n) * 16 + (jt & 3) * 4 + e] = (uint8_t)(w[l >> 2] >> (8 * (l & 3)));
-    }
-  } else if constexpr (BITS == 16) {
-#pragma unroll
-    for (int l = 0; l < E; ++l) {
-      const int d = q * E + l, jt = d >> 4, n = d & 15;
-      *reinterpret_cast<uint16_t*>(codes + (jt >> 1) * 1024 + (gv * 16 + n) * 16 + (jt & 1) * 8 + 2 * e) =
-          (uint16_t)(w[l >> 1] >> (16 * (l & 1)));
-    }
-  } else {  // 4-bit: words hold 8 consecutive d; pair n with n + 8 of the same n-tile
-#pragma unroll
-    for (int l = 0; l < E; l += 16) {
-      const int jt = (q * E + l) >> 4;
-      const uint32_t a = w[l >> 3], b = w[(l >> 3) + 1];  // n = 0..7 and n = 8..15
-#pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        const uint32_t lo = (a >> (4 * n)) & 0xFu, hi = (b >> (4 * n)) & 0xFu;
-        codes[(jt >> 2) * 512 + (gv * 8 + n) * 16 + (jt & 3) * 4 + e] = (uint8_t)(lo | (hi << 4));
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------- one plane
 
 template <int C, int D, bool ROT, int PLANE>
@@ -365,9 +357,6 @@ __device__ __forceinline__ void encode_plane(float (&x)[D / 4], int q, uint8_t* 
       if constexpr (scale_bytes(C) == 2) {  // INT8-G64: one group per lane (D = 256)
         static_assert(GPL == 1, "");
         *reinterpret_cast<uint16_t*>(scales + (t * G + grp0) * 2) = (uint16_t)sb[0];
-      } else if constexpr (PLANE == 1 && C == C_E2G16) {  // V UE4M3: (t/4)*4G + grp*4 + t%4
-#pragma unroll
-        for (int gl = 0; gl < GPL; ++gl) scales[(t >> 2) * 4 * G + (grp0 + gl) * 4 + (t & 3)] = (uint8_t)sb[gl];
       } else if constexpr (GPL == 4) {
         *reinterpret_cast<uint32_t*>(scales + t * G + grp0) = sb[0] | (sb[1] << 8) | (sb[2] << 16) | (sb[3] << 24);
       } else if constexpr (GPL == 2) {
@@ -377,8 +366,8 @@ __device__ __forceinline__ void encode_plane(float (&x)[D / 4], int q, uint8_t* 
       }
     }
   }
-  if constexpr (PLANE == 0) store_k_codes<BITS, D>(codes, out.w, q, t);
-  else store_v_codes<BITS, D>(codes, out.w, q, t);
+  static_assert(PLANE == 0, "V rows are encoded by v_row_group");
+  store_k_codes<BITS, D>(codes, out.w, q, t);
 }
 
 // ---------------------------------------------------------------- V waves
@@ -413,7 +402,9 @@ __device__ __forceinline__ void fwht256_row16(float (&x)[16], int j) {
 // Codes of element i of the lane for all 4 tokens: one 32-bit word per i
 // holding token e in byte e (8-bit codes), two words per i holding tokens
 // (0, 1) and (2, 3) (16-bit codes), or, for 4-bit codes, one word per
-// i < F / 2 holding token e's codes of elements i and i + 8 in byte e.
+// m < F / 2 holding elements 2m and 2m + 1: bytes 0, 1 hold element 2m of
+// tokens (0, 1) and (2, 3), bytes 2, 3 element 2m + 1, the earlier token of
+// each pair in the low nibble (the tile's byte order).
 template <int C, int F>
 struct VWords {
   static constexpr int N = codec_bits(C) == 16 ? 2 * F : codec_bits(C) == 8 ? F : F / 2;
@@ -450,6 +441,47 @@ __device__ __forceinline__ void store_tokens(uint8_t* p, uint64_t W, int first, 
       *reinterpret_cast<uint16_t*>(q) = (uint16_t)v;
       *reinterpret_cast<uint32_t*>(q + 2) = (uint32_t)(v >> 16);
     }
+  }
+}
+
+// Store the 4-bit V codes of token e of a row's 4 (codes in the tile byte
+// order of VWords, lane j holding n-tile j) at slab position te of slab gv
+// of the token block at `codes`, leaving the other tokens' nibbles intact.
+// The quad of n-tiles 4q .. 4q + 3 covers 8 bytes of every tile row (row n
+// of chunk q / 2, bytes 8 (q % 2) .. + 7); the nibbles are first gathered
+// across the quad so that lane k holds those 8 bytes' worth of rows
+// n = k + 4m, and each lane then does 64-bit and/or on 4 distinct words.
+__device__ __forceinline__ void store_token_nibbles(uint8_t* codes, const uint32_t (&w)[8], int e, int gv, int te,
+                                                    int j) {
+  const int k = j & 3, q = j >> 2;
+  // this token's nibble of column n: word n / 2, bits 16 (n % 2) + se
+  const int se = 8 * (e >> 1) + 4 * (e & 1);
+  uint32_t x[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) x[m] = (w[m] >> se) & 0x000F000Fu;
+  // E[r] (16 bits, nibble i = column r + 4 i): V0 = (E[0], E[1]), V1 = (E[2], E[3])
+  const uint32_t V0 = x[0] | (x[2] << 4) | (x[4] << 8) | (x[6] << 12);
+  const uint32_t V1 = x[1] | (x[3] << 4) | (x[5] << 8) | (x[7] << 12);
+  // transpose E across the quad: lane k ends with E of every n-tile for r = k
+  const bool b1 = (k & 2) != 0, b0 = (k & 1) != 0;
+  const uint32_t A = b1 ? V1 : V0;                       // own E[rb], E[rb + 1], rb = 2 b1
+  const uint32_t B = lane_xor_u32<2>(b1 ? V0 : V1);      // lane k ^ 2's
+  const uint32_t lo = __builtin_amdgcn_perm(B, A, 0x05040100u), hi = __builtin_amdgcn_perm(B, A, 0x07060302u);
+  const uint32_t keep = b0 ? hi : lo;                    // (E_k, E_{k^2}) for r = k
+  const uint32_t R = lane_xor_u32<1>(b0 ? lo : hi);      // (E_{k^1}, E_{k^3}) for r = k
+  const uint32_t X = b0 ? R : keep, Y = b0 ? keep : R;   // n-tiles (0, 2) and (1, 3), swapped when b1
+  const uint32_t xy_lo = __builtin_amdgcn_perm(Y, X, 0x05040100u), xy_hi = __builtin_amdgcn_perm(Y, X, 0x07060302u);
+  const uint32_t P = b1 ? xy_hi : xy_lo;                 // n-tiles 4q, 4q + 1 at bits 0, 16
+  const uint32_t Q = b1 ? xy_lo : xy_hi;                 // n-tiles 4q + 2, 4q + 3
+  const int st = 8 * (te >> 1) + 4 * (te & 1);           // the slot's nibble in its byte pair
+  const uint64_t mask = 0x000F000F000F000Full << st;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const uint64_t v = ((uint64_t)((Q >> (4 * m)) & 0x000F000Fu) << 32) | ((P >> (4 * m)) & 0x000F000Fu);
+    unsigned long long* wp = reinterpret_cast<unsigned long long*>(
+        codes + (q >> 1) * 1024 + (gv * 16 + k + 4 * m) * 16 + (q & 1) * 8);
+    atomicAnd(wp, ~mask);
+    atomicOr(wp, v << st);
   }
 }
 
@@ -522,7 +554,8 @@ __device__ __forceinline__ void v_row_group(uint8_t* __restrict__ pool, const ui
           const float amax = max_over_lanes<GS / F>(abs_max<F>(x[h2]));
           group_scale<C>(amax, s[h2], r[h2], sb[2 * pr + h2]);
           if constexpr (C != C_E4MX)
-            if (!(s[h2] > 0.0f)) keep &= ~(0xFFu << (8 * (2 * pr + h2)));
+            if (!(s[h2] > 0.0f))
+              keep &= BITS == 4 ? ~(0x000F000Fu << (8 * pr + 4 * h2)) : ~(0xFFu << (8 * (2 * pr + h2)));
         }
       }
       auto quot = [&](int h2, float xv) -> float {
@@ -541,18 +574,18 @@ __device__ __forceinline__ void v_row_group(uint8_t* __restrict__ pool, const ui
                           : e4m3_pair<false>(0u, quot(0, x[0][i]), quot(1, x[1][i]));
           }
         }
-      } else {  // 4-bit: elements i and i + 8 of the lane's n-tile share a byte
+      } else {  // 4-bit: one element of tokens 2 pr and 2 pr + 1 per byte
 #pragma unroll
-        for (int i = 0; i < F / 2; ++i) {
-          uint32_t w = pr ? out.w[i] : 0u;
+        for (int m = 0; m < F / 2; ++m) {
+          uint32_t w = pr ? out.w[m] : 0u;
           if (pr == 0) {
-            w = e2m1_pair<0>(w, quot(0, x[0][i]), quot(0, x[0][i + 8]));
-            w = e2m1_pair<1>(w, quot(1, x[1][i]), quot(1, x[1][i + 8]));
+            w = e2m1_pair<0>(w, quot(0, x[0][2 * m]), quot(1, x[1][2 * m]));
+            w = e2m1_pair<2>(w, quot(0, x[0][2 * m + 1]), quot(1, x[1][2 * m + 1]));
           } else {
-            w = e2m1_pair<2>(w, quot(0, x[0][i]), quot(0, x[0][i + 8]));
-            w = e2m1_pair<3>(w, quot(1, x[1][i]), quot(1, x[1][i + 8]));
+            w = e2m1_pair<1>(w, quot(0, x[0][2 * m]), quot(1, x[1][2 * m]));
+            w = e2m1_pair<3>(w, quot(0, x[0][2 * m + 1]), quot(1, x[1][2 * m + 1]));
           }
-          out.w[i] = w;
+          out.w[m] = w;
         }
       }
     }
@@ -576,19 +609,36 @@ __device__ __forceinline__ void v_row_group(uint8_t* __restrict__ pool, const ui
     uint8_t* hb = pool + page * geo.page_bytes + (int64_t)head * geo.head_bytes;
     uint8_t* codes = hb + geo.off_vc + (int64_t)blk * geo.vcode_blk;
     uint8_t* scales = hb + geo.off_vs + (int64_t)blk * geo.vscale_blk;
-    if constexpr (D == 256 && BITS != 16) {
+    if constexpr (D == 256 && BITS == 8) {
       // the 16-byte tile chunk of n-tiles 4a .. 4a + 3 (lanes 4a + c) and one
       // n: transpose each 4 x 4 block of words across the quad so that lane
       // c holds the chunk of n = 4 m + c
-      constexpr int NWORDS = BITS == 8 ? F : F / 2;
 #pragma unroll
-      for (int m = 0; m < NWORDS / 4; ++m) {
+      for (int m = 0; m < F / 4; ++m) {
         uint32_t W[4] = {out.w[4 * m], out.w[4 * m + 1], out.w[4 * m + 2], out.w[4 * m + 3]};
         quad_transpose(W, j & 3);
         const int n = 4 * m + (j & 3);
-        uint8_t* dst = BITS == 8 ? codes + (jt >> 2) * 1024 + (gv * 16 + n) * 16 : codes + (jt >> 2) * 512 + (gv * 8 + n) * 16;
-        *reinterpret_cast<uint4*>(dst) = make_uint4(W[0], W[1], W[2], W[3]);
+        *reinterpret_cast<uint4*>(codes + (jt >> 2) * 1024 + (gv * 16 + n) * 16) = make_uint4(W[0], W[1], W[2], W[3]);
       }
+    } else if constexpr (D == 256 && BITS == 4) {
+      // the 16-byte tile rows n of chunk jt / 8 hold n-tiles 8c .. 8c + 7
+      // (lanes 8c + k), 2 bytes each: transpose the 8 x 8 words across the
+      // group so that lane k holds columns 2k and 2k + 1 of all 8 n-tiles,
+      // then the low halves form row n = 2k and the high halves row 2k + 1
+      const int k = j & 7;
+      uint32_t W[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) W[m] = out.w[m];
+      oct_transpose(W, k);
+      uint32_t lo[4], hi[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lo[i] = __builtin_amdgcn_perm(W[2 * i + 1], W[2 * i], 0x05040100u);
+        hi[i] = __builtin_amdgcn_perm(W[2 * i + 1], W[2 * i], 0x07060302u);
+      }
+      uint8_t* dst = codes + (jt >> 3) * 1024 + (gv * 16 + 2 * k) * 16;
+      *reinterpret_cast<uint4*>(dst) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      *reinterpret_cast<uint4*>(dst + 16) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
     } else if constexpr (D == 256) {
       // 16-bit: the chunk of n-tiles 2b, 2b + 1 (lanes 2b + p) and one n;
       // lane p of a pair assembles n = 2 q + p
@@ -626,11 +676,12 @@ __device__ __forceinline__ void v_row_group(uint8_t* __restrict__ pool, const ui
         }
       }
     }
-  } else if (ok[0] && ok[1] && ok[2] && ok[3] && slot[1] == slot[0] + 1 && slot[2] == slot[0] + 2 &&
-             slot[3] == slot[0] + 3) {
+  } else if (BITS != 4 && ok[0] && ok[1] && ok[2] && ok[3] && slot[1] == slot[0] + 1 &&
+             slot[2] == slot[0] + 2 && slot[3] == slot[0] + 3) {
     // consecutive slots s0 .. s0 + 3 with a = s0 % 4 != 0: tokens 0 .. 3 - a
     // go to positions a .. 3 of slab s0 - a, tokens 4 - a .. 3 to positions
-    // 0 .. a - 1 of the next slab
+    // 0 .. a - 1 of the next slab (4-bit codes share bytes between tokens
+    // and take the per-token path below)
     const int a = slot[0] & 3;
     uint8_t* cw[2];
     int gvv[2];
@@ -643,16 +694,14 @@ __device__ __forceinline__ void v_row_group(uint8_t* __restrict__ pool, const ui
       cw[h2] = pool + page * geo.page_bytes + (int64_t)head * geo.head_bytes + geo.off_vc +
                (int64_t)(off >> 4) * geo.vcode_blk;
     }
-    constexpr int NG = BITS == 4 ? F / 2 : F;  // 4-token groups per lane
 #pragma unroll
-    for (int i = 0; i < NG; ++i) {
+    for (int i = 0; i < F; ++i) {
       int o[2];
       uint64_t W;
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
-        o[h2] = BITS == 8  ? (jt >> 2) * 1024 + (gvv[h2] * 16 + n0 + i) * 16 + (jt & 3) * 4
-              : BITS == 16 ? (jt >> 1) * 1024 + (gvv[h2] * 16 + n0 + i) * 16 + (jt & 1) * 8
-                           : (jt >> 2) * 512 + (gvv[h2] * 8 + i) * 16 + (jt & 3) * 4;
+        o[h2] = BITS == 8 ? (jt >> 2) * 1024 + (gvv[h2] * 16 + n0 + i) * 16 + (jt & 3) * 4
+                          : (jt >> 1) * 1024 + (gvv[h2] * 16 + n0 + i) * 16 + (jt & 1) * 8;
       if constexpr (BITS == 16) W = (uint64_t)out.w[2 * i] | ((uint64_t)out.w[2 * i + 1] << 32);
       else W = out.w[i];
       constexpr int TB = BITS == 16 ? 2 : 1;
@@ -695,9 +744,12 @@ __device__ __forceinline__ void v_row_group(uint8_t* __restrict__ pool, const ui
           *reinterpret_cast<uint16_t*>(codes + (jt >> 1) * 1024 + (gv * 16 + n0 + i) * 16 + (jt & 1) * 8 + 2 * te) =
               (uint16_t)(out.w[2 * i + (e >> 1)] >> (16 * (e & 1)));
       } else {
-#pragma unroll
-        for (int i = 0; i < F / 2; ++i)
-          codes[(jt >> 2) * 512 + (gv * 8 + i) * 16 + (jt & 3) * 4 + te] = (uint8_t)(out.w[i] >> (8 * e));
+        // 4-bit: this token's nibble of each column shares its byte with
+        // the other token of its pair (written by this call or another), so
+        // the nibbles are set with atomic and/or, which leave the partner's
+        // bits alone whoever writes them and in whatever order
+        static_assert(F == 16, "one n-tile per lane");
+        store_token_nibbles(codes, out.w, e, gv, te, j);
       }
       if constexpr (scale_bytes(C) > 0) {
         if (lead) {
@@ -712,11 +764,14 @@ __device__ __forceinline__ void v_row_group(uint8_t* __restrict__ pool, const ui
 
 // One V item: the V rows of 16 consecutive tokens b0 .. b0 + 15 of one kv
 // head, 4 tokens per row of 16 lanes.  When the slots from a = slot(b0) % 4
-// slots earlier run on consecutively for 16 tokens, the item takes that
-// window instead, so every row holds one whole slab of the tile; the a
-// tokens before b0 then get written by this item too (with the bytes their
-// own item writes), and its own last a tokens are left to the next item if
-// that one takes the same kind of window, else done here in a second pass.
+// slots earlier run on consecutively for 16 tokens, the item starts its
+// window a tokens early instead, so every row holds one whole slab of the
+// tile.  Item X writes exactly the tokens from its own window start up to
+// the next item's (which it decides from the same slots the next item
+// sees), so every token is written once: the rows take the first 16 and a
+// second pass of row 0 the at most 3 left when the next window starts
+// later than this one ends.  So a tile word is written either by one whole
+// slab store or only by the atomics of the 4-bit per-token path.
 template <int FMT, int D>
 __device__ __forceinline__ void append_v_wave(uint8_t* __restrict__ pool, const uint16_t* __restrict__ v,
                                               int64_t T, const int32_t* __restrict__ slots, const Geometry& geo,
@@ -725,35 +780,34 @@ __device__ __forceinline__ void append_v_wave(uint8_t* __restrict__ pool, const 
   const int head = (int)(vw - tg * geo.H_kv);
   const int j = lane & 15, row = lane >> 4;
   const int64_t b0 = tg * 16;
-  int a = 0;
-  bool shifted = false, tail_here = false;
+  int64_t lo = b0, hi = b0 + 16;  // this item's tokens
   if constexpr (D == 256) {
     // lane l holds the slot of token b0 - 3 + l (l < 35; -1 outside [0, T)):
     // both windows are decided from these values with lane votes
     const int64_t tl = b0 - 3 + lane;
     const int sl = (lane < 35 && tl >= 0 && tl < T) ? slots[tl] : -1;
-    // do the 16 tokens from lane l0 on have slots s, s + 1, ...?  (s = slot at lane l0 + a)
-    auto runs_on = [&](int l0, int s) -> bool {
-      const bool in = lane >= l0 && lane < l0 + 16;
-      return __all(!in || (s >= 0 && sl == s + (lane - l0)));
+    // does every group of 4 tokens from lane l0 on fill one slab (slots
+    // 4i, 4i + 1, 4i + 2, 4i + 3 of one page)?  Pages hold whole slabs, so
+    // a run of slots that crosses pages still qualifies.
+    auto slabs_from = [&](int l0) -> bool {
+      const int k = lane - l0;
+      const int f = __shfl(sl, l0 + (k & ~3));  // slot of the group's first token
+      const bool in = k >= 0 && k < 16;
+      return __all(!in || (sl >= 0 && (sl & 3) == (k & 3) && (sl >> 2) == (f >> 2)));
     };
-    const int s0 = __shfl(sl, 3);
-    if (s0 >= 0) {
-      a = s0 & 3;
-      shifted = runs_on(3 - a, s0 - a);
-      if (shifted && a > 0) {
-        const int s1 = __shfl(sl, 19);
-        tail_here = !(s1 >= 0 && (s1 & 3) == a && runs_on(19 - a, s1 - a));
-      }
-    }
+    // the window shift of the item whose first token sits at lane l0 + 3
+    auto window_shift = [&](int l0) -> int {
+      const int s = __shfl(sl, l0 + 3);
+      if (s < 0) return 0;
+      const int a = s & 3;
+      return slabs_from(l0 + 3 - a) ? a : 0;
+    };
+    lo = b0 - window_shift(0);
+    hi = b0 + 16 - window_shift(16);
   }
-  if (shifted) {
-    v_row_group<FMT, D>(pool, v, slots, geo, v_scale, head, j, b0 - a + 4 * row, b0 - a, b0 - a + 16);
-    if (tail_here && row == 0)
-      v_row_group<FMT, D>(pool, v, slots, geo, v_scale, head, j, b0 + 16 - a, b0 + 16 - a, b0 + 16 < T ? b0 + 16 : T);
-  } else {
-    v_row_group<FMT, D>(pool, v, slots, geo, v_scale, head, j, b0 + 4 * row, b0, b0 + 16 < T ? b0 + 16 : T);
-  }
+  if (hi > T) hi = T;
+  v_row_group<FMT, D>(pool, v, slots, geo, v_scale, head, j, lo + 4 * row, lo, hi < lo + 16 ? hi : lo + 16);
+  if (hi > lo + 16 && row == 0) v_row_group<FMT, D>(pool, v, slots, geo, v_scale, head, j, lo + 16, lo + 16, hi);
 }
 
 // One K item: the K rows of 16 consecutive tokens of one kv head.

@@ -79,7 +79,7 @@ struct DT {
   static constexpr bool DOUBLE_BUF = D == 128 || FMT == F_FP8_ROW || FMT == F_FP8_TENSOR;
   static constexpr int NT = D / 16;
   static constexpr int KCH = D * KBITS / 512;                       // 16-B K chunks per lane per block
-  static constexpr int VCH = (VBITS == 16 ? 2 : 1) * NT * 4 / 16;   // 16-B V chunks per lane per block
+  static constexpr int VCH = VBITS * NT / 32;                       // 16-B V chunks per lane per block
   static constexpr int KSW = KC == C_E4ROW ? 2 : KC == C_I8G64 ? 8 : KC == C_E4MX ? D / 32 : KC == C_E2G16 ? 4 : 0;
   static constexpr int VSW = VC == C_E4ROW ? 2 : VC == C_I8G64 ? 8 : VC == C_E4MX ? D / 32 : VC == C_E2G16 ? 16 : 0;
   static constexpr int G = n_groups(KC, D) > 0 ? n_groups(KC, D) : 1;
@@ -153,15 +153,10 @@ __device__ __forceinline__ void load_v(Buf<FMT, D>& buf, const uint8_t* head0, c
                                        const cint32* bt_row, int j, int lane) {
   using T = DT<FMT, D>;
   const BlockAddr ba = block_addr(head0, geo, bt_row, j);
-  const int g = lane >> 4, c16 = lane & 15;
+  const int g = lane >> 4;
   const uint8_t* vc = ba.hb + geo.off_vc + (int64_t)ba.bip * geo.vcode_blk;
 #pragma unroll
-  for (int q = 0; q < T::VCH; ++q) {
-    if constexpr (T::VBITS == 4)
-      buf.v[q] = *reinterpret_cast<const uint4*>(vc + q * 512 + (g * 8 + (c16 & 7)) * 16);
-    else
-      buf.v[q] = *reinterpret_cast<const uint4*>(vc + q * 1024 + lane * 16);
-  }
+  for (int q = 0; q < T::VCH; ++q) buf.v[q] = *reinterpret_cast<const uint4*>(vc + q * 1024 + lane * 16);
   if constexpr (T::VSW > 0) {
     const uint8_t* vs = ba.hb + geo.off_vs + (int64_t)ba.bip * geo.vscale_blk;
     load_words(buf.vs, vs + g * (4 * T::VSW));
@@ -325,9 +320,8 @@ __device__ __forceinline__ void read_stage_k(Buf<FMT, D>& buf, uint32_t stage, i
 template <int FMT, int D>
 __device__ __forceinline__ void read_stage_v(Buf<FMT, D>& buf, uint32_t stage, int lane) {
   using T = DT<FMT, D>;
-  const int g = lane >> 4, c16 = lane & 15;
-  const uint32_t ca = stage + T::SV + (T::VBITS == 4 ? (g * 8 + (c16 & 7)) * 16 : lane * 16);
-  lds_read_part<T::VCH, T::VBITS == 4 ? 512 : 1024, T::VSW>(buf.v, buf.vs, ca, stage + T::SVS + g * (4 * T::VSW));
+  const int g = lane >> 4;
+  lds_read_part<T::VCH, 1024, T::VSW>(buf.v, buf.vs, stage + T::SV + lane * 16, stage + T::SVS + g * (4 * T::VSW));
 }
 
 // ----------------------------------------------------------- operand expanders
@@ -529,14 +523,17 @@ __device__ __forceinline__ f16x4 v_operand(const Buf<FMT, D>& buf, int nt, int l
     a *= bitcast<f16x2>(s01);
     b *= bitcast<f16x2>(s23);
     return f16x4{a[0], a[1], b[0], b[1]};
-  } else {  // C_E2G16: byte e holds (token 4g+e, n) low and (token 4g+e, n+8) high
-    const uint32_t w = word(buf.v[nt >> 2], nt & 3);
-    const uint32_t x = w >> (((lane & 15) >= 8) ? 4 : 0);  // this lane's nibble of each byte in bits 0-3
-    // byte 0: t0 | t1 << 4, byte 2: t2 | t3 << 4 (bytes 1, 3 unused)
-    uint32_t y;  // (x & 0x0F0F0F0F) | ((x >> 4) & 0xF0F0F0F0) in one bitfield insert
-    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(y) : "v"(0x0F0F0F0Fu), "v"(x), "v"(x >> 4));
-    f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y, 1.0f, 0);
-    f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(y, 1.0f, 2);
+  } else {  // C_E2G16: bytes 2 (nt & 1) and 2 (nt & 1) + 1 of word (nt & 7) / 2 of chunk nt / 8
+            // hold tokens (4g, 4g + 1) and (4g + 2, 4g + 3) of column n, the earlier token low
+    const uint32_t w = word(buf.v[nt >> 3], (nt & 7) >> 1);
+    f16x2 a, b;
+    if (nt & 1) {
+      a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+      b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+    } else {
+      a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+      b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+    }
     const uint32_t sw = buf.vs[nt];  // UE4M3 of tokens 4g..4g+3, group nt
     a *= __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)sw, 1.0f, false);
     b *= __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)sw, 1.0f, true);
@@ -600,12 +597,16 @@ __device__ __forceinline__ void clear_tail(Buf<FMT, D>& buf, int nvalid, int g) 
   for (int e = 0; e < 4; ++e) bmask |= (e < nv) ? (0xFFu << (8 * e)) : 0u;
   const uint32_t h01 = (nv > 0 ? 0xFFFFu : 0u) | (nv > 1 ? 0xFFFF0000u : 0u);
   const uint32_t h23 = (nv > 2 ? 0xFFFFu : 0u) | (nv > 3 ? 0xFFFF0000u : 0u);
+  // 4-bit codes: nibble i of every word belongs to token i % 4
+  const uint32_t n16 = nv >= 4 ? 0xFFFFu : nv <= 0 ? 0u : (1u << (4 * nv)) - 1u;
+  const uint32_t nmask = n16 | (n16 << 16);
 #pragma unroll
   for (int q = 0; q < T::VCH; ++q) {
     if constexpr (T::VBITS == 16) {
       buf.v[q].x &= h01; buf.v[q].y &= h23; buf.v[q].z &= h01; buf.v[q].w &= h23;
     } else {
-      buf.v[q].x &= bmask; buf.v[q].y &= bmask; buf.v[q].z &= bmask; buf.v[q].w &= bmask;
+      const uint32_t m = T::VBITS == 4 ? nmask : bmask;
+      buf.v[q].x &= m; buf.v[q].y &= m; buf.v[q].z &= m; buf.v[q].w &= m;
     }
   }
   if constexpr (T::VC == C_E4ROW) {

@@ -31,7 +31,7 @@ __device__ __forceinline__ float stored_value(const uint8_t* codes, const uint8_
     else if constexpr (BITS == 8)
       code = codes[(jt >> 2) * 1024 + (g * 16 + n) * 16 + (jt & 3) * 4 + e];
     else
-      code = (codes[(jt >> 2) * 512 + (g * 8 + (n & 7)) * 16 + (jt & 3) * 4 + e] >> (n >= 8 ? 4 : 0)) & 0xFu;
+      code = (codes[(jt >> 3) * 1024 + (g * 16 + n) * 16 + (jt & 7) * 2 + (e >> 1)] >> ((e & 1) * 4)) & 0xFu;
   }
   if constexpr (C == C_BF16) return bf16_to_f32(code);
   if constexpr (C == C_F16) return f16_bits_to_f32(code);

@@ -28,11 +28,13 @@
 //   V codes, t = 4g + e, d = 16*jt + n:
 //     8-bit:  byte = (jt/4)*1024 + (g*16+n)*16 + (jt%4)*4 + e
 //     16-bit: byte = (jt/2)*1024 + (g*16+n)*16 + (jt%2)*8 + 2e
-//     4-bit:  byte = (jt/4)*512 + (g*8 + n%8)*16 + (jt%4)*4 + e,
-//             high nibble for n >= 8 (a byte never mixes two tokens)
+//     4-bit:  byte = (jt/8)*1024 + (g*16+n)*16 + (jt%8)*2 + e/2,
+//             high nibble for odd e (a byte holds column n of the token
+//             pair 4g + 2p, 4g + 2p + 1)
 //   This is the B-operand order of v_mfma_f32_16x16x16_f16 for the product
 //   P (rows x tokens) . V (tokens x d): lane g*16+n holds tokens 4g..4g+3 of
-//   column n of n-tile jt.
+//   column n of n-tile jt; for 4-bit codes each byte converts straight into
+//   the f16 pair (4g + 2p, 4g + 2p + 1) of one operand register.
 //
 //   Scales, G groups per row: fp16 scales at (t*G + grp)*2; UE8M0 and the K
 //   UE4M3 bytes at t*G + grp; V UE4M3 bytes at (t/4)*4G + grp*4 + t%4.

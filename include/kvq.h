@@ -111,7 +111,10 @@ kvq_status kvq_page_bytes(const kvq_cache_desc* desc, size_t* bytes_per_page);
  *  slot_mapping  device int32 [num_tokens]: page * page_size + offset;
  *                a negative entry skips that token.  Two tokens must not
  *                share a slot in one call.
- * Only the bytes of the written slots change.  num_tokens == 0 is a no-op. */
+ * Only the bits of the written slots change: 4-bit V codes share each byte
+ * between two neighbouring slots, and the other slot's nibble is kept, also
+ * when both are written by different calls in any order.  num_tokens == 0
+ * is a no-op. */
 kvq_status kvq_quantize_append(const kvq_cache_desc* desc, void* pool,
                                const void* k_bf16, const void* v_bf16,
                                int64_t num_tokens, const int32_t* slot_mapping,

@@ -26,9 +26,10 @@ V codes (t = 4 * g + e, d = 16 * jt + n)::
 
     8-bit:  byte = (jt // 4) * 1024 + (g * 16 + n) * 16 + (jt % 4) * 4 + e
     16-bit: byte = (jt // 2) * 1024 + (g * 16 + n) * 16 + (jt % 2) * 8 + 2 e
-    4-bit:  byte = (jt // 4) * 512 + (g * 8 + n % 8) * 16 + (jt % 4) * 4 + e,
-            high nibble when n >= 8 (both nibbles of a byte belong to the
-            same token, so writing one token never touches another's bits)
+    4-bit:  byte = (jt // 8) * 1024 + (g * 16 + n) * 16 + (jt % 8) * 2 + e // 2,
+            high nibble when e is odd: a byte holds column n of the token
+            pair (4 g + 2 p, 4 g + 2 p + 1), so writing one token changes
+            one nibble of each byte it touches and keeps the other
 
 Scales (G groups per row)::
 
@@ -109,7 +110,7 @@ def v_code_pos(bits, t, d):
     if bits == 16:
         return (jt // 2) * 1024 + (g * 16 + n) * 16 + (jt % 2) * 8 + 2 * e, np.zeros_like(d, bool)
     if bits == 4:
-        return (jt // 4) * 512 + (g * 8 + n % 8) * 16 + (jt % 4) * 4 + e, n >= 8
+        return (jt // 8) * 1024 + (g * 16 + n) * 16 + (jt % 8) * 2 + e // 2, e % 2 == 1
     raise ValueError(bits)
 
 
@@ -159,13 +160,13 @@ def _write_codes(pool, geo, plane, base, blk, t, codes, bits):
     else:
         hi = np.broadcast_to(hi, (n, D))
         c = codes.astype(np.uint8) & 0xF
-        # both nibbles of every touched byte come from this row, so the byte
-        # is assembled first and then stored whole
+        # a byte holds two values of one K row, or one column of two V
+        # tokens: clear this row's nibbles, then set them, so that the other
+        # nibble keeps whatever it held (rows of one call use distinct slots)
         val = np.where(hi, c << 4, c).astype(np.uint8)
-        uniq, inv = np.unique(addr.ravel(), return_inverse=True)
-        acc = np.zeros(len(uniq), dtype=np.uint8)
-        np.bitwise_or.at(acc, inv, val.ravel())
-        pool[uniq] = acc
+        own = np.where(hi, 0xF0, 0x0F).astype(np.uint8)
+        np.bitwise_and.at(pool, addr.ravel(), ~own.ravel())
+        np.bitwise_or.at(pool, addr.ravel(), val.ravel())
 
 
 def _write_scales(pool, geo, plane, codec, base, blk, t, scales):

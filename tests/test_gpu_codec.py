@@ -168,3 +168,66 @@ def test_append_chunks_at_any_offset(fmt, cfg):
     # the chunks really start at every slab alignment
     starts = slots.numpy()[np.arange(4) * chunk]
     assert sorted(set((starts % 4).tolist())) == [1, 2, 3] or len(set((starts % 4).tolist())) >= 2
+
+
+@pytest.mark.parametrize("fmt,cfg", [("NVFP4_G16", 3), ("K8V4", 4), ("INT8_G64", 2), ("FP8_ROW", 2), ("MXFP8", 5),
+                                     ("BF16", 1)])
+def test_append_slots_in_random_order(fmt, cfg):
+    """One call writes every slot of a few pages in random input order, so the
+    tokens that share a slab (and, for 4-bit V, a byte) sit in different rows
+    and waves and are stored concurrently, token by token."""
+    require_gpu()
+    c = W.make_case(cfg, fmt, device="cpu", B=1, lengths=[8])
+    geo = OL.Geometry(c.fmt, c.D, c.P, c.H_kv)
+    num_pages = 4
+    d = kvq.desc(c.fmt, c.D, c.P, c.H_kv, num_pages, c.k_scale, c.v_scale)
+    n = num_pages * c.P
+    gen = torch.Generator().manual_seed(41)
+    k = (torch.randn((n, c.H_kv, c.D), generator=gen) * 2.0).to(torch.bfloat16)
+    v = torch.randn((n, c.H_kv, c.D), generator=gen).to(torch.bfloat16)
+    slots = torch.as_tensor(np.random.default_rng(41).permutation(n).astype(np.int32))
+    pool = kvq.alloc_pool(d, fill=0x5A)
+    note("append random order", fmt)
+    kvq.quantize_append(d, pool, k.cuda(), v.cuda(), slots.cuda())
+    torch.cuda.synchronize()
+    ref = np.full(num_pages * geo.page_bytes, 0x5A, np.uint8)
+    OA.quantize_append(geo, ref, W.bf16_bits(k), W.bf16_bits(v), slots.numpy(), c.k_scale, c.v_scale)
+    got = pool.cpu().numpy()
+    diff = np.flatnonzero(got != ref)
+    assert diff.size == 0, "%s: %d bytes differ at %s: got %s ref %s" % (fmt, diff.size, diff[:8], got[diff[:8]],
+                                                                        ref[diff[:8]])
+
+
+@pytest.mark.parametrize("fmt,cfg", [("NVFP4_G16", 3), ("K8V4", 4), ("FP8_ROW", 2)])
+def test_single_token_steps_and_rewrites(fmt, cfg):
+    """Decode-style appends of one token per sequence, step after step (the
+    even and odd tokens of each 4-bit V byte pair arrive in different calls),
+    and a rewrite of an already written slot with new values after each step
+    (a rejected draft token): the pool matches the oracle after every call."""
+    lens = [6, 65, 11]
+    steps = 5
+    c = W.make_case(cfg, fmt, device="cpu", B=3, lengths=lens, reserve=steps)
+    bl = build(c)
+    k_all, v_all, slots_all = W.append_chunk(c, steps)
+    slots_all = slots_all.numpy().reshape(c.B, steps)
+    k_all = k_all.reshape(c.B, steps, c.H_kv, c.D)
+    v_all = v_all.reshape(c.B, steps, c.H_kv, c.D)
+    gen = torch.Generator().manual_seed(43)
+    for s in range(steps):
+        k, v = k_all[:, s].contiguous(), v_all[:, s].contiguous()
+        sl = torch.as_tensor(slots_all[:, s].copy())
+        calls = [(k, v, sl)]
+        # rewrite the token just written to sequence s % B with other values
+        b = s % c.B
+        calls.append(((torch.randn((1, c.H_kv, c.D), generator=gen) * 3.0).to(torch.bfloat16),
+                      torch.randn((1, c.H_kv, c.D), generator=gen).to(torch.bfloat16),
+                      torch.as_tensor(slots_all[b:b + 1, s].copy())))
+        for kk, vv, ss in calls:
+            note("single token step", fmt, "step", s, "slots", ss.tolist())
+            kvq.quantize_append(bl.desc, bl.pool_gpu, kk.cuda(), vv.cuda(), ss.cuda())
+            torch.cuda.synchronize()
+            OA.quantize_append(bl.geo, bl.pool_ref, W.bf16_bits(kk), W.bf16_bits(vv), ss.numpy(), c.k_scale,
+                               c.v_scale)
+            got, ref, diff = _mismatch(bl)
+            assert diff.size == 0, "%s step %d: %d bytes differ at %s: got %s ref %s" % (
+                fmt, s, diff.size, diff[:8], got[diff[:8]], ref[diff[:8]])

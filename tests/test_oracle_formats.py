@@ -207,10 +207,15 @@ def test_code_layouts_are_bijections(bits, D):
         if bits == 4:
             key = byte * 2 + hi
             assert np.array_equal(np.sort(key), np.arange(2 * nbytes))
-            # both nibbles of a byte belong to one token
             owner = {}
-            for b, tt in zip(byte, t):
-                assert owner.setdefault(int(b), int(tt)) == tt
+            for b, tt, dd, h in zip(byte, t, d, hi):
+                owner.setdefault(int(b), []).append((int(h), int(tt), int(dd)))
+            for vals in owner.values():
+                (h0, t0, d0), (h1, t1, d1) = sorted(vals)
+                if pos_fn is Lo.k_code_pos:  # two consecutive values of one token
+                    assert t0 == t1 and d1 == d0 + 1 and d0 % 2 == 0
+                else:  # one column of an (even, odd) token pair, the even one low
+                    assert d0 == d1 and t1 == t0 + 1 and t0 % 2 == 0
         else:
             assert np.array_equal(np.sort(byte), np.arange(0, nbytes, per))
 
@@ -248,3 +253,23 @@ def test_write_read_round_trip_and_isolation():
         r0 = Lo.read_rows(before, geo, other, 1)
         r1 = Lo.read_rows(pool, geo, other, 1)
         assert all(np.array_equal(a, b) for a, b in zip(r0, r1) if a is not None)
+
+
+@pytest.mark.parametrize("fmt", [3, 4])
+def test_token_pair_written_in_two_calls(fmt):
+    """4-bit V bytes hold one column of two tokens: writing the two tokens of
+    a pair in two calls, in either order, gives the bytes one call gives."""
+    geo = Lo.Geometry(fmt, 256, 64, 2)
+    rng = np.random.default_rng(31)
+    slots = np.array([6, 7, 9, 8, 17, 40])  # pairs (6, 7), (8, 9); 17 and 40 alone
+    kc = rng.integers(0, 256 if fmt == 4 else 16, (6, 256))
+    vc = rng.integers(0, 16, (6, 256))
+    ks = rng.integers(0, 1 << 16, (6, 1)) if fmt == 4 else rng.integers(0, 256, (6, 16))
+    vs = rng.integers(0, 256, (6, 16))
+    joint = np.full(geo.page_bytes, 0x3C, dtype=np.uint8)
+    Lo.write_rows(joint, geo, slots, 1, kc, ks, vc, vs)
+    for order in ([0, 2, 4, 5], [1, 3, 4, 5]), ([1, 3], [0, 2, 4, 5]):
+        split = np.full(geo.page_bytes, 0x3C, dtype=np.uint8)
+        for sel in order:
+            Lo.write_rows(split, geo, slots[sel], 1, kc[sel], ks[sel], vc[sel], vs[sel])
+        assert np.array_equal(split, joint)
