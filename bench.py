@@ -94,11 +94,13 @@ class Setup:
         kvq.quantize_append(self.desc, self.pool, c.k, c.v, c.slot_mapping)  # fill the cache
         self.bt = torch.as_tensor(c.block_table, device="cuda")
         self.sl = torch.as_tensor(c.seq_lens, device="cuda")
-        # the step appends each sequence's newest token (position L_b - 1) again
-        last = np.cumsum(c.seq_lens.astype(np.int64)) - 1
-        idx = torch.as_tensor(last, device="cuda")
-        self.k_new = c.k.index_select(0, idx).contiguous()
-        self.v_new = c.v.index_select(0, idx).contiguous()
+        # the step appends each sequence's n_q newest tokens (positions
+        # L_b - n_q .. L_b - 1, the decoded or drafted ones) again
+        lens = c.seq_lens.astype(np.int64)
+        idx = (np.cumsum(lens) - c.n_q)[:, None] + np.arange(c.n_q)[None, :]
+        idx = torch.as_tensor(idx.reshape(-1), device="cuda")
+        self.k_new = c.k.index_select(0, idx).view(c.B, c.n_q, c.H_kv, c.D).contiguous()
+        self.v_new = c.v.index_select(0, idx).view(c.B, c.n_q, c.H_kv, c.D).contiguous()
         self.slot_new = c.slot_mapping.index_select(0, idx).contiguous()
         self.q = c.q
         self.nwg, self.slots = kvq.decode_plan(self.desc, c.B, c.n_q, c.H_q, c.max_pages)
@@ -109,22 +111,28 @@ class Setup:
         self.kv_bytes = int(c.seq_lens.astype(np.int64).sum()) * c.H_kv * self.bpt
         torch.cuda.synchronize()
 
-    def step(self, stream, ev=None):
+    def step(self, stream, ev=None, fused=True):
+        """One decode step: append the new tokens, attend, reduce.  Fused: the
+        two launches kvq_decode_step makes (the split kernel stores the new
+        tokens), timed apart; else quantize-append and the two launches of
+        kvq_decode_attention."""
         c = self.case
-        if ev is not None:
-            ev[0].record(stream)
-        kvq.quantize_append(self.desc, self.pool, self.k_new, self.v_new, self.slot_new, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
-        # the two launches kvq_decode_attention makes, timed apart
-        kvq.decode_split(self.desc, self.pool, self.q, self.bt, self.sl, c.softmax_scale, self.ws,
-                         flags=kvq.SPLIT_WRITE_WHOLE_UNITS, out=self.out, lse=self.lse, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
+        rec = (lambda i: ev[i].record(stream)) if ev is not None else (lambda i: None)
+        rec(0)
+        if fused:
+            kvq.decode_step_split(self.desc, self.pool, self.k_new, self.v_new, self.q, self.bt, self.sl,
+                                  c.softmax_scale, self.ws, flags=kvq.SPLIT_WRITE_WHOLE_UNITS, out=self.out,
+                                  lse=self.lse, stream=stream)
+        else:
+            kvq.quantize_append(self.desc, self.pool, self.k_new.view(-1, c.H_kv, c.D),
+                                self.v_new.view(-1, c.H_kv, c.D), self.slot_new, stream=stream)
+            rec(1)
+            kvq.decode_split(self.desc, self.pool, self.q, self.bt, self.sl, c.softmax_scale, self.ws,
+                             flags=kvq.SPLIT_WRITE_WHOLE_UNITS, out=self.out, lse=self.lse, stream=stream)
+        rec(2)
         kvq.decode_combine(self.desc, c.B, c.n_q, c.H_q, c.max_pages, self.sl, self.ws, self.out, self.lse,
                            flags=kvq.SPLIT_WRITE_WHOLE_UNITS, stream=stream)
-        if ev is not None:
-            ev[3].record(stream)
+        rec(3)
 
 
 class Probe:
@@ -167,8 +175,8 @@ def _stats(x):
             "p90": float(np.percentile(x, 90))}
 
 
-def time_steps(s, steps, warmup, stream, probe=None):
-    """Per-step HIP-event times (ms) of the step and of its three launches.
+def time_steps(s, steps, warmup, stream, probe=None, fused=True):
+    """Per-step HIP-event times (ms) of the step and of its launches.
 
     With a probe, its cache-evicting read runs before each step, outside
     the step's events; the wall time between the first and last step then
@@ -177,7 +185,7 @@ def time_steps(s, steps, warmup, stream, probe=None):
         for _ in range(warmup):
             if probe is not None:
                 probe.flush(stream)
-            s.step(stream)
+            s.step(stream, fused=fused)
         torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
@@ -186,16 +194,20 @@ def time_steps(s, steps, warmup, stream, probe=None):
         for i in range(steps):
             if probe is not None:
                 probe.flush(stream)
-            s.step(stream, evs[i])
+            s.step(stream, evs[i], fused=fused)
         t1.record(stream)
         torch.cuda.synchronize()
-    return {
+    t = {
         "wall": t0.elapsed_time(t1) / steps,
         "step": _stats([e[0].elapsed_time(e[3]) for e in evs]),
-        "append": _stats([e[0].elapsed_time(e[1]) for e in evs]),
-        "split": _stats([e[1].elapsed_time(e[2]) for e in evs]),
         "combine": _stats([e[2].elapsed_time(e[3]) for e in evs]),
     }
+    if fused:
+        t["split"] = _stats([e[0].elapsed_time(e[2]) for e in evs])
+    else:
+        t["append"] = _stats([e[0].elapsed_time(e[1]) for e in evs])
+        t["split"] = _stats([e[1].elapsed_time(e[2]) for e in evs])
+    return t
 
 
 def append_chunk_bench(formats, stream, probe, reps=10):
@@ -238,7 +250,7 @@ def append_chunk_bench(formats, stream, probe, reps=10):
 
 
 # the sources the split kernel is compiled from
-SPLIT_SOURCES = ["kvq_decode.hip", "kvq_device.hpp", "kvq_format.hpp", "kvq_internal.hpp"]
+SPLIT_SOURCES = ["kvq_decode.hip", "kvq_device.hpp", "kvq_encode.hpp", "kvq_format.hpp", "kvq_internal.hpp"]
 
 
 def kernel_sources_sha():
@@ -295,7 +307,7 @@ def summarize_counters(fetch_dir, write_dir, bench_json):
             raise SystemExit("expected one kernel matching %r, found %s" % (needle, [k for k, _ in hits]))
         return hits[0]
 
-    split_name = "decode_split_kernel<%d, %d>" % (kvq.FORMATS[fmt], line["config"]["head_dim"])
+    split_name = "decode_split_kernel<%d, %d, false>" % (kvq.FORMATS[fmt], line["config"]["head_dim"])
     kname, (f_kib, n_f) = pick(fetch, split_name)
     _, (w_kib, n_w) = pick(write, split_name)
     _, (cf_kib, _) = pick(fetch, "kvq_probe::copy_kernel")
@@ -320,7 +332,7 @@ def summarize_counters(fetch_dir, write_dir, bench_json):
 def cpu_baseline(s, budget_s=10.0):
     """The oracle as it stands, on whole sequences of the same workload (all
     kv heads; its pool built untimed), timed per decode step: append the
-    newest token, then fp64 attention over every cached page."""
+    n_q newest tokens, then fp64 attention over every cached page."""
     from threadpoolctl import threadpool_info
     from oracle import attention as OA, layout as OL
 
@@ -334,9 +346,10 @@ def cpu_baseline(s, budget_s=10.0):
         lo, hi = int(starts[b]), int(starts[b + 1])
         kb, vb = W.bf16_bits(c.k[lo:hi]), W.bf16_bits(c.v[lo:hi])
         slots = c.slot_mapping[lo:hi].cpu().numpy()
-        OA.quantize_append(geo, pool, kb[:-1], vb[:-1], slots[:-1], c.k_scale, c.v_scale)  # resident cache
+        n = c.n_q
+        OA.quantize_append(geo, pool, kb[:-n], vb[:-n], slots[:-n], c.k_scale, c.v_scale)  # resident cache
         t = time.perf_counter()
-        OA.quantize_append(geo, pool, kb[-1:], vb[-1:], slots[-1:], c.k_scale, c.v_scale)  # the step's append
+        OA.quantize_append(geo, pool, kb[-n:], vb[-n:], slots[-n:], c.k_scale, c.v_scale)  # the step's append
         OA.attention_ref(geo, pool, q_bits, c.block_table, c.seq_lens, c.softmax_scale, c.n_q, c.k_scale,
                          c.v_scale, only=[(b, h) for h in range(c.H_kv)])
         elapsed += time.perf_counter() - t
@@ -349,7 +362,7 @@ def cpu_baseline(s, budget_s=10.0):
     return {"value": nbytes / elapsed / 1e9, "unit": "GB/s", "cores": int(max(blas) if blas else 1),
             "kind": "oracle",
             "sample": "%d whole sequences (%d cached tokens x %d kv heads) of the same workload; one step each: "
-                      "append the newest token, then fp64 attention over all cached pages; %.1f s" % (
+                      "append the n_q newest tokens, then fp64 attention over all cached pages; %.1f s" % (
                           seqs, tokens, c.H_kv, elapsed)}
 
 
@@ -392,8 +405,11 @@ def main():
     for fmt in formats:
         print("[bench] %s %s: building the cache" % (args.workload, fmt), file=sys.stderr, flush=True)
         s = Setup(wl["config"], fmt)
-        t = time_steps(s, args.steps, args.warmup, stream, flush)
+        # the step as append + decode (the headline), then as one fused step
+        t = time_steps(s, args.steps, args.warmup, stream, flush, fused=False)
+        tf = time_steps(s, args.steps, args.warmup, stream, flush, fused=True)
         ms = t["step"]["mean"] if flush is not None else t["wall"]
+        ms_f = tf["step"]["mean"] if flush is not None else tf["wall"]
         c = s.case
         res = {
             "GB_per_s": s.kv_bytes / (ms * 1e-3) / 1e9,
@@ -402,15 +418,22 @@ def main():
             "step_ms": t["step"], "wall_ms_per_step": t["wall"],
             "kv_bytes": s.kv_bytes,
             "bytes_per_token": s.bpt,
+            "new_tokens_per_step": c.B * c.n_q,
             "split_kernel_ms": t["split"], "combine_ms": t["combine"], "step_append_ms": t["append"],
-            "step_append_tok_per_s": c.B / (t["append"]["mean"] * 1e-3),
             "split_workgroups": s.nwg, "partial_slots": s.slots,
+            "fused_step": {
+                "GB_per_s": s.kv_bytes / (ms_f * 1e-3) / 1e9,
+                "pct_of_hbm_peak": 100.0 * s.kv_bytes / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "ms_per_step": ms_f, "step_ms": tf["step"],
+                "split_kernel_ms": tf["split"], "combine_ms": tf["combine"]},
         }
         per[fmt] = res
-        print("[bench] %s %s: %.1f GB/s (%.1f%% of peak), step %.3f ms, split %.3f ms (p10 %.3f p90 %.3f), "
-              "combine %.3f ms, append %.3f ms" % (
-                  args.workload, fmt, res["GB_per_s"], res["pct_of_hbm_peak"], ms, t["split"]["mean"],
-                  t["split"]["p10"], t["split"]["p90"], t["combine"]["mean"], t["append"]["mean"]),
+        print("[bench] %s %s: %.1f GB/s (%.1f%% of peak), step %.3f ms = append %.3f + split %.3f (p10 %.3f p90 "
+              "%.3f) + combine %.3f | fused step %.1f GB/s: %.3f ms = split storing the new tokens %.3f + "
+              "combine %.3f" % (
+                  args.workload, fmt, res["GB_per_s"], res["pct_of_hbm_peak"], ms, t["append"]["mean"],
+                  t["split"]["mean"], t["split"]["p10"], t["split"]["p90"], t["combine"]["mean"],
+                  res["fused_step"]["GB_per_s"], ms_f, tf["split"]["mean"], tf["combine"]["mean"]),
               file=sys.stderr, flush=True)
         if primary is None:
             primary = (fmt, s, res)
@@ -442,7 +465,8 @@ def main():
                    "split_workgroups": s.nwg, "cache_flush_between_steps": flush is not None},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(args.workload, fmt),
-                     "kernel": "decode_split_kernel<%s>" % fmt, "kernel_ms": split_ms,
+                     "kernel": "decode_split_kernel<%d, %d, false> (%s)" % (kvq.FORMATS[fmt], c.D, fmt),
+                     "kernel_ms": split_ms,
                      "algorithmic_bytes_per_launch": s.kv_bytes,
                      "measured_streaming_read_GBs": read_gbs, "frac_of_measured_read": achieved / read_gbs,
                      "measured_copy_GBs": copy_gbs},

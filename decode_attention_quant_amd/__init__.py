@@ -25,6 +25,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too sm
 EXPORTS = [
     "kvq_page_bytes", "kvq_quantize_append", "kvq_decode_workspace_size", "kvq_decode_attention",
     "kvq_decode_split", "kvq_decode_combine", "kvq_decode_plan", "kvq_dequant_page", "kvq_status_string",
+    "kvq_decode_step", "kvq_decode_step_split",
 ]
 
 
@@ -58,6 +59,8 @@ def library():
             "kvq_decode_workspace_size": [D, I32, I32, I32, I32, I32, ctypes.POINTER(SZ)],
             "kvq_decode_attention": [D, P, P, I32, I32, I32, P, I32, P, F, P, P, P, SZ, P],
             "kvq_decode_split": [D, P, P, I32, I32, I32, P, I32, P, F, I32, I32, P, P, P, SZ, P],
+            "kvq_decode_step": [D, P, P, P, P, I32, I32, I32, P, I32, P, F, P, P, P, SZ, P],
+            "kvq_decode_step_split": [D, P, P, P, P, I32, I32, I32, P, I32, P, F, I32, I32, P, P, P, SZ, P],
             "kvq_decode_combine": [D, I32, I32, I32, I32, P, I32, I32, P, SZ, P, P, P],
             "kvq_decode_plan": [D, I32, I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)],
             "kvq_dequant_page": [D, P, I64, I32, P, P, P],
@@ -158,6 +161,41 @@ def decode_attention(d, pool, q, block_table, seq_lens, softmax_scale, out=None,
         float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)),
         "kvq_decode_attention")
     return out
+
+
+def decode_step(d, pool, k_new, v_new, q, block_table, seq_lens, softmax_scale, out=None, lse=None, workspace=None,
+                stream=None):
+    """Append k_new, v_new [B][n_q][H_kv][D] (bf16) at positions seq_lens[b] - n_q + i and run decode attention,
+    in one split launch plus the reduce; returns out[B][n_q][H_q][D] fp32."""
+    _need(pool, torch.uint8, "pool")
+    _need(k_new, torch.bfloat16, "k_new")
+    _need(v_new, torch.bfloat16, "v_new")
+    _need(q, torch.bfloat16, "q")
+    _need(block_table, torch.int32, "block_table")
+    _need(seq_lens, torch.int32, "seq_lens")
+    B, n_q, H_q, D = q.shape
+    if tuple(k_new.shape[:2]) != (B, n_q) or k_new.shape != v_new.shape:
+        raise ValueError("k_new and v_new must be [B][n_q][H_kv][D] with q's B and n_q")
+    max_pages = block_table.shape[1]
+    if out is None:
+        out = torch.empty((B, n_q, H_q, D), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(workspace_size(d, B, n_q, H_q, max_pages), q.device)
+    _check(library().kvq_decode_step(
+        ctypes.byref(d), _ptr(pool), _ptr(k_new), _ptr(v_new), _ptr(q), B, n_q, H_q, _ptr(block_table), max_pages,
+        _ptr(seq_lens), float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+        _stream(stream)), "kvq_decode_step")
+    return out
+
+
+def decode_step_split(d, pool, k_new, v_new, q, block_table, seq_lens, softmax_scale, workspace, num_workgroups=0,
+                      flags=0, out=None, lse=None, stream=None):
+    """The fused step's split phase (stores the new tokens, then decodes); finish with decode_combine."""
+    B, n_q, H_q, D = q.shape
+    _check(library().kvq_decode_step_split(
+        ctypes.byref(d), _ptr(pool), _ptr(k_new), _ptr(v_new), _ptr(q), B, n_q, H_q, _ptr(block_table),
+        block_table.shape[1], _ptr(seq_lens), float(softmax_scale), num_workgroups, flags, _ptr(out), _ptr(lse),
+        _ptr(workspace), workspace.numel(), _stream(stream)), "kvq_decode_step_split")
 
 
 def decode_split(d, pool, q, block_table, seq_lens, softmax_scale, workspace, num_workgroups=0, flags=0, out=None,

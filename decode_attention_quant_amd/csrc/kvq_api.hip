@@ -176,7 +176,8 @@ static kvq_status decode_run(const kvq_cache_desc* desc, const void* pool, const
                              int32_t n_q, int32_t H_q, const int32_t* block_table, int32_t max_pages,
                              const int32_t* seq_lens, float softmax_scale, int32_t nwg_req, bool write_direct,
                              bool run_split, bool run_combine, float* out, float* lse, void* workspace,
-                             size_t workspace_bytes, hipStream_t stream) {
+                             size_t workspace_bytes, hipStream_t stream, const void* k_new = nullptr,
+                             const void* v_new = nullptr) {
   kvq_status st = check_decode_shape(desc, batch, n_q, H_q, max_pages);
   if (st != KVQ_OK) return st;
   if (!isfinite(softmax_scale)) return KVQ_ERR_INVALID_ARGUMENT;
@@ -202,6 +203,13 @@ static kvq_status decode_run(const kvq_cache_desc* desc, const void* pool, const
   a.write_direct = write_direct ? 1 : 0;
   a.out = out;
   a.lse = lse;
+  if (k_new != nullptr) {  // fused step
+    a.pool_w = static_cast<uint8_t*>(const_cast<void*>(pool));
+    a.k_new = static_cast<const uint16_t*>(k_new);
+    a.v_new = static_cast<const uint16_t*>(v_new);
+    a.enc_k_scale = desc->k_scale;
+    a.enc_v_scale = desc->v_scale;
+  }
   hipError_t e = hipSuccess;
   if (run_split) e = launch_decode_split(geo, a, stream);
   if (e != hipSuccess) return KVQ_ERR_HIP;
@@ -215,6 +223,44 @@ kvq_status kvq_decode_attention(const kvq_cache_desc* desc, const void* pool, co
                                 float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return decode_run(desc, pool, q_bf16, batch, n_q, num_q_heads, block_table, max_pages_per_seq, seq_lens,
                     softmax_scale, 0, true, true, true, out, lse, workspace, workspace_bytes, stream);
+}
+
+kvq_status kvq_decode_step(const kvq_cache_desc* desc, void* pool, const void* k_new_bf16, const void* v_new_bf16,
+                           const void* q_bf16, int32_t batch, int32_t n_q, int32_t num_q_heads,
+                           const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* seq_lens,
+                           float softmax_scale, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  kvq_status st = check_decode_shape(desc, batch, n_q, num_q_heads, max_pages_per_seq);
+  if (st != KVQ_OK) return st;
+  // one row tile: the workgroup that owns a block is its only reader
+  if ((num_q_heads / desc->num_kv_heads) * n_q > 16) return KVQ_ERR_UNSUPPORTED;
+  if (batch > 0) {
+    if (k_new_bf16 == nullptr || v_new_bf16 == nullptr) return KVQ_ERR_INVALID_ARGUMENT;
+    if (!aligned(k_new_bf16, 16) || !aligned(v_new_bf16, 16)) return KVQ_ERR_INVALID_ARGUMENT;
+  }
+  return decode_run(desc, pool, q_bf16, batch, n_q, num_q_heads, block_table, max_pages_per_seq, seq_lens,
+                    softmax_scale, 0, true, true, true, out, lse, workspace, workspace_bytes, stream, k_new_bf16,
+                    v_new_bf16);
+}
+
+kvq_status kvq_decode_step_split(const kvq_cache_desc* desc, void* pool, const void* k_new_bf16,
+                                 const void* v_new_bf16, const void* q_bf16, int32_t batch, int32_t n_q,
+                                 int32_t num_q_heads, const int32_t* block_table, int32_t max_pages_per_seq,
+                                 const int32_t* seq_lens, float softmax_scale, int32_t num_workgroups,
+                                 int32_t flags, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  if ((flags & ~KVQ_SPLIT_WRITE_WHOLE_UNITS) != 0) return KVQ_ERR_INVALID_ARGUMENT;
+  kvq_status st = check_decode_shape(desc, batch, n_q, num_q_heads, max_pages_per_seq);
+  if (st != KVQ_OK) return st;
+  if ((num_q_heads / desc->num_kv_heads) * n_q > 16) return KVQ_ERR_UNSUPPORTED;
+  if (batch > 0) {
+    if (k_new_bf16 == nullptr || v_new_bf16 == nullptr) return KVQ_ERR_INVALID_ARGUMENT;
+    if (!aligned(k_new_bf16, 16) || !aligned(v_new_bf16, 16)) return KVQ_ERR_INVALID_ARGUMENT;
+  }
+  const bool whole = (flags & KVQ_SPLIT_WRITE_WHOLE_UNITS) != 0;
+  return decode_run(desc, pool, q_bf16, batch, n_q, num_q_heads, block_table, max_pages_per_seq, seq_lens,
+                    softmax_scale, num_workgroups, whole, true, false, whole ? out : nullptr, whole ? lse : nullptr,
+                    workspace, workspace_bytes, stream, k_new_bf16, v_new_bf16);
 }
 
 kvq_status kvq_decode_split(const kvq_cache_desc* desc, const void* pool, const void* q_bf16, int32_t batch,

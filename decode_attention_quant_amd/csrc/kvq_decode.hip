@@ -37,6 +37,7 @@
 #include <type_traits>
 
 #include "kvq_device.hpp"
+#include "kvq_encode.hpp"
 #include "kvq_internal.hpp"
 
 namespace kvq {
@@ -629,6 +630,42 @@ __device__ __forceinline__ void clear_tail(Buf<FMT, D>& buf, int nvalid, int g) 
   }
 }
 
+// ----------------------------------------------------------- fused append
+
+// Encode and store the new tokens of sequence b, kv head h at positions
+// [plo, phi) (all inside this workgroup's blocks): wave 0 the K rows (a
+// quad per token), wave 1 the V rows (a row of 16 lanes per 4 tokens), with
+// the write path's own encoders, so the bytes are those quantize-append
+// stores.  Input token i of sequence b is row b * n_q + i of k_new / v_new.
+template <int FMT, int D>
+__device__ __forceinline__ void append_new_tokens(const DecodeArgs& a, const Geometry& geo, int b, int h, int L,
+                                               int plo, int phi, int wave, int lane) {
+  const int pnew = L - a.n_q;          // position of new token 0
+  const int64_t tok0 = (int64_t)b * a.n_q;
+  const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
+  auto slot_of = [&](int64_t tok) -> int {
+    const int p = pnew + (int)(tok - tok0);
+    return p >= 0 ? bt[p / geo.P] * geo.P + p % geo.P : -1;
+  };
+  const int ilo = plo - pnew, ihi = phi - pnew;  // new-token indexes written here
+  if (wave == 0) {
+    const int q = lane & 3;
+    for (int i0 = ilo; i0 < ihi; i0 += 16) {
+      const int i = i0 + (lane >> 2);  // a whole quad shares it
+      if (i < ihi) {
+        const int64_t tok = tok0 + i;
+        uint32_t raw[D / 8];
+        enc::load_k_row<D>(raw, a.k_new + (tok * geo.H_kv + h) * D + q * (D / 4));
+        enc::encode_k_row<FMT, D>(a.pool_w, raw, slot_of(tok), geo, h, a.enc_k_scale, q);
+      }
+    }
+  } else if (wave == 1) {
+    for (int i0 = ilo; i0 < ihi; i0 += 16)
+      enc::v_row_group<FMT, D>(a.pool_w, a.v_new, slot_of, geo, a.enc_v_scale, h, lane & 15,
+                               tok0 + i0 + 4 * (lane >> 4), tok0 + ilo, tok0 + ihi);
+  }
+}
+
 // ----------------------------------------------------------- the kernel
 
 // Blocks per split workgroup: an equal share of the T blocks, but at least
@@ -658,7 +695,9 @@ __host__ __device__ constexpr size_t split_lds_bytes(int B, int R) {
          (merge > ring ? merge : ring);
 }
 
-template <int FMT, int D>
+// FUSED: also store the new tokens first (DecodeArgs::pool_w); a separate
+// instantiation, so the encoders' registers never weigh on the plain kernel.
+template <int FMT, int D, bool FUSED>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, DecodeArgs a) {
   using T = DT<FMT, D>;
   constexpr float NEG_INF = -__builtin_inff();
@@ -743,6 +782,24 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
     const int nblk = __builtin_amdgcn_readfirstlane(seg_end - x);
     const bool whole = blk0 == 0 && nblk == nb;
     const int u = b * geo.H_kv + h;
+
+    // ---- fused step: store the new tokens that fall in this segment's
+    //      blocks before any of those blocks is staged.  No other workgroup
+    //      reads them (one row tile), and this one reads them through the
+    //      same L2, so it is enough that its stores and atomics have
+    //      completed (vmcnt 0) before the barrier: a workgroup-scope fence,
+    //      not a device-wide L2 write-back.  The atomics of 4-bit V codes
+    //      touch only cache lines of this block's own code plane.
+    if constexpr (FUSED) {
+      const int plo = max(max(L - a.n_q, 0), 16 * blk0), phi = min(L, 16 * (blk0 + nblk));
+      if (plo < phi) {
+        append_new_tokens<FMT, D>(a, geo, b, h, L, plo, phi, wave, lane);
+        wait_vmcnt<0>();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      }
+    }
 
     // ---- query rows of this tile: row r (= c16 in S layout) -> (i, head)
     const int r = c16;
@@ -1145,7 +1202,7 @@ hipError_t decode_split_occupancy(const Geometry& geo, int B, int R, int* blocks
   const size_t lds = decode_split_lds_bytes(geo, B, R);
 #define KVQ_OCC_CASE(F, DD)                                                                        \
   if (geo.fmt == F && geo.D == DD)                                                                 \
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, decode_split_kernel<F, DD>, \
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, decode_split_kernel<F, DD, false>, \
                                                         256, lds);
   KVQ_FOR_EACH_DECODE(KVQ_OCC_CASE)
 #undef KVQ_OCC_CASE
@@ -1155,10 +1212,13 @@ hipError_t decode_split_occupancy(const Geometry& geo, int B, int R, int* blocks
 hipError_t launch_decode_split(const Geometry& geo, const DecodeArgs& a, hipStream_t stream) {
   const int tiles = (a.R + 15) / 16;
   const size_t lds = decode_split_lds_bytes(geo, a.B, a.R);
-#define KVQ_SPLIT_CASE(F, DD)                                                                    \
-  if (geo.fmt == F && geo.D == DD) {                                                             \
-    hipLaunchKernelGGL((decode_split_kernel<F, DD>), dim3(a.nwg, tiles), dim3(256), lds, stream, geo, a); \
-    return hipGetLastError();                                                                    \
+#define KVQ_SPLIT_CASE(F, DD)                                                                                 \
+  if (geo.fmt == F && geo.D == DD) {                                                                          \
+    if (a.pool_w != nullptr)                                                                                  \
+      hipLaunchKernelGGL((decode_split_kernel<F, DD, true>), dim3(a.nwg, tiles), dim3(256), lds, stream, geo, a); \
+    else                                                                                                      \
+      hipLaunchKernelGGL((decode_split_kernel<F, DD, false>), dim3(a.nwg, tiles), dim3(256), lds, stream, geo, a); \
+    return hipGetLastError();                                                                                 \
   }
   KVQ_FOR_EACH_DECODE(KVQ_SPLIT_CASE)
 #undef KVQ_SPLIT_CASE

@@ -33,6 +33,14 @@ struct DecodeArgs {
   float* out;                 // [B][n_q][H_q][D]
   float* lse;                 // [B][n_q][H_q], nullable
   int32_t write_direct;       // 1: finish units held by one workgroup in the split kernel
+  // Fused decode step (pool_w non-null): before reading a block, the split
+  // workgroup that owns it encodes and stores the new tokens in it, the n_q
+  // newest positions L_b - n_q .. L_b - 1 of each sequence, whose slots come
+  // from the block table.  Needs R <= 16 (one row tile per block).
+  uint8_t* pool_w;            // the pool, written (the same memory as pool)
+  const uint16_t* k_new;      // [B][n_q][H_kv][D] bf16
+  const uint16_t* v_new;      // [B][n_q][H_kv][D] bf16
+  float enc_k_scale, enc_v_scale;  // per-tensor encoding scales (FP8_TENSOR)
 };
 
 // LDS bytes of the split kernel for a batch of B sequences and R rows.

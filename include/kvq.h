@@ -155,6 +155,29 @@ kvq_status kvq_decode_attention(const kvq_cache_desc* desc, const void* pool,
                                 float softmax_scale, float* out, float* lse,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* One decode step with the append fused in (the decode-step variant of the
+ * write path followed by attention; NInfer guide: every generated token
+ * enters the cache through its codec and then attends over the whole
+ * cache).  Equal to kvq_quantize_append of the n_q newest tokens of every
+ * sequence followed by kvq_decode_attention, in one launch plus the
+ * cross-split reduce: the split workgroup that owns a block stores the new
+ * tokens that fall in it before reading it.
+ *  pool          device, written (the new tokens' bytes) and read.
+ *  k_new_bf16, v_new_bf16  device bf16 [batch][n_q][num_kv_heads][head_dim]:
+ *                token i of sequence b is stored at position
+ *                seq_lens[b] - n_q + i (skipped if negative), in the slot
+ *                block_table[b][pos / page_size] * page_size + pos % page_size.
+ *  The other arguments are those of kvq_decode_attention (seq_lens include
+ *  the new tokens; the same workspace size).  Needs
+ *  (num_q_heads / num_kv_heads) * n_q <= 16, else KVQ_ERR_UNSUPPORTED (call
+ *  the two entry points instead).  The pool bytes and the results equal
+ *  those of the two separate calls. */
+kvq_status kvq_decode_step(const kvq_cache_desc* desc, void* pool, const void* k_new_bf16,
+                           const void* v_new_bf16, const void* q_bf16, int32_t batch, int32_t n_q,
+                           int32_t num_q_heads, const int32_t* block_table, int32_t max_pages_per_seq,
+                           const int32_t* seq_lens, float softmax_scale, float* out, float* lse,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* The two phases of kvq_decode_attention, for callers that merge partial
  * results themselves (e.g. several devices each holding a range of a long
  * sequence's pages) or time them apart.
@@ -193,6 +216,17 @@ kvq_status kvq_decode_combine(const kvq_cache_desc* desc, int32_t batch, int32_t
                               const int32_t* seq_lens, int32_t num_workgroups, int32_t flags,
                               const void* workspace, size_t workspace_bytes,
                               float* out, float* lse, hipStream_t stream);
+
+/* The fused step's first phase: kvq_decode_split that also stores the new
+ * tokens, as kvq_decode_step does (same arguments as kvq_decode_step, plus
+ * num_workgroups and flags as in kvq_decode_split); finish with
+ * kvq_decode_combine.  For callers that time or schedule the phases apart. */
+kvq_status kvq_decode_step_split(const kvq_cache_desc* desc, void* pool, const void* k_new_bf16,
+                                 const void* v_new_bf16, const void* q_bf16, int32_t batch, int32_t n_q,
+                                 int32_t num_q_heads, const int32_t* block_table,
+                                 int32_t max_pages_per_seq, const int32_t* seq_lens, float softmax_scale,
+                                 int32_t num_workgroups, int32_t flags, float* out, float* lse,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* The plan kvq_decode_attention uses for this problem on the current device:
  * split workgroups and partial slots. */

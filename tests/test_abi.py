@@ -180,3 +180,23 @@ def test_probe_rejects_bad_arguments_on_the_host():
     assert lib.kvq_probe_copy(None, fake, 32, None) == 1
     assert lib.kvq_probe_read(fake, 0, fake, None) == 0             # empty: nothing to do
     assert lib.kvq_probe_copy(fake, fake, 0, None) == 0
+
+
+def test_decode_step_validation_enqueues_nothing():
+    """The fused step's own checks come before any HIP call."""
+    d = kvq.desc(3, 256, 64, 4, 100)
+    P = ctypes.c_void_p
+    ok = P(0x100000)
+    lib = kvq.library()
+
+    def call(k=ok, v=ok, B=2, nq=1, Hq=24, pool=ok):
+        return lib.kvq_decode_step(ctypes.byref(d), pool, k, v, ok, B, nq, Hq, ok, 10, ok, 0.0625, ok, None, ok,
+                                   1 << 30, None)
+
+    assert call(B=0) == 0                   # empty batch: nothing to do
+    assert call(k=None) == 1
+    assert call(v=None) == 1
+    assert call(k=P(0x100008)) == 1         # 16-byte alignment of the new rows
+    assert call(nq=3) == 2                  # G * n_q = 18 rows: more than one row tile
+    assert call(Hq=22) == 1                 # not a multiple of H_kv
+    assert call(pool=None, nq=1) == 1
