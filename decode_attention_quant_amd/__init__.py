@@ -25,7 +25,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too sm
 EXPORTS = [
     "kvq_page_bytes", "kvq_quantize_append", "kvq_decode_workspace_size", "kvq_decode_attention",
     "kvq_decode_split", "kvq_decode_combine", "kvq_decode_plan", "kvq_dequant_page", "kvq_status_string",
-    "kvq_decode_step", "kvq_decode_step_split",
+    "kvq_decode_step", "kvq_decode_step_split", "kvq_prefill_attention",
 ]
 
 
@@ -61,6 +61,7 @@ def library():
             "kvq_decode_split": [D, P, P, I32, I32, I32, P, I32, P, F, I32, I32, P, P, P, SZ, P],
             "kvq_decode_step": [D, P, P, P, P, I32, I32, I32, P, I32, P, F, P, P, P, SZ, P],
             "kvq_decode_step_split": [D, P, P, P, P, I32, I32, I32, P, I32, P, F, I32, I32, P, P, P, SZ, P],
+            "kvq_prefill_attention": [D, P, P, I32, I32, I32, P, I32, P, F, P, P, P],
             "kvq_decode_combine": [D, I32, I32, I32, I32, P, I32, I32, P, SZ, P, P, P],
             "kvq_decode_plan": [D, I32, I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)],
             "kvq_dequant_page": [D, P, I64, I32, P, P, P],
@@ -196,6 +197,22 @@ def decode_step_split(d, pool, k_new, v_new, q, block_table, seq_lens, softmax_s
         ctypes.byref(d), _ptr(pool), _ptr(k_new), _ptr(v_new), _ptr(q), B, n_q, H_q, _ptr(block_table),
         block_table.shape[1], _ptr(seq_lens), float(softmax_scale), num_workgroups, flags, _ptr(out), _ptr(lse),
         _ptr(workspace), workspace.numel(), _stream(stream)), "kvq_decode_step_split")
+
+
+def prefill_attention(d, pool, q, block_table, seq_lens, softmax_scale, out=None, lse=None, stream=None):
+    """Causal attention of a prefill chunk's queries q[B][n_q][H_q][D] (positions seq_lens[b] - n_q + i, already
+    appended) over the cache; returns out[B][n_q][H_q][D] fp32."""
+    _need(pool, torch.uint8, "pool")
+    _need(q, torch.bfloat16, "q")
+    _need(block_table, torch.int32, "block_table")
+    _need(seq_lens, torch.int32, "seq_lens")
+    B, n_q, H_q, D = q.shape
+    if out is None:
+        out = torch.empty((B, n_q, H_q, D), dtype=torch.float32, device=q.device)
+    _check(library().kvq_prefill_attention(
+        ctypes.byref(d), _ptr(pool), _ptr(q), B, n_q, H_q, _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
+        float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream)), "kvq_prefill_attention")
+    return out
 
 
 def decode_split(d, pool, q, block_table, seq_lens, softmax_scale, workspace, num_workgroups=0, flags=0, out=None,

@@ -285,6 +285,38 @@ kvq_status kvq_decode_combine(const kvq_cache_desc* desc, int32_t batch, int32_t
                     const_cast<void*>(workspace), workspace_bytes, stream);
 }
 
+kvq_status kvq_prefill_attention(const kvq_cache_desc* desc, const void* pool, const void* q_bf16, int32_t batch,
+                                 int32_t n_q, int32_t num_q_heads, const int32_t* block_table,
+                                 int32_t max_pages_per_seq, const int32_t* seq_lens, float softmax_scale, float* out,
+                                 float* lse, hipStream_t stream) {
+  kvq_status st = check_desc(desc);
+  if (st != KVQ_OK) return st;
+  if (batch < 0 || n_q < 1 || num_q_heads < 1 || max_pages_per_seq < 1) return KVQ_ERR_INVALID_ARGUMENT;
+  if (num_q_heads % desc->num_kv_heads != 0) return KVQ_ERR_INVALID_ARGUMENT;
+  if (!isfinite(softmax_scale)) return KVQ_ERR_INVALID_ARGUMENT;
+  const int64_t G = num_q_heads / desc->num_kv_heads;
+  const int64_t R = G * n_q;
+  const int64_t work = (int64_t)batch * desc->num_kv_heads * ((R + 63) / 64);
+  if (R > INT32_MAX / 2 || work > (int64_t)1 << 30) return KVQ_ERR_UNSUPPORTED;
+  if ((int64_t)max_pages_per_seq * desc->page_size >= ((int64_t)1 << 31) / 16) return KVQ_ERR_UNSUPPORTED;
+  if (batch == 0) return KVQ_OK;
+  if (pool == nullptr || q_bf16 == nullptr || block_table == nullptr || seq_lens == nullptr || out == nullptr)
+    return KVQ_ERR_INVALID_ARGUMENT;
+  if (!aligned(pool, 128) || !aligned(q_bf16, 16) || !aligned(out, 16)) return KVQ_ERR_INVALID_ARGUMENT;
+  DecodeArgs a{};
+  a.pool = static_cast<const uint8_t*>(pool);
+  a.q = static_cast<const uint16_t*>(q_bf16);
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.B = batch; a.n_q = n_q; a.H_q = num_q_heads; a.G = (int32_t)G; a.R = (int32_t)R;
+  a.max_pages = max_pages_per_seq;
+  a.qk_scale = softmax_scale * 1.4426950408889634f * (desc->format == F_FP8_TENSOR ? desc->k_scale : 1.0f);
+  a.v_out_scale = desc->format == F_FP8_TENSOR ? desc->v_scale : 1.0f;
+  a.out = out;
+  a.lse = lse;
+  return hip_status(launch_prefill(geo_of(desc), a, stream));
+}
+
 kvq_status kvq_dequant_page(const kvq_cache_desc* desc, const void* pool, int64_t page, int32_t flags, float* k_out,
                             float* v_out, hipStream_t stream) {
   kvq_status st = check_desc(desc);

@@ -34,601 +34,10 @@
 //   output instead.
 #include <hip/hip_runtime.h>
 
-#include <type_traits>
-
-#include "kvq_device.hpp"
+#include "kvq_decode_core.hpp"
 #include "kvq_encode.hpp"
-#include "kvq_internal.hpp"
 
 namespace kvq {
-
-template <int FMT, int D>
-struct DT {
-  static constexpr int KC = k_codec(FMT), VC = v_codec(FMT);
-  static constexpr int KBITS = codec_bits(KC), VBITS = codec_bits(VC);
-  static constexpr bool QI8 = KC == C_I8G64;    // Q.K on the int8 matrix cores, q in two int8 pieces
-  static constexpr bool QF16 = KC == C_E2G16;   // Q.K in f16, q split into f16 hi + lo
-  static constexpr bool QROT = k_rotated(FMT);  // q is rotated first (K was)
-  static constexpr bool VROT = v_rotated(FMT);
-  static constexpr int KSTEPS = D / 32;
-  static constexpr int QSTEPS = QI8 ? D / 64 : D / 32;  // MFMA k-steps of Q.K
-  static constexpr int QPIECES = (QI8 || QF16) ? 2 : 1;
-  // Bytes of one 16-token block in each plane, and their place in an LDS
-  // stage (the four plane regions back to back).
-  static constexpr int KB = code_block_bytes(KC, D), KSB = scale_block_bytes(KC, D);
-  static constexpr int VB = code_block_bytes(VC, D), VSB = scale_block_bytes(VC, D);
-  static constexpr int SK = 0, SKS = KB, SV = KB + KSB, SVS = KB + KSB + VB;
-  static constexpr int STAGE = KB + KSB + VB + VSB;
-  // Direct global->LDS loads (16 bytes per lane) that copy one block.
-  static constexpr int NDMA = (KB + 1023) / 1024 + (KSB + 1023) / 1024 + (VB + 1023) / 1024 + (VSB + 1023) / 1024;
-  // Blocks are staged through a per-wave ring of RING_S blocks in LDS,
-  // RING_S - 1 of them in flight while one is consumed, where that fits in
-  // RING_LDS bytes per workgroup (two workgroups per CU).  INT8-G64 keeps
-  // its register pipeline: with q in two int8 pieces its loop is shorter
-  // than the ring's extra LDS reads and waits cost (measured).
-  static constexpr int RING_LDS = 72 * 1024;
-  static constexpr int RING_FIT = RING_LDS / (4 * STAGE);
-  static constexpr int RING_S = RING_FIT > 4 ? 4 : RING_FIT;
-  static constexpr bool RING = RING_S >= 2 && FMT != F_INT8_G64;
-  // Without the ring: Q operands in LDS (one ds_read_b128 per k-step) where
-  // registers would otherwise spill.
-  static constexpr bool QLDS = !RING;
-  // Without the ring: prefetch whole blocks into a second register buffer
-  // where it fits next to the O accumulators; otherwise reuse one buffer,
-  // loading the next block's K as soon as Q.K is done and its V as soon as
-  // P.V is done.
-  static constexpr bool DOUBLE_BUF = D == 128 || FMT == F_FP8_ROW || FMT == F_FP8_TENSOR;
-  static constexpr int NT = D / 16;
-  static constexpr int KCH = D * KBITS / 512;                       // 16-B K chunks per lane per block
-  static constexpr int VCH = VBITS * NT / 32;                       // 16-B V chunks per lane per block
-  static constexpr int KSW = KC == C_E4ROW ? 2 : KC == C_I8G64 ? 8 : KC == C_E4MX ? D / 32 : KC == C_E2G16 ? 4 : 0;
-  static constexpr int VSW = VC == C_E4ROW ? 2 : VC == C_I8G64 ? 8 : VC == C_E4MX ? D / 32 : VC == C_E2G16 ? 16 : 0;
-  static constexpr int G = n_groups(KC, D) > 0 ? n_groups(KC, D) : 1;
-};
-
-// Tables the kernel only reads (page table, sequence lengths) are read
-// through the constant address space, so uniform indexes become scalar
-// loads: a vector load here would be counted by vmcnt, and waiting for it
-// would also wait for every block prefetch issued before it.
-typedef const __attribute__((address_space(4))) int32_t cint32;
-__device__ __forceinline__ const cint32* as_const(const int32_t* p) { return (const cint32*)p; }
-
-template <int FMT, int D>
-struct Buf {
-  uint4 k[DT<FMT, D>::KCH];
-  uint4 v[DT<FMT, D>::VCH];
-  uint32_t ks[DT<FMT, D>::KSW > 0 ? DT<FMT, D>::KSW : 1];
-  uint32_t vs[DT<FMT, D>::VSW > 0 ? DT<FMT, D>::VSW : 1];
-};
-
-template <int N>
-__device__ __forceinline__ void load_words(uint32_t (&w)[N], const uint8_t* p) {
-  if constexpr (N == 2) {
-    const uint2 x = *reinterpret_cast<const uint2*>(p);
-    w[0] = x.x; w[1] = x.y;
-  } else {
-    static_assert(N % 4 == 0, "");
-#pragma unroll
-    for (int i = 0; i < N / 4; ++i) {
-      const uint4 x = *reinterpret_cast<const uint4*>(p + 16 * i);
-      w[4 * i] = x.x; w[4 * i + 1] = x.y; w[4 * i + 2] = x.z; w[4 * i + 3] = x.w;
-    }
-  }
-}
-
-// Addresses of token block j (absolute block index within the unit).
-struct BlockAddr {
-  const uint8_t* hb;  // head block of the page holding block j
-  int bip;            // block index inside the page
-};
-__device__ __forceinline__ BlockAddr block_addr(const uint8_t* head0, const Geometry& geo, const cint32* bt_row,
-                                                int j) {
-  const int bpp_log2 = geo.P == 128 ? 3 : 2;  // 16-token blocks per page: 8 or 4
-  const int page = __builtin_amdgcn_readfirstlane(j >> bpp_log2);
-  BlockAddr r;
-  r.bip = j & ((1 << bpp_log2) - 1);
-  r.hb = head0 + (int64_t)bt_row[page] * geo.page_bytes;
-  return r;
-}
-
-// Load the K codes (and K scales) of token block j into registers.
-template <int FMT, int D>
-__device__ __forceinline__ void load_k(Buf<FMT, D>& buf, const uint8_t* head0, const Geometry& geo,
-                                       const cint32* bt_row, int j, int lane) {
-  using T = DT<FMT, D>;
-  const BlockAddr ba = block_addr(head0, geo, bt_row, j);
-  const int g = lane >> 4, c16 = lane & 15;
-  const uint8_t* kc = ba.hb + geo.off_kc + (int64_t)ba.bip * geo.kcode_blk;
-#pragma unroll
-  for (int i = 0; i < T::KCH; ++i) buf.k[i] = *reinterpret_cast<const uint4*>(kc + i * 1024 + lane * 16);
-  if constexpr (T::KSW > 0) {
-    const uint8_t* ks = ba.hb + geo.off_ks + (int64_t)ba.bip * geo.kscale_blk;
-    const int off = T::KC == C_E2G16 ? c16 * 16 : g * (4 * T::KSW);
-    load_words(buf.ks, ks + off);
-  }
-}
-
-// Load the V codes (and V scales) of token block j into registers.
-template <int FMT, int D>
-__device__ __forceinline__ void load_v(Buf<FMT, D>& buf, const uint8_t* head0, const Geometry& geo,
-                                       const cint32* bt_row, int j, int lane) {
-  using T = DT<FMT, D>;
-  const BlockAddr ba = block_addr(head0, geo, bt_row, j);
-  const int g = lane >> 4;
-  const uint8_t* vc = ba.hb + geo.off_vc + (int64_t)ba.bip * geo.vcode_blk;
-#pragma unroll
-  for (int q = 0; q < T::VCH; ++q) buf.v[q] = *reinterpret_cast<const uint4*>(vc + q * 1024 + lane * 16);
-  if constexpr (T::VSW > 0) {
-    const uint8_t* vs = ba.hb + geo.off_vs + (int64_t)ba.bip * geo.vscale_blk;
-    load_words(buf.vs, vs + g * (4 * T::VSW));
-  }
-}
-
-template <int FMT, int D>
-__device__ __forceinline__ void load_block(Buf<FMT, D>& buf, const uint8_t* head0, const Geometry& geo,
-                                           const cint32* bt_row, int j, int lane) {
-  load_k<FMT, D>(buf, head0, geo, bt_row, j, lane);
-  load_v<FMT, D>(buf, head0, geo, bt_row, j, lane);
-}
-
-// ----------------------------------------------------------- LDS ring
-// A wave copies each 16-token block into a stage of its own LDS ring with
-// direct global->LDS loads (global_load_lds_dwordx4: lane l's 16 bytes land
-// at the stage address + 16 l), which hold no registers while in flight.
-// Completion is tracked with explicit vmcnt waits: inside the block loop
-// these copies are the only vector-memory instructions, and they complete in
-// order.  Stages are read back with ds_read_b128 in inline asm that waits for
-// its own results, so the compiler's conservative wait for every
-// outstanding copy before an LDS read never enters the loop.
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef const __attribute__((address_space(1))) void gbl_void_t;
-
-template <int BYTES>
-__device__ __forceinline__ void copy_plane(uint32_t dst, const uint8_t* src, int lane) {
-#pragma unroll
-  for (int c = 0; c < BYTES / 1024; ++c)
-    __builtin_amdgcn_global_load_lds((gbl_void_t*)(src + c * 1024 + lane * 16),
-                                     (lds_void_t*)(uintptr_t)(dst + c * 1024), 16, 0, 0);
-  constexpr int REM = BYTES % 1024;
-  if constexpr (REM > 0) {
-    if (lane < REM / 16)
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)(src + (BYTES / 1024) * 1024 + lane * 16),
-                                       (lds_void_t*)(uintptr_t)(dst + (BYTES / 1024) * 1024), 16, 0, 0);
-  }
-}
-
-// Start copying token block j into the stage at LDS byte address `stage`.
-template <int FMT, int D>
-__device__ __forceinline__ void stage_block(uint32_t stage, const uint8_t* head0, const Geometry& geo,
-                                            const cint32* bt_row, int j, int lane) {
-  using T = DT<FMT, D>;
-  const BlockAddr ba = block_addr(head0, geo, bt_row, j);
-  copy_plane<T::KB>(stage + T::SK, ba.hb + geo.off_kc + (int64_t)ba.bip * T::KB, lane);
-  if constexpr (T::KSB > 0) copy_plane<T::KSB>(stage + T::SKS, ba.hb + geo.off_ks + (int64_t)ba.bip * T::KSB, lane);
-  copy_plane<T::VB>(stage + T::SV, ba.hb + geo.off_vc + (int64_t)ba.bip * T::VB, lane);
-  if constexpr (T::VSB > 0) copy_plane<T::VSB>(stage + T::SVS, ba.hb + geo.off_vs + (int64_t)ba.bip * T::VSB, lane);
-}
-
-// s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt fields at "no wait").
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// Wait until every copy of a block is done when `after` blocks (wave-
-// uniform, < S) were staged behind it.
-template <int NDMA, int S>
-__device__ __forceinline__ void wait_staged(int after) {
-  if constexpr (S > 3) {
-    if (after >= 3) { wait_vmcnt<3 * NDMA>(); return; }
-  }
-  if constexpr (S > 2) {
-    if (after >= 2) { wait_vmcnt<2 * NDMA>(); return; }
-  }
-  if (after >= 1) { wait_vmcnt<NDMA>(); return; }
-  wait_vmcnt<0>();
-}
-
-// NC 16-byte code chunks at c + i * CS (i < NC) and SW scale words at s
-// (consecutive), read from LDS in one asm block that waits for them.
-template <int NC, int CS, int SW>
-__device__ __forceinline__ void lds_read_part(uint4 (&c)[NC], uint32_t (&w)[SW > 0 ? SW : 1], uint32_t ca,
-                                              uint32_t sa) {
-  static_assert(NC == 2 || NC == 4, "");
-  static_assert(SW == 0 || SW == 2 || SW == 4 || SW == 8 || SW == 16, "");
-#define KVQ_R(o, a, off) "ds_read_b128 %" #o ", %" #a " offset:%" #off "\n\t"
-#define KVQ_W "s_waitcnt lgkmcnt(0)"
-  if constexpr (NC == 2) {
-    if constexpr (SW == 0) {
-      asm volatile(KVQ_R(0, 2, 3) KVQ_R(1, 2, 4) KVQ_W
-                   : "=&v"(c[0]), "=&v"(c[1]) : "v"(ca), "i"(0), "i"(CS) : "memory");
-    } else if constexpr (SW == 2) {
-      uint2 s0;
-      asm volatile(KVQ_R(0, 3, 5) KVQ_R(1, 3, 6) "ds_read_b64 %2, %4\n\t" KVQ_W
-                   : "=&v"(c[0]), "=&v"(c[1]), "=&v"(s0) : "v"(ca), "v"(sa), "i"(0), "i"(CS) : "memory");
-      w[0] = s0.x; w[1] = s0.y;
-    } else if constexpr (SW == 4) {
-      uint4 s0;
-      asm volatile(KVQ_R(0, 3, 5) KVQ_R(1, 3, 6) KVQ_R(2, 4, 5) KVQ_W
-                   : "=&v"(c[0]), "=&v"(c[1]), "=&v"(s0) : "v"(ca), "v"(sa), "i"(0), "i"(CS) : "memory");
-      w[0] = s0.x; w[1] = s0.y; w[2] = s0.z; w[3] = s0.w;
-    } else if constexpr (SW == 8) {
-      uint4 s0, s1;
-      asm volatile(KVQ_R(0, 4, 6) KVQ_R(1, 4, 7) KVQ_R(2, 5, 6) KVQ_R(3, 5, 8) KVQ_W
-                   : "=&v"(c[0]), "=&v"(c[1]), "=&v"(s0), "=&v"(s1) : "v"(ca), "v"(sa), "i"(0), "i"(CS), "i"(16)
-                   : "memory");
-      w[0] = s0.x; w[1] = s0.y; w[2] = s0.z; w[3] = s0.w; w[4] = s1.x; w[5] = s1.y; w[6] = s1.z; w[7] = s1.w;
-    } else {
-      uint4 s0, s1, s2, s3;
-      asm volatile(KVQ_R(0, 6, 8) KVQ_R(1, 6, 9) KVQ_R(2, 7, 8) KVQ_R(3, 7, 10) KVQ_R(4, 7, 11) KVQ_R(5, 7, 12) KVQ_W
-                   : "=&v"(c[0]), "=&v"(c[1]), "=&v"(s0), "=&v"(s1), "=&v"(s2), "=&v"(s3)
-                   : "v"(ca), "v"(sa), "i"(0), "i"(CS), "i"(16), "i"(32), "i"(48) : "memory");
-      const uint4 ss[4] = {s0, s1, s2, s3};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) { w[4 * i] = ss[i].x; w[4 * i + 1] = ss[i].y; w[4 * i + 2] = ss[i].z; w[4 * i + 3] = ss[i].w; }
-    }
-  } else {
-    if constexpr (SW == 0) {
-      asm volatile(KVQ_R(0, 4, 5) KVQ_R(1, 4, 6) KVQ_R(2, 4, 7) KVQ_R(3, 4, 8) KVQ_W
-                   : "=&v"(c[0]), "=&v"(c[1]), "=&v"(c[2]), "=&v"(c[3])
-                   : "v"(ca), "i"(0), "i"(CS), "i"(2 * CS), "i"(3 * CS) : "memory");
-    } else if constexpr (SW == 2) {
-      uint2 s0;
-      asm volatile(KVQ_R(0, 5, 7) KVQ_R(1, 5, 8) KVQ_R(2, 5, 9) KVQ_R(3, 5, 10) "ds_read_b64 %4, %6\n\t" KVQ_W
-                   : "=&v"(c[0]), "=&v"(c[1]), "=&v"(c[2]), "=&v"(c[3]), "=&v"(s0)
-                   : "v"(ca), "v"(sa), "i"(0), "i"(CS), "i"(2 * CS), "i"(3 * CS) : "memory");
-      w[0] = s0.x; w[1] = s0.y;
-    } else if constexpr (SW == 4) {
-      uint4 s0;
-      asm volatile(KVQ_R(0, 5, 7) KVQ_R(1, 5, 8) KVQ_R(2, 5, 9) KVQ_R(3, 5, 10) KVQ_R(4, 6, 7) KVQ_W
-                   : "=&v"(c[0]), "=&v"(c[1]), "=&v"(c[2]), "=&v"(c[3]), "=&v"(s0)
-                   : "v"(ca), "v"(sa), "i"(0), "i"(CS), "i"(2 * CS), "i"(3 * CS) : "memory");
-      w[0] = s0.x; w[1] = s0.y; w[2] = s0.z; w[3] = s0.w;
-    } else if constexpr (SW == 8) {
-      uint4 s0, s1;
-      asm volatile(KVQ_R(0, 6, 8) KVQ_R(1, 6, 9) KVQ_R(2, 6, 10) KVQ_R(3, 6, 11) KVQ_R(4, 7, 8) KVQ_R(5, 7, 12) KVQ_W
-                   : "=&v"(c[0]), "=&v"(c[1]), "=&v"(c[2]), "=&v"(c[3]), "=&v"(s0), "=&v"(s1)
-                   : "v"(ca), "v"(sa), "i"(0), "i"(CS), "i"(2 * CS), "i"(3 * CS), "i"(16) : "memory");
-      w[0] = s0.x; w[1] = s0.y; w[2] = s0.z; w[3] = s0.w; w[4] = s1.x; w[5] = s1.y; w[6] = s1.z; w[7] = s1.w;
-    } else {
-      uint4 s0, s1, s2, s3;
-      asm volatile(KVQ_R(0, 8, 10) KVQ_R(1, 8, 11) KVQ_R(2, 8, 12) KVQ_R(3, 8, 13)
-                   KVQ_R(4, 9, 10) KVQ_R(5, 9, 14) KVQ_R(6, 9, 15) KVQ_R(7, 9, 16) KVQ_W
-                   : "=&v"(c[0]), "=&v"(c[1]), "=&v"(c[2]), "=&v"(c[3]), "=&v"(s0), "=&v"(s1), "=&v"(s2), "=&v"(s3)
-                   : "v"(ca), "v"(sa), "i"(0), "i"(CS), "i"(2 * CS), "i"(3 * CS), "i"(16), "i"(32), "i"(48)
-                   : "memory");
-      const uint4 ss[4] = {s0, s1, s2, s3};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) { w[4 * i] = ss[i].x; w[4 * i + 1] = ss[i].y; w[4 * i + 2] = ss[i].z; w[4 * i + 3] = ss[i].w; }
-    }
-  }
-#undef KVQ_R
-#undef KVQ_W
-}
-
-// The K codes and scales of the block in `stage`, in the registers and lane
-// order load_k would give.
-template <int FMT, int D>
-__device__ __forceinline__ void read_stage_k(Buf<FMT, D>& buf, uint32_t stage, int lane) {
-  using T = DT<FMT, D>;
-  const int g = lane >> 4, c16 = lane & 15;
-  const uint32_t sa = stage + T::SKS + (T::KC == C_E2G16 ? c16 * 16 : g * (4 * T::KSW));
-  lds_read_part<T::KCH, 1024, T::KSW>(buf.k, buf.ks, stage + T::SK + lane * 16, sa);
-}
-
-// The V codes and scales of the block in `stage`, as load_v would give them.
-template <int FMT, int D>
-__device__ __forceinline__ void read_stage_v(Buf<FMT, D>& buf, uint32_t stage, int lane) {
-  using T = DT<FMT, D>;
-  const int g = lane >> 4;
-  lds_read_part<T::VCH, 1024, T::VSW>(buf.v, buf.vs, stage + T::SV + lane * 16, stage + T::SVS + g * (4 * T::VSW));
-}
-
-// ----------------------------------------------------------- operand expanders
-
-// 8 E4M3 codes (two dwords) -> bf16x8, exact
-__device__ __forceinline__ bf16x8 e4m3x8_bf16(uint32_t w0, uint32_t w1) {
-  uint4 r;
-  r.x = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, false));
-  r.y = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, true));
-  r.z = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, false));
-  r.w = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, true));
-  return bitcast<bf16x8>(r);
-}
-
-// 4 signed int8 codes -> 2 x f16x2, exact: the byte with its sign bit
-// flipped (c + 128) becomes the low mantissa of 1024, then 1152 is removed.
-__device__ __forceinline__ void i8x4_f16(uint32_t w, f16x2& lo, f16x2& hi) {
-  const uint32_t u = w ^ 0x80808080u;
-  const f16x2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
-  lo = bitcast<f16x2>(__builtin_amdgcn_perm(0x64646464u, u, 0x04010400u)) + bias;
-  hi = bitcast<f16x2>(__builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) + bias;
-}
-
-__device__ __forceinline__ f16x8 i8x8_f16(uint32_t w0, uint32_t w1) {
-  f16x2 a, b, c, d;
-  i8x4_f16(w0, a, b);
-  i8x4_f16(w1, c, d);
-  return bitcast<f16x8>(make_uint4(bitcast<uint32_t>(a), bitcast<uint32_t>(b), bitcast<uint32_t>(c),
-                                   bitcast<uint32_t>(d)));
-}
-
-// 8 E2M1 codes (one dword, element e in nibble e) -> f16x8, exact
-__device__ __forceinline__ f16x8 e2m1x8_f16(uint32_t w) {
-  uint4 r;
-  r.x = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0));
-  r.y = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1));
-  r.z = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2));
-  r.w = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3));
-  return bitcast<f16x8>(r);
-}
-
-__device__ __forceinline__ uint32_t word(const uint4& q, int i) {
-  return i == 0 ? q.x : i == 1 ? q.y : i == 2 ? q.z : q.w;
-}
-
-// ----------------------------------------------------------- Q operands
-
-template <int FMT, int D>
-struct QOps {
-  // B operands of S = K . Q^T, k-step kk, piece p (bf16 q; f16 hi, lo; or
-  // int8 coarse, fine), as raw 16-byte lane values
-  using T = DT<FMT, D>;
-  uint4 reg[T::QLDS ? 1 : T::QSTEPS * T::QPIECES];
-  const uint4* lds;
-  int lane;
-  __device__ __forceinline__ uint4 get(int kk, int p) const {
-    if constexpr (T::QLDS) return lds[(kk * T::QPIECES + p) * 64 + lane];
-    else return reg[kk * T::QPIECES + p];
-  }
-};
-
-// ----------------------------------------------------------- S = K . Q^T
-
-template <int FMT, int D>
-__device__ __forceinline__ f32x4 qk_block(const Buf<FMT, D>& buf, const QOps<FMT, D>& qo, int lane) {
-  using T = DT<FMT, D>;
-  f32x4 S = {0.f, 0.f, 0.f, 0.f};
-  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (T::KC == C_BF16) {
-    // two independent accumulator chains (even / odd k-steps)
-    f32x4 S1 = zero;
-#pragma unroll
-    for (int kk = 0; kk < T::KSTEPS; kk += 2) {
-      S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(buf.k[kk]), bitcast<bf16x8>(qo.get(kk, 0)), S, 0, 0, 0);
-      S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(buf.k[kk + 1]), bitcast<bf16x8>(qo.get(kk + 1, 0)), S1,
-                                                   0, 0, 0);
-    }
-    S += S1;
-  } else if constexpr (T::KC == C_E4ROW || T::KC == C_E4TEN) {
-    f32x4 S1 = zero;
-#pragma unroll
-    for (int i = 0; i < T::KCH; ++i) {
-      S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_bf16(buf.k[i].x, buf.k[i].y), bitcast<bf16x8>(qo.get(2 * i, 0)), S, 0, 0, 0);
-      S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_bf16(buf.k[i].z, buf.k[i].w), bitcast<bf16x8>(qo.get(2 * i + 1, 0)), S1, 0, 0, 0);
-    }
-    S += S1;
-    if constexpr (T::KC == C_E4ROW) {
-      // one fp16 scale per token: tokens 4g..4g+3 in ks[0] (lo, hi), ks[1]
-      S[0] *= f16_bits_to_f32(buf.ks[0] & 0xFFFFu);
-      S[1] *= f16_bits_to_f32(buf.ks[0] >> 16);
-      S[2] *= f16_bits_to_f32(buf.ks[1] & 0xFFFFu);
-      S[3] *= f16_bits_to_f32(buf.ks[1] >> 16);
-    }
-  } else if constexpr (T::KC == C_E4MX) {
-    // one UE8M0 per 32 values = per k-step: scale each k-step's partial sum
-    constexpr int G = D / 32;
-#pragma unroll
-    for (int i = 0; i < T::KCH; ++i) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int kk = 2 * i + hh;
-        const f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            e4m3x8_bf16(hh ? buf.k[i].z : buf.k[i].x, hh ? buf.k[i].w : buf.k[i].y), bitcast<bf16x8>(qo.get(kk, 0)),
-            zero, 0, 0, 0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int bi = e * G + kk;  // token 4g+e, group kk
-          const int ex = (int)((buf.ks[bi >> 2] >> (8 * (bi & 3))) & 0xFFu) - 127;
-          S[e] += ldexpf(acc[e], ex);
-        }
-      }
-    }
-  } else if constexpr (T::KC == C_I8G64) {
-    // one fp16 scale per 64 values = one 16-byte chunk = one int8 k-step:
-    // the raw codes are the A operand; q = coarse + fine / 254 (int8 each)
-    const i32x4 izero = {0, 0, 0, 0};
-#pragma unroll
-    for (int grp = 0; grp < T::KCH; ++grp) {
-      const i32x4 kc = bitcast<i32x4>(buf.k[grp]);
-      const i32x4 a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(kc, bitcast<i32x4>(qo.get(grp, 0)), izero, 0, 0, 0);
-      const i32x4 a2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(kc, bitcast<i32x4>(qo.get(grp, 1)), izero, 0, 0, 0);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int hw = e * 4 + grp;  // halfword of token 4g+e, group grp
-        const float sc = f16_bits_to_f32((buf.ks[hw >> 1] >> (16 * (hw & 1))) & 0xFFFFu);
-        S[e] += (float)(a1[e] * 254 + a2[e]) * sc;  // |a1| <= 64*127*127: no int32 overflow
-      }
-    }
-  } else if constexpr (T::KC == C_E2G16) {
-    // E2M1 x UE4M3 is exact in f16: fold the group scale into the operand.
-    // lane (g, t): k-step kk covers d in [32kk + 8g, +8) -> group 2kk + g/2
-    const int gb = (lane >> 5) & 1;
-    f32x4 Slo = zero;
-#pragma unroll
-    for (int i = 0; i < T::KCH; ++i) {
-#pragma unroll
-      for (int hh = 0; hh < 4; ++hh) {
-        const int kk = 4 * i + hh;
-        const uint32_t sw = buf.ks[kk >> 1];
-        const uint32_t sb = (sw >> (8 * (2 * (kk & 1) + gb))) & 0xFFu;
-        const _Float16 s = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)sb, 1.0f, false)[0];
-        f16x8 a = e2m1x8_f16(word(buf.k[i], hh));
-        a *= s;
-        // hi and lo parts of q in separate chains
-        S = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bitcast<f16x8>(qo.get(kk, 0)), S, 0, 0, 0);
-        Slo = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bitcast<f16x8>(qo.get(kk, 1)), Slo, 0, 0, 0);
-      }
-    }
-    S += Slo;
-  }
-  return S;
-}
-
-// ----------------------------------------------------------- V operands
-
-// B operand of O += P . V for n-tile nt: tokens 4g..4g+3 of column 16*nt + n.
-template <int FMT, int D>
-__device__ __forceinline__ f16x4 v_operand(const Buf<FMT, D>& buf, int nt, int lane) {
-  using T = DT<FMT, D>;
-  if constexpr (T::VC == C_F16) {
-    const uint4& q = buf.v[nt >> 1];
-    const uint32_t a = (nt & 1) ? q.z : q.x, b = (nt & 1) ? q.w : q.y;
-    return bitcast<f16x4>(make_uint2(a, b));
-  } else if constexpr (T::VC == C_E4ROW || T::VC == C_E4TEN || T::VC == C_E4MX) {
-    const uint32_t w = word(buf.v[nt >> 2], nt & 3);
-    if constexpr (T::VC == C_E4MX) {
-      // UE8M0 per (token, 32 values): code * 2^e in fp32, one RNE to f16
-      constexpr int G = D / 32;
-      const int grp = nt >> 1;
-      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-      float x[4] = {lo[0], lo[1], hi[0], hi[1]};
-      f16x4 r;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int bi = e * G + grp;
-        const int ex = (int)((buf.vs[bi >> 2] >> (8 * (bi & 3))) & 0xFFu) - 127;
-        r[e] = (_Float16)ldexpf(x[e], ex);
-      }
-      return r;
-    } else {
-      f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, false);
-      f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, true);
-      if constexpr (T::VC == C_E4ROW) {
-        a *= bitcast<f16x2>(buf.vs[0]);
-        b *= bitcast<f16x2>(buf.vs[1]);
-      }
-      return f16x4{a[0], a[1], b[0], b[1]};
-    }
-  } else if constexpr (T::VC == C_I8G64) {
-    const uint32_t w = word(buf.v[nt >> 2], nt & 3);
-    f16x2 a, b;
-    i8x4_f16(w, a, b);
-    // scales: halfword (e*4 + grp) of vs; pair tokens (0,1) and (2,3)
-    const int grp = nt >> 2;
-    const uint32_t sel = (grp & 1) ? 0x07060302u : 0x05040100u;
-    const uint32_t s01 = __builtin_amdgcn_perm(buf.vs[2 + (grp >> 1)], buf.vs[grp >> 1], sel);
-    const uint32_t s23 = __builtin_amdgcn_perm(buf.vs[6 + (grp >> 1)], buf.vs[4 + (grp >> 1)], sel);
-    a *= bitcast<f16x2>(s01);
-    b *= bitcast<f16x2>(s23);
-    return f16x4{a[0], a[1], b[0], b[1]};
-  } else {  // C_E2G16: bytes 2 (nt & 1) and 2 (nt & 1) + 1 of word (nt & 7) / 2 of chunk nt / 8
-            // hold tokens (4g, 4g + 1) and (4g + 2, 4g + 3) of column n, the earlier token low
-    const uint32_t w = word(buf.v[nt >> 3], (nt & 7) >> 1);
-    f16x2 a, b;
-    if (nt & 1) {
-      a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
-      b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
-    } else {
-      a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
-      b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
-    }
-    const uint32_t sw = buf.vs[nt];  // UE4M3 of tokens 4g..4g+3, group nt
-    a *= __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)sw, 1.0f, false);
-    b *= __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)sw, 1.0f, true);
-    return f16x4{a[0], a[1], b[0], b[1]};
-  }
-}
-
-// ----------------------------------------------------------- 64-lane FWHT
-// Unnormalized-order-free Hadamard (any fp32 order is fine on the read
-// path): lane l holds elements E*l .. E*l+E-1 of a 64*E vector.
-template <int E>
-__device__ __forceinline__ void fwht_wave(float (&x)[E], int lane) {
-#pragma unroll
-  for (int h = 1; h < E; h <<= 1)
-#pragma unroll
-    for (int i = 0; i < E; ++i)
-      if ((i & h) == 0) {
-        const float a = x[i], b = x[i + h];
-        x[i] = a + b;
-        x[i + h] = a - b;
-      }
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const bool upper = (lane & m) != 0;
-#pragma unroll
-    for (int i = 0; i < E; ++i) {
-      const float p = __shfl_xor(x[i], m);
-      x[i] = upper ? (p - x[i]) : (x[i] + p);
-    }
-  }
-}
-
-// Maximum over the four lanes 16 g + c (g = 0..3) that share c, without an
-// LDS round trip: each swap leaves x of this lane and of its partner at
-// distance 16 (then 32) in the two results.
-__device__ __forceinline__ float max_over_g(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(bitcast<uint32_t>(x), bitcast<uint32_t>(x), false, false);
-  x = fmaxf(bitcast<float>((uint32_t)a[0]), bitcast<float>((uint32_t)a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(bitcast<uint32_t>(x), bitcast<uint32_t>(x), false, false);
-  return fmaxf(bitcast<float>((uint32_t)b[0]), bitcast<float>((uint32_t)b[1]));
-}
-
-// Slack of the running maximum, in log2 units (see pv_phase).
-constexpr float RESCALE_SLACK = 8.0f;
-
-// 2^x with the hardware exp: results below 2^-126 flush to zero, which only
-// drops probabilities far below anything that can change an fp32 sum
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// ----------------------------------------------------------- tail blocks
-
-// Zero the V codes and V scales of this lane's tokens 4g+e at or past
-// `nvalid` (slots past the sequence end may hold any bytes, NaN codes
-// included), so that tokens with zero probability add exactly zero.
-template <int FMT, int D>
-__device__ __forceinline__ void clear_tail(Buf<FMT, D>& buf, int nvalid, int g) {
-  using T = DT<FMT, D>;
-  const int nv = nvalid - 4 * g;  // valid tokens among this lane's four
-  uint32_t bmask = 0;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) bmask |= (e < nv) ? (0xFFu << (8 * e)) : 0u;
-  const uint32_t h01 = (nv > 0 ? 0xFFFFu : 0u) | (nv > 1 ? 0xFFFF0000u : 0u);
-  const uint32_t h23 = (nv > 2 ? 0xFFFFu : 0u) | (nv > 3 ? 0xFFFF0000u : 0u);
-  // 4-bit codes: nibble i of every word belongs to token i % 4
-  const uint32_t n16 = nv >= 4 ? 0xFFFFu : nv <= 0 ? 0u : (1u << (4 * nv)) - 1u;
-  const uint32_t nmask = n16 | (n16 << 16);
-#pragma unroll
-  for (int q = 0; q < T::VCH; ++q) {
-    if constexpr (T::VBITS == 16) {
-      buf.v[q].x &= h01; buf.v[q].y &= h23; buf.v[q].z &= h01; buf.v[q].w &= h23;
-    } else {
-      const uint32_t m = T::VBITS == 4 ? nmask : bmask;
-      buf.v[q].x &= m; buf.v[q].y &= m; buf.v[q].z &= m; buf.v[q].w &= m;
-    }
-  }
-  if constexpr (T::VC == C_E4ROW) {
-    buf.vs[0] &= h01;
-    buf.vs[1] &= h23;
-  } else if constexpr (T::VC == C_I8G64) {  // token e: words 2e, 2e+1
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (e >= nv) { buf.vs[2 * e] = 0u; buf.vs[2 * e + 1] = 0u; }
-  } else if constexpr (T::VC == C_E4MX) {  // token e: D/128 words
-    constexpr int WPT = D / 128;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-#pragma unroll
-      for (int w = 0; w < WPT; ++w)
-        if (e >= nv) buf.vs[e * WPT + w] = 0u;
-  } else if constexpr (T::VC == C_E2G16) {
-#pragma unroll
-    for (int w = 0; w < T::VSW; ++w) buf.vs[w] &= bmask;
-  }
-}
 
 // ----------------------------------------------------------- fused append
 
@@ -1185,10 +594,6 @@ __global__ __launch_bounds__(SG * D / 4) void decode_combine_kernel(DecodeArgs a
 
 // ----------------------------------------------------------- launchers
 
-#define KVQ_FOR_EACH_DECODE(X)                                                                     \
-  X(F_BF16, 128) X(F_BF16, 256) X(F_FP8_ROW, 128) X(F_FP8_ROW, 256) X(F_FP8_TENSOR, 128)          \
-  X(F_FP8_TENSOR, 256) X(F_MXFP8, 128) X(F_MXFP8, 256) X(F_INT8_G64, 256) X(F_NVFP4_G16, 256)   \
-  X(F_K8V4, 256)
 
 size_t decode_split_lds_bytes(const Geometry& geo, int B, int R) {
 #define KVQ_LDS_CASE(F, DD) \

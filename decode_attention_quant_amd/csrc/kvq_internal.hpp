@@ -52,6 +52,8 @@ hipError_t launch_append(uint8_t* pool, const uint16_t* k, const uint16_t* v, in
                          const Geometry& geo, float k_scale, float v_scale, hipStream_t stream);
 hipError_t launch_decode_split(const Geometry& geo, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_combine(const Geometry& geo, const DecodeArgs& a, hipStream_t stream);
+// Chunked-prefill attention (no split: DecodeArgs' workspace fields unused).
+hipError_t launch_prefill(const Geometry& geo, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_dequant_page(const Geometry& geo, const uint8_t* pool, int64_t page, bool stored_domain,
                                float k_scale, float v_scale, float* k_out, float* v_out, hipStream_t stream);
 

@@ -228,6 +228,22 @@ kvq_status kvq_decode_step_split(const kvq_cache_desc* desc, void* pool, const v
                                  int32_t num_workgroups, int32_t flags, float* out, float* lse,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Chunked-prefill causal attention over the compressed cache (NInfer guide:
+ * a prefill chunk's tokens, once appended, attend over the cache causally;
+ * the same quantity as kvq_decode_attention, for n_q up to a whole chunk).
+ * Arguments, layouts and the causal rule are those of kvq_decode_attention:
+ * query token i of sequence b sits at position seq_lens[b] - n_q + i (its
+ * K/V already stored) and attends to positions 0 .. that one.  No
+ * workspace: each (sequence, kv head) is not split; a workgroup takes 64
+ * query rows (G * n_q rows per kv head) and walks the cache once for them.
+ * Limits: G * n_q < 2^30; batch * num_kv_heads * ceil(G * n_q / 64) <= 2^30.
+ * Errors as in kvq_decode_attention. */
+kvq_status kvq_prefill_attention(const kvq_cache_desc* desc, const void* pool, const void* q_bf16,
+                                 int32_t batch, int32_t n_q, int32_t num_q_heads,
+                                 const int32_t* block_table, int32_t max_pages_per_seq,
+                                 const int32_t* seq_lens, float softmax_scale, float* out, float* lse,
+                                 hipStream_t stream);
+
 /* The plan kvq_decode_attention uses for this problem on the current device:
  * split workgroups and partial slots. */
 kvq_status kvq_decode_plan(const kvq_cache_desc* desc, int32_t batch, int32_t n_q,

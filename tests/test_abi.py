@@ -200,3 +200,27 @@ def test_decode_step_validation_enqueues_nothing():
     assert call(nq=3) == 2                  # G * n_q = 18 rows: more than one row tile
     assert call(Hq=22) == 1                 # not a multiple of H_kv
     assert call(pool=None, nq=1) == 1
+
+
+def test_prefill_validation_enqueues_nothing():
+    d = kvq.desc(4, 256, 64, 4, 100)
+    P = ctypes.c_void_p
+    ok = P(0x100000)
+    lib = kvq.library()
+
+    def call(pool=ok, q=ok, B=2, nq=37, Hq=24, bt=ok, sl=ok, out=ok, scale=0.0625):
+        return lib.kvq_prefill_attention(ctypes.byref(d), pool, q, B, nq, Hq, bt, 10, sl, scale, out, None, None)
+
+    assert call(B=0) == 0
+    assert call(pool=None) == 1
+    assert call(q=None) == 1
+    assert call(bt=None) == 1
+    assert call(sl=None) == 1
+    assert call(out=None) == 1
+    assert call(q=P(0x100008)) == 1
+    assert call(out=P(0x100004)) == 1
+    assert call(nq=0) == 1
+    assert call(Hq=22) == 1
+    assert call(scale=float("inf")) == 1
+    bad = kvq.desc(3, 128, 64, 4, 100)  # NVFP4 needs head_dim 256
+    assert lib.kvq_prefill_attention(ctypes.byref(bad), ok, ok, 2, 4, 24, ok, 10, ok, 0.1, ok, None, None) == 2
