@@ -54,6 +54,7 @@ import decode_attention_quant_amd as kvq  # noqa: E402
 import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense f16 / bf16 matrix peak
 FLUSH_BYTES = 1 << 30          # read before each timed step: 4x the 256 MB MALL
 RATE_BYTES = 4 << 30           # buffer of the streaming-rate measurement
 COPY_BYTES = RATE_BYTES // 2   # bytes each way of the probe's copy
@@ -249,6 +250,59 @@ def append_chunk_bench(formats, stream, probe, reps=10):
     return res
 
 
+def prefill_bench(stream, probe, chunk=APPEND_CHUNK, fmt="K8V4", reps=3):
+    """Chunked prefill of the mixed-length workload: 64 sequences of
+    ~U(ln 1K, ln 128K) cached tokens, each followed by a `chunk`-token prefill
+    chunk (appended through the write path, untimed); then every chunk query
+    attends causally over its sequence's cache (timed).  Attention flops are
+    4 D H_q per visible (query, position) pair; the kernel's matrix products
+    are f16/bf16, so the roof is the 2.5 PFLOP/s dense peak."""
+    c = W.make_case(4, fmt, device="cuda", n_q=chunk, reserve=chunk)
+    d = kvq.desc(c.fmt, c.D, c.P, c.H_kv, c.num_pages, c.k_scale, c.v_scale)
+    pool = kvq.alloc_pool(d)
+    kvq.quantize_append(d, pool, c.k, c.v, c.slot_mapping)
+    k, v, slots = W.append_chunk(c, chunk, device="cuda")
+    kvq.quantize_append(d, pool, k, v, slots)
+    del k, v, slots
+    c.k = c.v = None
+    torch.cuda.empty_cache()
+    lens = c.seq_lens.astype(np.int64)
+    sl = torch.as_tensor((lens + chunk).astype(np.int32), device="cuda")
+    bt = torch.as_tensor(c.block_table, device="cuda")
+    out = torch.empty(c.q.shape, dtype=torch.float32, device="cuda")
+    visible = int(np.sum(chunk * (lens + 1) + chunk * (chunk - 1) // 2))  # sum over queries of positions seen
+    flops = 4.0 * c.D * c.H_q * visible
+    ts = []
+    with torch.cuda.stream(stream):
+        for i in range(reps + 1):
+            probe.flush(stream)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record(stream)
+            kvq.prefill_attention(d, pool, c.q, bt, sl, c.softmax_scale, out=out, stream=stream)
+            e[1].record(stream)
+            if i >= 1:
+                ts.append(e)
+        torch.cuda.synchronize()
+    ms = [e[0].elapsed_time(e[1]) for e in ts]
+    mean = float(np.mean(ms))
+    tflops = flops / (mean * 1e-3) / 1e12
+    kv_bytes = int((lens + chunk).sum()) * c.H_kv * kv_bytes_per_token(d)
+    res = {"workload": "64 sequences x one %d-token prefill chunk after U(ln 1K, ln 128K) cached tokens, "
+                       "24 q / 4 kv heads, head_dim 256, causal over the cache" % chunk,
+           "kv_dtype": fmt, "query_tokens": int(c.B * chunk), "attention_flops": flops,
+           "ms": mean, "ms_runs": ms, "TFLOP_per_s": tflops,
+           "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": tflops / MFMA_PEAK_TFLOPS, "kernel": "prefill_kernel<%d, %d> (%s)" % (
+                            kvq.FORMATS[fmt], c.D, fmt)},
+           "kv_bytes_per_call": kv_bytes, "row_tiles": int(c.B * c.H_kv * ((6 * chunk + 63) // 64))}
+    print("[bench] prefill %s: %d query tokens over %.2f GB of cache in %.2f ms, %.0f TFLOP/s (%.1f%% of %.0f)" % (
+        fmt, c.B * chunk, kv_bytes / 1e9, mean, tflops, 100 * tflops / MFMA_PEAK_TFLOPS, MFMA_PEAK_TFLOPS),
+        file=sys.stderr, flush=True)
+    del pool, out, c
+    torch.cuda.empty_cache()
+    return res
+
+
 # the sources the split kernel is compiled from
 SPLIT_SOURCES = ["kvq_decode.hip", "kvq_device.hpp", "kvq_encode.hpp", "kvq_format.hpp", "kvq_internal.hpp"]
 
@@ -376,6 +430,7 @@ def main():
     ap.add_argument("--append-formats", default=",".join(APPEND_FORMATS),
                     help="formats of the prefill-chunk append measurement, or 'none'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill attention measurement")
     ap.add_argument("--no-flush", action="store_true", help="time steps back to back, caches warm")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -446,6 +501,7 @@ def main():
     achieved = s.kv_bytes / (split_ms * 1e-3) / 1e9
     append_formats = [] if args.append_formats == "none" else args.append_formats.split(",")
     appends = append_chunk_bench(append_formats, stream, probe) if append_formats else {}
+    prefill = None if args.no_prefill else prefill_bench(stream, probe)
     line = {
         "metric": METRIC,
         "value": res["GB_per_s"],
@@ -476,6 +532,7 @@ def main():
                           "kv_dtype": append_formats[0], **appends[append_formats[0]],
                           "per_kv_dtype": appends} if appends else None),
         "per_kv_dtype": per,
+        "prefill_attention": prefill,
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) on %s" % fmt, file=sys.stderr, flush=True)
