@@ -8,37 +8,39 @@
 // Decode spreads one unit's blocks over many workgroups; prefill has rows to
 // spare instead (G * n_q per kv head, 12288 for a 2048-token chunk at G = 6),
 // so nothing is split: a workgroup takes 64 rows of one (sequence b, kv head
-// h) unit, 16 per wave, and every wave walks the unit's blocks up to its rows'
-// last visible position through its own LDS ring, with the decode kernel's
-// per-block code (K expanded exactly into matrix-core operands, Q.K, online
-// softmax with the lazy running maximum, P.V).  The four waves of a
-// workgroup read the same blocks at about the same time, and the work items
-// are laid out so that one unit's row tiles run on one XCD, so its L2 serves
-// the repeats and HBM sees a unit's cache about once per XCD.  Each wave
-// finishes its own rows: normalization, the inverse rotation of V for the
-// rotated formats (through LDS, 8 rows at a time), output and lse.
+// h) unit, 16 per wave, and walks the unit's blocks up to its rows' last
+// visible position.  Wave 0 copies each block once into the workgroup's LDS
+// ring; one barrier per block publishes it and frees the stage read last;
+// every wave then runs the decode kernel's per-block code on it for its own
+// rows (K expanded exactly into matrix-core operands, Q.K, online softmax
+// with the lazy running maximum, P.V).  The work items are laid out so that
+// one unit's row tiles run on one XCD, whose L2 then serves the repeats, so
+// HBM sees a unit's cache about once per XCD.  Each wave finishes its own
+// rows: normalization, the inverse rotation of V for the rotated formats
+// (through LDS, 8 rows at a time), output and lse.
 #include <hip/hip_runtime.h>
 
 #include "kvq_decode_core.hpp"
 
 namespace kvq {
 
-// Ring depth of the prefill kernel: stages per wave that fit in 72 KB per
-// workgroup of 4 waves (two workgroups per CU), from 1 to 4.  Outside the
-// block loop a wave's ring holds 8 fp32 rows of D.
+// The workgroup's block ring: up to 4 stages within 64 KB (two workgroups
+// per CU).  Outside the block loop the same area holds 8 fp32 rows of D per
+// wave.
 template <int FMT, int D>
 struct PT {
   using T = DT<FMT, D>;
-  static constexpr int FIT = 72 * 1024 / (4 * T::STAGE);
-  static constexpr int S = FIT > 4 ? 4 : (FIT < 1 ? 1 : FIT);
-  static constexpr int WAVE_LDS = S * T::STAGE;
+  static constexpr int FIT = 64 * 1024 / T::STAGE;
+  static constexpr int S = FIT > 4 ? 4 : FIT;
+  static_assert(S >= 2, "the ring keeps a block in flight while one is read");
+  static constexpr int ROWS_BYTES = 4 * 8 * D * 4;  // 8 fp32 rows per wave
+  static constexpr int AREA = S * T::STAGE > ROWS_BYTES ? S * T::STAGE : ROWS_BYTES;
   static constexpr int HDR_FLOATS = 256;  // per wave 16 m, 16 l, 16 q maxima (4 waves)
-  static_assert(WAVE_LDS >= 8 * D * 4, "a wave's ring holds 8 fp32 rows");
 };
 
 template <int FMT, int D>
 __host__ __device__ constexpr size_t prefill_lds_bytes() {
-  return PT<FMT, D>::HDR_FLOATS * sizeof(float) + 4 * (size_t)PT<FMT, D>::WAVE_LDS;
+  return PT<FMT, D>::HDR_FLOATS * sizeof(float) + (size_t)PT<FMT, D>::AREA;
 }
 
 // One work item = 64 rows (a row tile) of one unit; item wi runs on workgroup
@@ -62,22 +64,21 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(Geometry geo, DecodeArg
   const int L = as_const(a.seq_lens)[b];
 
   float* hdr = lds + wave * 48;  // m [16], l [16], q maxima [16] of this wave's rows
-  uint8_t* ringp = reinterpret_cast<uint8_t*>(lds + PP::HDR_FLOATS) + wave * PP::WAVE_LDS;
-  float* wbuf = reinterpret_cast<float*>(ringp);  // the ring, as 8 fp32 rows, outside the block loop
-  const uint32_t ring0 = (uint32_t)(uintptr_t)(void*)ringp;
+  uint8_t* area = reinterpret_cast<uint8_t*>(lds + PP::HDR_FLOATS);
+  float* wbuf = reinterpret_cast<float*>(area) + wave * 8 * D;  // this wave's 8 rows, outside the block loop
+  const uint32_t ring0 = (uint32_t)(uintptr_t)(void*)area;     // the ring during it
 
   // ---- this wave's rows r0 .. r0 + 15; lane row c16 (S layout) -> (query i, head)
   const int r0 = 64 * tile + 16 * wave;
-  if (r0 >= a.R) return;  // the waves share nothing, so one may leave early
+  const bool has_rows = r0 < a.R;  // wave-uniform; a wave without rows still joins the barriers
   const int rr = r0 + c16;
   const bool row_ok = rr < a.R;
   const int qi = rr / a.G, qh = h * a.G + (rr - qi * a.G);
   const int limit = row_ok ? L - a.n_q + qi : -1;  // last visible position of the row
-  int lim_max = limit;
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) lim_max = max(lim_max, __shfl_xor(lim_max, m));
-  lim_max = __builtin_amdgcn_readfirstlane(lim_max);
-  const int nk = lim_max >= 0 ? (lim_max >> 4) + 1 : 0;  // blocks the wave walks
+  // blocks the workgroup walks: up to the last visible position of its last row
+  const int last_row = min(a.R, 64 * tile + 64) - 1;
+  const int lim_wg = L - a.n_q + last_row / a.G;
+  const int nk = lim_wg >= 0 ? (lim_wg >> 4) + 1 : 0;
 
   // ---- Q operands of the wave's rows (as the decode kernel's, per wave)
   QOps<FMT, D, false> qo;
@@ -158,9 +159,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(Geometry geo, DecodeArg
         }
       }
     }
-    // every read of wbuf is done before the ring's copies overwrite it
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   }
+  // every wave is done with its rows in the area before the ring's copies overwrite it
+  __syncthreads();
 
   // ---- stream the unit's blocks 0 .. nk - 1 through this wave's ring
   const uint8_t* head0 = a.pool + (int64_t)h * geo.head_bytes;
@@ -170,18 +171,25 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(Geometry geo, DecodeArg
 #pragma unroll
   for (int nt = 0; nt < T::NT; ++nt) O[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   {
+    // wave 0 copies blocks 0 .. S - 2 ahead; in iteration k it waits for
+    // block k, the barrier publishes it (and every wave is then done with
+    // block k - 1), and wave 0 refills that stage with block k + S - 1
     constexpr int S = PP::S;
+    if (wave == 0) {
 #pragma unroll
-    for (int k = 0; k < S - 1; ++k)
-      if (k < nk) stage_block<FMT, D>(ring0 + k * T::STAGE, head0, geo, bt_row, k, lane);
+      for (int k = 0; k < S - 1; ++k)
+        if (k < nk) stage_block<FMT, D>(ring0 + k * T::STAGE, head0, geo, bt_row, k, lane);
+    }
     Buf<FMT, D> A;
     int st = 0;
     for (int k = 0; k < nk; ++k) {
-      // the stage read last (block k - 1) is refilled with block k + S - 1
-      if (k + S - 1 < nk)
+      if (wave == 0) wait_staged<T::NDMA, S>(min(S - 2, nk - 1 - k));
+      __syncthreads();
+      if (wave == 0 && k + S - 1 < nk)
         stage_block<FMT, D>(ring0 + ((st + S - 1) % S) * T::STAGE, head0, geo, bt_row, k + S - 1, lane);
-      wait_staged<T::NDMA, S>(min(S - 1, nk - 1 - k));
       const uint32_t stg = ring0 + st * T::STAGE;
+      st = st + 1 == S ? 0 : st + 1;
+      if (!has_rows) continue;
       const int t0 = 16 * k;
       read_stage_k<FMT, D>(A, stg, lane);
       __builtin_amdgcn_sched_barrier(0);
@@ -221,9 +229,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(Geometry geo, DecodeArg
         O[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(P, v_operand<FMT, D>(A, nt, lane), O[nt], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      st = st + 1 == S ? 0 : st + 1;
     }
   }
+  __syncthreads();  // every wave is done with the ring before the area holds rows again
+  if (!has_rows) return;
 
   // ---- finish the rows: l over the row's 4 lane groups; row 4g + e of O
   l_run += __shfl_xor(l_run, 16);
