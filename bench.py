@@ -304,7 +304,8 @@ def prefill_bench(stream, probe, chunk=APPEND_CHUNK, fmt="K8V4", reps=3):
 
 
 # the sources the split kernel is compiled from
-SPLIT_SOURCES = ["kvq_decode.hip", "kvq_device.hpp", "kvq_encode.hpp", "kvq_format.hpp", "kvq_internal.hpp"]
+SPLIT_SOURCES = ["kvq_decode.hip", "kvq_decode_core.hpp", "kvq_device.hpp", "kvq_encode.hpp", "kvq_format.hpp",
+                 "kvq_internal.hpp"]
 
 
 def kernel_sources_sha():
@@ -460,7 +461,11 @@ def main():
     for fmt in formats:
         print("[bench] %s %s: building the cache" % (args.workload, fmt), file=sys.stderr, flush=True)
         s = Setup(wl["config"], fmt)
-        # the step as append + decode (the headline), then as one fused step
+        # the step as append + decode (the headline), then as one fused step,
+        # after a few untimed steps of each (the first steps after the cache
+        # is built run slower)
+        for fused in (False, True):
+            time_steps(s, 3, 1, stream, flush, fused=fused)
         t = time_steps(s, args.steps, args.warmup, stream, flush, fused=False)
         tf = time_steps(s, args.steps, args.warmup, stream, flush, fused=True)
         ms = t["step"]["mean"] if flush is not None else t["wall"]

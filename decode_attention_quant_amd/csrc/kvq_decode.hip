@@ -42,13 +42,13 @@ namespace kvq {
 // ----------------------------------------------------------- fused append
 
 // Encode and store the new tokens of sequence b, kv head h at positions
-// [plo, phi) (all inside this workgroup's blocks): wave 0 the K rows (a
-// quad per token), wave 1 the V rows (a row of 16 lanes per 4 tokens), with
-// the write path's own encoders, so the bytes are those quantize-append
-// stores.  Input token i of sequence b is row b * n_q + i of k_new / v_new.
+// [plo, phi) (at most one 16-token block) with one wave: the K rows (a quad
+// per token), then the V rows (a row of 16 lanes per 4 tokens), with the
+// write path's own encoders, so the bytes are those quantize-append stores.
+// Input token i of sequence b is row b * n_q + i of k_new / v_new.
 template <int FMT, int D>
 __device__ __forceinline__ void append_new_tokens(const DecodeArgs& a, const Geometry& geo, int b, int h, int L,
-                                               int plo, int phi, int wave, int lane) {
+                                               int plo, int phi, int lane) {
   const int pnew = L - a.n_q;          // position of new token 0
   const int64_t tok0 = (int64_t)b * a.n_q;
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
@@ -57,22 +57,18 @@ __device__ __forceinline__ void append_new_tokens(const DecodeArgs& a, const Geo
     return p >= 0 ? bt[p / geo.P] * geo.P + p % geo.P : -1;
   };
   const int ilo = plo - pnew, ihi = phi - pnew;  // new-token indexes written here
-  if (wave == 0) {
+  {
     const int q = lane & 3;
-    for (int i0 = ilo; i0 < ihi; i0 += 16) {
-      const int i = i0 + (lane >> 2);  // a whole quad shares it
-      if (i < ihi) {
-        const int64_t tok = tok0 + i;
-        uint32_t raw[D / 8];
-        enc::load_k_row<D>(raw, a.k_new + (tok * geo.H_kv + h) * D + q * (D / 4));
-        enc::encode_k_row<FMT, D>(a.pool_w, raw, slot_of(tok), geo, h, a.enc_k_scale, q);
-      }
+    const int i = ilo + (lane >> 2);  // a whole quad shares it
+    if (i < ihi) {
+      const int64_t tok = tok0 + i;
+      uint32_t raw[D / 8];
+      enc::load_k_row<D>(raw, a.k_new + (tok * geo.H_kv + h) * D + q * (D / 4));
+      enc::encode_k_row<FMT, D>(a.pool_w, raw, slot_of(tok), geo, h, a.enc_k_scale, q);
     }
-  } else if (wave == 1) {
-    for (int i0 = ilo; i0 < ihi; i0 += 16)
-      enc::v_row_group<FMT, D>(a.pool_w, a.v_new, slot_of, geo, a.enc_v_scale, h, lane & 15,
-                               tok0 + i0 + 4 * (lane >> 4), tok0 + ilo, tok0 + ihi);
   }
+  enc::v_row_group<FMT, D>(a.pool_w, a.v_new, slot_of, geo, a.enc_v_scale, h, lane & 15,
+                           tok0 + ilo + 4 * (lane >> 4), tok0 + ilo, tok0 + ihi);
 }
 
 // ----------------------------------------------------------- the kernel
@@ -132,10 +128,14 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
   {
     const int per_t = (a.B + 255) / 256;
     const int b0 = threadIdx.x * per_t;
-    int run = 0;
+    int run = 0, first = 0;  // first: blocks of sequence b0 (the only one when B <= 256)
     for (int i = 0; i < per_t; ++i) {
       const int bb = b0 + i;
-      if (bb < a.B) run += ((a.seq_lens[bb] + 15) >> 4) * geo.H_kv;
+      if (bb < a.B) {
+        const int nbk = ((a.seq_lens[bb] + 15) >> 4) * geo.H_kv;
+        if (i == 0) first = nbk;
+        run += nbk;
+      }
     }
     float* tot = sm_o;  // scratch [257] before the merge area is used (it holds >= 512)
     tot[threadIdx.x] = __int_as_float(run);
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
       const int bb = b0 + i;
       if (bb < a.B) {
         cum[bb] = base;
-        base += ((a.seq_lens[bb] + 15) >> 4) * geo.H_kv;
+        base += i == 0 ? first : ((a.seq_lens[bb] + 15) >> 4) * geo.H_kv;
       }
     }
     if (threadIdx.x == 0) cum[a.B] = __float_as_int(tot[256]);
@@ -191,23 +191,39 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
     const int nblk = __builtin_amdgcn_readfirstlane(seg_end - x);
     const bool whole = blk0 == 0 && nblk == nb;
     const int u = b * geo.H_kv + h;
+    // A segment's start-up is a chain of latencies (the query, the first
+    // copies, the new tokens' stores): it runs at the top priority, ahead of
+    // the other workgroup's waves streaming on the same SIMDs.
+    __builtin_amdgcn_s_setprio(3);
 
-    // ---- fused step: store the new tokens that fall in this segment's
-    //      blocks before any of those blocks is staged.  No other workgroup
-    //      reads them (one row tile), and this one reads them through the
-    //      same L2, so it is enough that its stores and atomics have
-    //      completed (vmcnt 0) before the barrier: a workgroup-scope fence,
-    //      not a device-wide L2 write-back.  The atomics of 4-bit V codes
-    //      touch only cache lines of this block's own code plane.
+    // ---- fused step: the wave that owns a block holding new tokens stores
+    //      them (n_q <= 16: at most two blocks, so two waves).  Only that
+    //      wave reads the block (one row tile, one owner), through the same
+    //      L2, so its stores and atomics only have to be complete before its
+    //      own copy of the block is issued; the atomics of 4-bit V codes
+    //      touch only cache lines of the block's own code plane.  Loads and
+    //      stores of a wave complete in order as far as the vector-memory
+    //      counter goes, so a ring block staged at iteration k >= 1, issued
+    //      after the wait for block k - 1, needs no wait of its own.  A block
+    //      staged at start-up is stored first and waited for; a block that
+    //      the ring stages later is stored once the first copies are out
+    //      (its loads then overlap theirs), just before the block loop.
+    int kmine = -1;  // this wave's index k of its block with new tokens
+    int mlo = 0, mhi = 0;
     if constexpr (FUSED) {
       const int plo = max(max(L - a.n_q, 0), 16 * blk0), phi = min(L, 16 * (blk0 + nblk));
-      if (plo < phi) {
-        append_new_tokens<FMT, D>(a, geo, b, h, L, plo, phi, wave, lane);
-        wait_vmcnt<0>();
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __syncthreads();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      for (int jb = plo >> 4; plo < phi && jb <= (phi - 1) >> 4; ++jb) {
+        if (((jb - blk0) & 3) == wave) {
+          kmine = (jb - blk0) >> 2;
+          mlo = max(plo, 16 * jb);
+          mhi = min(phi, 16 * jb + 16);
+        }
       }
+    }
+    const bool late_append = T::RING && kmine >= T::RING_S - 1;
+    if (FUSED && kmine >= 0 && !late_append) {
+      append_new_tokens<FMT, D>(a, geo, b, h, L, mlo, mhi, lane);
+      wait_vmcnt<0>();
     }
 
     // ---- query rows of this tile: row r (= c16 in S layout) -> (i, head)
@@ -217,11 +233,36 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
     const int qi = rr / a.G, qh = h * a.G + (rr - qi * a.G);
     const int limit = row_ok ? L - a.n_q + qi : -1;  // last visible position of this row
     float crow = a.qk_scale;
+    const uint8_t* head0 = a.pool + (int64_t)h * geo.head_bytes;
+    const cint32* bt_row = as_const(a.block_table) + (int64_t)b * a.max_pages;
 
+    // ---- start-up latencies overlap: the page numbers of this wave's first
+    //      blocks and the query rows are loaded together; a rotated query
+    //      is transformed as soon as it lands, and the copies of the first
+    //      S - 1 blocks go out before the rest of the query setup
+    //      All of these loads are issued on every path (indexes past the end
+    //      are clamped to valid ones, whose data is then not used), so that
+    //      the compiler can count them exactly and does not drain every
+    //      outstanding load where paths join.
+    int nk = 0;  // ring formats: this wave's blocks blk0 + wave + 4 k, k < nk
+    BlockAddr pre[T::RING ? T::RING_S - 1 : 1];
+    if constexpr (T::RING) {
+      nk = nblk > wave ? (nblk - wave + 3) >> 2 : 0;
+#pragma unroll
+      for (int k = 0; k < T::RING_S - 1; ++k)
+        pre[k] = block_addr(head0, geo, bt_row, min(blk0 + wave + 4 * k, blk0 + nblk - 1));
+    }
+    auto stage_first = [&]() {  // blocks k >= nk land in stages that are never read
+      if constexpr (T::RING) {
+#pragma unroll
+        for (int k = 0; k < T::RING_S - 1; ++k) stage_block_at<FMT, D>(ring0 + k * T::STAGE, pre[k], geo, lane);
+      }
+    };
     QOps<FMT, D> qo;
     qo.lane = lane;
     qo.lds = qst;
     uint4 qv[T::QSTEPS * T::QPIECES];
+    constexpr int E = D / 64;
     if constexpr (!T::QROT) {
       const uint16_t* qp = a.q + (((int64_t)b * a.n_q + qi) * a.H_q + qh) * D;
 #pragma unroll
@@ -230,30 +271,84 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
         if (row_ok) q4 = *reinterpret_cast<const uint4*>(qp + 32 * kk + 8 * g);
         qv[kk] = q4;
       }
+      stage_first();
+      // Take the query operands here, not at their first use inside the
+      // block loop: a register load still pending at the loop entry makes
+      // the compiler wait for every load (vmcnt 0) in each iteration, which
+      // would drain the ring.
+#pragma unroll
+      for (int i = 0; i < T::QSTEPS; ++i) asm volatile("" : : "v"(qv[i].x), "v"(qv[i].y), "v"(qv[i].z), "v"(qv[i].w));
     } else {
-      // q' = H q / 16 in fp32 (rows spread over the waves, through LDS)
-      float* qrot = sm_o;  // [Rt][D]
-      constexpr int E = D / 64;
-      for (int row = wave; row < Rt; row += 4) {
+      // q' = H q / 16 in fp32 for rows wave, wave + 4, ... of the tile,
+      // transposed through LDS: for ring formats row `row` sits in the last
+      // stage of wave (row & 3)'s ring, which no copy targets before the
+      // block loop, and is written and read with the self-waiting accesses
+      // above while the first blocks are in flight; otherwise row `row` of
+      // the merge area.  max|q'| of row `row` goes to qexp[row].
+      static_assert(E == 4, "the rotation is 256-point");
+      uint2 qraw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = wave + 4 * i < Rt ? wave + 4 * i : 0;  // rows past Rt load row 0, unused
         const int rr2 = 16 * rt + row;
         const int i2 = rr2 / a.G, h2 = h * a.G + (rr2 - i2 * a.G);
-        const uint16_t* qp = a.q + (((int64_t)b * a.n_q + i2) * a.H_q + h2) * D + E * lane;
-        float xq[E];
-        const uint2 q2 = *reinterpret_cast<const uint2*>(qp);
-        xq[0] = bf16_to_f32(q2.x & 0xFFFFu); xq[1] = bf16_to_f32(q2.x >> 16);
-        xq[2] = bf16_to_f32(q2.y & 0xFFFFu); xq[3] = bf16_to_f32(q2.y >> 16);
-        fwht_wave<E>(xq, lane);
-        float am = 0.f;
-#pragma unroll
-        for (int i = 0; i < E; ++i) { xq[i] *= 0.0625f; am = fmaxf(am, fabsf(xq[i])); }
-#pragma unroll
-        for (int m = 1; m < 64; m <<= 1) am = fmaxf(am, __shfl_xor(am, m));
-#pragma unroll
-        for (int i = 0; i < E; ++i) qrot[row * D + E * lane + i] = xq[i];
-        if (lane == 0) qexp[row] = am;
+        qraw[i] = *reinterpret_cast<const uint2*>(a.q + (((int64_t)b * a.n_q + i2) * a.H_q + h2) * D + E * lane);
       }
-      __syncthreads();
-      const float am = row_ok ? qexp[r] : 0.f;
+      float xq[4][E], amx[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        {
+          xq[i][0] = bf16_to_f32(qraw[i].x & 0xFFFFu); xq[i][1] = bf16_to_f32(qraw[i].x >> 16);
+          xq[i][2] = bf16_to_f32(qraw[i].y & 0xFFFFu); xq[i][3] = bf16_to_f32(qraw[i].y >> 16);
+          fwht_wave<E>(xq[i], lane);
+          float am = 0.f;
+#pragma unroll
+          for (int e = 0; e < E; ++e) { xq[i][e] *= 0.0625f; am = fmaxf(am, fabsf(xq[i][e])); }
+#pragma unroll
+          for (int m = 1; m < 64; m <<= 1) am = fmaxf(am, __shfl_xor(am, m));
+          amx[i] = am;
+        }
+      }
+      stage_first();
+      const uint32_t qexp_a = (uint32_t)(uintptr_t)(void*)qexp;
+      auto qrow_a = [&](int row) -> uint32_t {  // LDS byte address of row `row` (ring formats)
+        return (uint32_t)(uintptr_t)(void*)sm_o +
+               (uint32_t)((row & 3) * T::RING_S * T::STAGE + (T::RING_S - 1) * T::STAGE + (row >> 2) * D * 4);
+      };
+      if constexpr (T::RING) static_assert(T::STAGE >= 4 * D * 4, "four rows fit a stage");
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = wave + 4 * i;  // rows past Rt hold values nobody reads
+        {
+          if constexpr (T::RING) {
+            lds_put4(qrow_a(row) + 16 * lane, xq[i][0], xq[i][1], xq[i][2], xq[i][3]);
+            if (lane == 0) lds_put1(qexp_a + 4 * row, amx[i]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) sm_o[row * D + E * lane + e] = xq[i][e];
+            if (lane == 0) qexp[row] = amx[i];
+          }
+        }
+      }
+      // The rows are in LDS once each write has waited for itself; a bare
+      // barrier then publishes them (__syncthreads' fence would also wait
+      // for the copies in flight).
+      if constexpr (T::RING) __builtin_amdgcn_s_barrier();
+      else __syncthreads();
+      // 8 consecutive elements d0 .. d0 + 7 of this lane's row r
+      auto row8 = [&](int d0, float (&x)[8]) {
+        if constexpr (T::RING) {
+          lds_get8(qrow_a(r) + 4 * d0, x);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = sm_o[r * D + d0 + e];
+        }
+      };
+      float am = 0.f;
+      if (row_ok) {
+        if constexpr (T::RING) am = lds_get1(qexp_a + 4 * r);
+        else am = qexp[r];
+      }
       if constexpr (T::QI8) {
         // q' ~ (c1 + c2 / 254) / inv, int8 c1 = RN(q' inv), c2 = RN(254 (q' inv - c1)),
         // inv = 127 / max|q'|: error below max|q'| / 64516 per element
@@ -262,11 +357,14 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
 #pragma unroll
         for (int kk = 0; kk < T::QSTEPS; ++kk) {
           uint32_t w1[4] = {0, 0, 0, 0}, w2[4] = {0, 0, 0, 0};
+          float xa[8], xb[8];
+          // k-slot 16g + j of int8 k-step kk <-> d as laid out in the K chunk:
+          // j < 8 at 64 kk + 8 g + j, else at 64 kk + 32 + 8 g + (j - 8)
+          row8(64 * kk + 8 * g, xa);
+          row8(64 * kk + 32 + 8 * g, xb);
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
-            // k-slot 16g + j of int8 k-step kk <-> d as laid out in the K chunk
-            const int d = 64 * kk + (j < 8 ? 8 * g + j : 32 + 8 * g + (j - 8));
-            const float v = row_ok ? qrot[r * D + d] * inv : 0.f;
+            const float v = row_ok ? (j < 8 ? xa[j] : xb[j - 8]) * inv : 0.f;
             const float c1 = fmaxf(fminf(rintf(v), 127.f), -127.f);
             const float c2 = fmaxf(fminf(rintf((v - c1) * 254.0f), 127.f), -127.f);
             w1[j >> 2] |= ((uint32_t)(int)c1 & 0xFFu) << (8 * (j & 3));
@@ -282,10 +380,12 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
         if (row_ok) crow = a.qk_scale * ldexpf(1.0f, ex - 8);
 #pragma unroll
         for (int kk = 0; kk < T::QSTEPS; ++kk) {
+          float x8[8];
+          row8(32 * kk + 8 * g, x8);
           f16x8 qh16, ql16;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float v = row_ok ? ldexpf(qrot[r * D + 32 * kk + 8 * g + e], 8 - ex) : 0.f;
+            const float v = row_ok ? ldexpf(x8[e], 8 - ex) : 0.f;
             qh16[e] = (_Float16)v;
             ql16[e] = (_Float16)(v - (float)qh16[e]);
           }
@@ -304,12 +404,21 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
     } else {
 #pragma unroll
       for (int i = 0; i < T::QSTEPS * T::QPIECES; ++i) qo.reg[i] = qv[i];
-      if constexpr (T::QROT) __syncthreads();  // qrot (the merge area) is free again
+      // the rotated rows' LDS (merge area, or the rings' last stages, which
+      // the block loop refills first) is free again; ring formats read it
+      // with self-waiting accesses, so a bare barrier suffices there
+      if constexpr (T::QROT) {
+        if constexpr (T::RING) __builtin_amdgcn_s_barrier();
+        else __syncthreads();
+      }
+    }
+
+    if (FUSED && late_append) {
+      append_new_tokens<FMT, D>(a, geo, b, h, L, mlo, mhi, lane);
+      if (kmine == T::RING_S - 1) wait_vmcnt<0>();  // staged by the first iteration's refill
     }
 
     // ---- stream this wave's token blocks: blk0 + wave, blk0 + wave + 4, ...
-    const uint8_t* head0 = a.pool + (int64_t)h * geo.head_bytes;
-    const cint32* bt_row = as_const(a.block_table) + (int64_t)b * a.max_pages;
     float m_run = NEG_INF, l_run = 0.f;
     f32x4 O[T::NT];
 #pragma unroll
@@ -371,14 +480,17 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
       if constexpr (T::RING) {
         // this wave's blocks j_k = blk0 + wave + 4 k, k < nk; block k sits in
         // stage k % S, and blocks k + 1 .. k + S - 1 are in flight meanwhile
+        // (the first S - 1 were staged before the query setup)
         constexpr int S = T::RING_S;
-        const int nk = nblk > wave ? (nblk - wave + 3) >> 2 : 0;
-#pragma unroll
-        for (int k = 0; k < S - 1; ++k)
-          if (k < nk) stage_block<FMT, D>(ring0 + k * T::STAGE, head0, geo, bt_row, j + 4 * k, lane);
         Buf<FMT, D> A;
         float sc[4];
         int st = 0;
+        // Two workgroups share each SIMD, and the instruction arbiter
+        // favours the older wave: left alone, one wave finishes long before
+        // the other, which then runs its last blocks without a partner to
+        // hide its stalls.  Stepping the priority down as a wave progresses
+        // lets the one behind catch up, so the two finish close together.
+        const int q1 = nk >> 2, q2 = nk >> 1, q3 = nk - (nk >> 2);
         for (int k = 0; k < nk; ++k) {
           // stage st - 1 (block k - 1) has been read: refill it with block k + S - 1
           if (k + S - 1 < nk) {
@@ -393,7 +505,14 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
           pv_phase(A, j, sc);
           j += 4;
           st = st + 1 == S ? 0 : st + 1;
+          if (k == q1) __builtin_amdgcn_s_setprio(2);
+          if (k == q2) __builtin_amdgcn_s_setprio(1);
+          if (k == q3) __builtin_amdgcn_s_setprio(0);
         }
+        // a wave with no blocks here still has its first copies in flight
+        // (clamped to a valid block); they must land before the merge
+        // reuses the ring's LDS
+        wait_vmcnt<0>();
       } else if constexpr (T::DOUBLE_BUF) {
         Buf<FMT, D> A, Bb;
         float sc[4];
@@ -424,7 +543,9 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
       }
     }
 
-    // ---- merge the 4 waves
+    // ---- merge the 4 waves (the workgroup waits on its barriers: above the
+    //      other workgroup's streaming waves, below a starting segment)
+    __builtin_amdgcn_s_setprio(2);
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
     if (lane < 16) {
@@ -455,7 +576,6 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
     __syncthreads();
 
     // ---- write: one wave per row
-    constexpr int E = D / 64;
     const bool direct = whole && a.write_direct;
     for (int row = wave; row < Rt; row += 4) {
       float M = NEG_INF;
@@ -553,16 +673,38 @@ __global__ __launch_bounds__(SG * D / 4) void decode_combine_kernel(DecodeArgs a
     l += w * ls;
     acc.x += w * o.x; acc.y += w * o.y; acc.z += w * o.z; acc.w += w * o.w;
   };
+  // up to KF partials in flight per thread: their loads go out together, so
+  // a unit split many ways costs about one memory round trip, not one per
+  // partial
+  constexpr int KF = 8;
   int s = g;
-  for (; s + SG < nseg; s += 2 * SG) {  // two partials in flight per thread
-    const float m0 = ml[s * sml], l0 = ml[s * sml + 1];
-    const float m1 = ml[(s + SG) * sml], l1 = ml[(s + SG) * sml + 1];
-    const float4 o0 = *reinterpret_cast<const float4*>(po + s * so);
-    const float4 o1 = *reinterpret_cast<const float4*>(po + (s + SG) * so);
-    take(m0, l0, o0);
-    take(m1, l1, o1);
+  for (; s + (KF - 1) * SG < nseg; s += KF * SG) {
+    float ms[KF], ls[KF];
+    float4 os[KF];
+#pragma unroll
+    for (int i = 0; i < KF; ++i) {
+      ms[i] = ml[(s + i * SG) * sml];
+      ls[i] = ml[(s + i * SG) * sml + 1];
+      os[i] = *reinterpret_cast<const float4*>(po + (s + i * SG) * so);
+    }
+#pragma unroll
+    for (int i = 0; i < KF; ++i) take(ms[i], ls[i], os[i]);
   }
-  if (s < nseg) take(ml[s * sml], ml[s * sml + 1], *reinterpret_cast<const float4*>(po + s * so));
+  {
+    float ms[KF - 1], ls[KF - 1];
+    float4 os[KF - 1];
+#pragma unroll
+    for (int i = 0; i < KF - 1; ++i) {
+      if (s + i * SG < nseg) {
+        ms[i] = ml[(s + i * SG) * sml];
+        ls[i] = ml[(s + i * SG) * sml + 1];
+        os[i] = *reinterpret_cast<const float4*>(po + (s + i * SG) * so);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < KF - 1; ++i)
+      if (s + i * SG < nseg) take(ms[i], ls[i], os[i]);
+  }
 
   sacc[g][c] = acc;
   if (c == 0) { sm[g] = m; sl[g] = l; }

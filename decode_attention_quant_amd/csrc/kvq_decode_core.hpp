@@ -173,16 +173,47 @@ __device__ __forceinline__ void copy_plane(uint32_t dst, const uint8_t* src, int
   }
 }
 
-// Start copying token block j into the stage at LDS byte address `stage`.
+// Start copying the token block at `ba` into the stage at LDS byte address
+// `stage`.
 template <int FMT, int D>
-__device__ __forceinline__ void stage_block(uint32_t stage, const uint8_t* head0, const Geometry& geo,
-                                            const cint32* bt_row, int j, int lane) {
+__device__ __forceinline__ void stage_block_at(uint32_t stage, const BlockAddr& ba, const Geometry& geo, int lane) {
   using T = DT<FMT, D>;
-  const BlockAddr ba = block_addr(head0, geo, bt_row, j);
   copy_plane<T::KB>(stage + T::SK, ba.hb + geo.off_kc + (int64_t)ba.bip * T::KB, lane);
   if constexpr (T::KSB > 0) copy_plane<T::KSB>(stage + T::SKS, ba.hb + geo.off_ks + (int64_t)ba.bip * T::KSB, lane);
   copy_plane<T::VB>(stage + T::SV, ba.hb + geo.off_vc + (int64_t)ba.bip * T::VB, lane);
   if constexpr (T::VSB > 0) copy_plane<T::VSB>(stage + T::SVS, ba.hb + geo.off_vs + (int64_t)ba.bip * T::VSB, lane);
+}
+
+// Start copying token block j into the stage at LDS byte address `stage`.
+template <int FMT, int D>
+__device__ __forceinline__ void stage_block(uint32_t stage, const uint8_t* head0, const Geometry& geo,
+                                            const cint32* bt_row, int j, int lane) {
+  stage_block_at<FMT, D>(stage, block_addr(head0, geo, bt_row, j), geo, lane);
+}
+
+// LDS accesses written in asm that waits for its own LDS counter.  While
+// global-to-LDS copies are in flight, the compiler puts a full vmcnt(0) in
+// front of every LDS access it emits (it cannot tell the copies' targets
+// apart), which would wait for all of them; these leave them in flight.
+__device__ __forceinline__ void lds_put4(uint32_t addr, float x0, float x1, float x2, float x3) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = {__float_as_uint(x0), __float_as_uint(x1), __float_as_uint(x2), __float_as_uint(x3)};
+  asm volatile("ds_write_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_put1(uint32_t addr, float x) {
+  asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(addr), "v"(__float_as_uint(x)) : "memory");
+}
+__device__ __forceinline__ void lds_get8(uint32_t addr, float (&x)[8]) {
+  uint4 lo, hi;
+  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:16\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(lo), "=&v"(hi) : "v"(addr) : "memory");
+  x[0] = __uint_as_float(lo.x); x[1] = __uint_as_float(lo.y); x[2] = __uint_as_float(lo.z); x[3] = __uint_as_float(lo.w);
+  x[4] = __uint_as_float(hi.x); x[5] = __uint_as_float(hi.y); x[6] = __uint_as_float(hi.z); x[7] = __uint_as_float(hi.w);
+}
+__device__ __forceinline__ float lds_get1(uint32_t addr) {
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(addr) : "memory");
+  return __uint_as_float(v);
 }
 
 // s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt fields at "no wait").

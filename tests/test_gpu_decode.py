@@ -162,6 +162,29 @@ def test_many_partials_per_unit_head_dim_128(nwg):
     assert_lse_close(lse.cpu().numpy(), ref_lse, "mxfp8 nwg=%d" % nwg)
 
 
+def test_combine_over_a_hundred_partials():
+    """One 60000-token sequence over 2 kv heads split 1024 ways: about 125
+    partials per unit, so the combine's threads each hold 8 partials in
+    flight (and the rest take the tail path)."""
+    c = W.make_case(1, "FP8_ROW", device="cpu", B=1, lengths=[60000])
+    bl = build(c)
+    ref, ref_lse = oracle_attention(bl)
+    q = c.q.cuda()
+    nwg = 1024
+    ws = kvq.alloc_workspace(kvq.workspace_size(bl.desc, c.B, c.n_q, c.H_q, c.max_pages, nwg))
+    ws.fill_(0xFF)
+    out = torch.full((c.B, c.n_q, c.H_q, c.D), float("nan"), device="cuda")
+    lse = torch.full((c.B, c.n_q, c.H_q), float("nan"), device="cuda")
+    note("combine many partials", "nwg", nwg)
+    kvq.decode_split(bl.desc, bl.pool_gpu, q, bl.bt, bl.sl, c.softmax_scale, ws, num_workgroups=nwg,
+                     flags=kvq.SPLIT_WRITE_WHOLE_UNITS, out=out, lse=lse)
+    kvq.decode_combine(bl.desc, c.B, c.n_q, c.H_q, c.max_pages, bl.sl, ws, out, lse, num_workgroups=nwg,
+                       flags=kvq.SPLIT_WRITE_WHOLE_UNITS)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), ref, "many partials")
+    assert_lse_close(lse.cpu().numpy(), ref_lse, "many partials")
+
+
 @pytest.mark.parametrize("fmt,cfg", [("NVFP4_G16", 3), ("FP8_ROW", 2), ("INT8_G64", 2), ("K8V4", 4), ("MXFP8", 5),
                                      ("BF16", 1)])
 def test_scores_that_climb_and_jump(fmt, cfg):

@@ -136,3 +136,44 @@ def test_fused_steps_in_a_row(fmt, cfg):
                            c.v_scale)
         c.seq_lens = c.seq_lens + 1
         c.reserve -= 1
+
+
+@pytest.mark.parametrize("fmt,cfg", [("NVFP4_G16", 3), ("MXFP8", 5), ("K8V4", 4), ("FP8_ROW", 2), ("INT8_G64", 2)])
+@pytest.mark.parametrize("nwg", [1, 3])
+def test_fused_step_with_long_ranges(fmt, cfg, nwg):
+    """Few split workgroups, so each wave walks tens of blocks and its block
+    holding the new tokens comes late in its ring (copied without a wait of
+    its own after the stores): pools byte-identical and outputs bit-identical
+    to append then decode with the same split."""
+    n_new = W.CONFIGS[cfg]["n_q"]
+    lens = [3001, 1500, 62] if cfg != 5 else [3001, 1500, 124, 2]
+    c = W.make_case(cfg, fmt, device="cpu", B=len(lens), lengths=lens, reserve=n_new)
+    bl = build(c, oracle=False)
+    k, v, slots = W.append_chunk(c, n_new)
+    sl_new = torch.as_tensor(c.seq_lens + n_new, dtype=torch.int32, device="cuda")
+    q = c.q.cuda()
+    B, n_q, H_q, D = q.shape
+    res = []
+    for fused in (False, True):
+        pool = bl.pool_gpu.clone()
+        ws = kvq.alloc_workspace(kvq.workspace_size(bl.desc, B, n_q, H_q, c.max_pages, nwg))
+        out = torch.full((B, n_q, H_q, D), float("nan"), device="cuda")
+        lse = torch.full((B, n_q, H_q), float("nan"), device="cuda")
+        note("long-range step", fmt, "nwg", nwg, "fused" if fused else "separate")
+        if fused:
+            kvq.decode_step_split(bl.desc, pool, k.view(B, n_q, c.H_kv, D).cuda(), v.view(B, n_q, c.H_kv, D).cuda(),
+                                  q, bl.bt, sl_new, c.softmax_scale, ws, num_workgroups=nwg,
+                                  flags=kvq.SPLIT_WRITE_WHOLE_UNITS, out=out, lse=lse)
+        else:
+            kvq.quantize_append(bl.desc, pool, k.cuda(), v.cuda(), slots.cuda())
+            kvq.decode_split(bl.desc, pool, q, bl.bt, sl_new, c.softmax_scale, ws, num_workgroups=nwg,
+                             flags=kvq.SPLIT_WRITE_WHOLE_UNITS, out=out, lse=lse)
+        kvq.decode_combine(bl.desc, B, n_q, H_q, c.max_pages, sl_new, ws, out, lse, num_workgroups=nwg,
+                           flags=kvq.SPLIT_WRITE_WHOLE_UNITS)
+        torch.cuda.synchronize()
+        res.append((out.cpu().numpy(), lse.cpu().numpy(), pool.cpu().numpy()))
+    (o0, l0, p0), (o1, l1, p1) = res
+    diff = np.flatnonzero(p0 != p1)
+    assert diff.size == 0, "%s: pools differ in %d bytes" % (fmt, diff.size)
+    assert np.array_equal(o0.view(np.uint32), o1.view(np.uint32)), "outputs differ " + fmt
+    assert np.array_equal(l0.view(np.uint32), l1.view(np.uint32)), "lse differ " + fmt
