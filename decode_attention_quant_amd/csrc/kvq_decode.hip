@@ -463,7 +463,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
         l_run += p[e];
       }
       const f16x4 P = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
-      if (t0 + 16 > L) clear_tail<FMT, D>(buf, L - t0, g);
+      if (__builtin_expect(t0 + 16 > L, 0)) clear_tail<FMT, D>(buf, L - t0, g);  // only the last block
       // keep the compiler from hoisting every V conversion ahead of the
       // products (it would hold all of them live and spill)
 #pragma unroll
