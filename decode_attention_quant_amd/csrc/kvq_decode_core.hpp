@@ -224,17 +224,20 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // Wait until every copy of a block is done when `after` blocks (wave-
-// uniform, < S) were staged behind it.
-template <int NDMA, int S>
+// uniform, < S) were staged behind it.  Copies complete in order, so
+// vmcnt(after * NDMA) suffices; a count past the counter's 6 bits waits at
+// 63, which is only more than needed.
+template <int NDMA, int S, int A = S - 1>
 __device__ __forceinline__ void wait_staged(int after) {
-  if constexpr (S > 3) {
-    if (after >= 3) { wait_vmcnt<3 * NDMA>(); return; }
+  if constexpr (A > 0) {
+    if (after >= A) {
+      wait_vmcnt<(A * NDMA < 63 ? A * NDMA : 63)>();
+      return;
+    }
+    wait_staged<NDMA, S, A - 1>(after);
+  } else {
+    wait_vmcnt<0>();
   }
-  if constexpr (S > 2) {
-    if (after >= 2) { wait_vmcnt<2 * NDMA>(); return; }
-  }
-  if (after >= 1) { wait_vmcnt<NDMA>(); return; }
-  wait_vmcnt<0>();
 }
 
 // NC 16-byte code chunks at c + i * CS (i < NC) and SW scale words at s
@@ -338,6 +341,13 @@ __device__ __forceinline__ void read_stage_v(Buf<FMT, D>& buf, uint32_t stage, i
   using T = DT<FMT, D>;
   const int g = lane >> 4;
   lds_read_part<T::VCH, 1024, T::VSW>(buf.v, buf.vs, stage + T::SV + lane * 16, stage + T::SVS + g * (4 * T::VSW));
+}
+
+// One 16-byte LDS write that waits for itself (see lds_read_part).
+__device__ __forceinline__ void lds_put16(uint32_t addr, uint4 v) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  asm volatile("ds_write_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(addr), "v"(w) : "memory");
 }
 
 // ----------------------------------------------------------- operand expanders

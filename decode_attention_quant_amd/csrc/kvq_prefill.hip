@@ -24,17 +24,24 @@
 
 namespace kvq {
 
-// The workgroup's block ring: up to 4 stages within 64 KB (two workgroups
-// per CU).  Outside the block loop the same area holds 8 fp32 rows of D per
-// wave.
+// The workgroup's block ring: up to 4 stages within 64 KB (deeper rings
+// measured slower).  V codes that need expanding (all but fp16 V) are
+// expanded once per block for the four waves: two buffers of f16 B operands
+// of the 16x16x16 P.V products, [pair of n-tiles][lane] 16 bytes each, after
+// the ring.  With them two workgroups fit a CU.  Outside the block loop the
+// same area holds 8 fp32 rows of D per wave.
 template <int FMT, int D>
 struct PT {
   using T = DT<FMT, D>;
   static constexpr int FIT = 64 * 1024 / T::STAGE;
   static constexpr int S = FIT > 4 ? 4 : FIT;
   static_assert(S >= 2, "the ring keeps a block in flight while one is read");
+  static constexpr bool VSH = T::VC != C_F16;
+  static_assert(!VSH || S >= 3, "blocks k (K) and k + 1 (V) are read while k + 2 is in flight");
+  static constexpr int VBUF = T::NT * 64 * 8;  // one block's f16 V operands
+  static constexpr int RING_BYTES = S * T::STAGE + (VSH ? 2 * VBUF : 0);
   static constexpr int ROWS_BYTES = 4 * 8 * D * 4;  // 8 fp32 rows per wave
-  static constexpr int AREA = S * T::STAGE > ROWS_BYTES ? S * T::STAGE : ROWS_BYTES;
+  static constexpr int AREA = RING_BYTES > ROWS_BYTES ? RING_BYTES : ROWS_BYTES;
   static constexpr int HDR_FLOATS = 256;  // per wave 16 m, 16 l, 16 q maxima (4 waves)
 };
 
@@ -171,24 +178,58 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(Geometry geo, DecodeArg
 #pragma unroll
   for (int nt = 0; nt < T::NT; ++nt) O[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   {
-    // wave 0 copies blocks 0 .. S - 2 ahead; in iteration k it waits for
-    // block k, the barrier publishes it (and every wave is then done with
-    // block k - 1), and wave 0 refills that stage with block k + S - 1
+    // Wave 0 copies blocks 0 .. S - 2 ahead, block k into stage k % S.
+    // Without shared V: in iteration k it waits for block k, the barrier
+    // publishes it (and every wave is then done with block k - 1), and wave
+    // 0 refills that stage with block k + S - 1.  With shared V, block k + 1
+    // is what wave 0 waits for: after the barrier every wave expands a
+    // quarter of block k + 1's V operands into buffer (k + 1) & 1, while the
+    // products of block k read K from its stage and V from buffer k & 1
+    // (filled the iteration before, published by this barrier).
     constexpr int S = PP::S;
+    const uint32_t vexp0 = ring0 + S * T::STAGE;
+    auto expand_v = [&](int kb) {
+      Buf<FMT, D> Vb;
+      read_stage_v<FMT, D>(Vb, ring0 + (kb % S) * T::STAGE, lane);
+      if (16 * kb + 16 > L) clear_tail<FMT, D>(Vb, L - 16 * kb, g);
+      const uint32_t dst = vexp0 + (kb & 1) * PP::VBUF;
+      constexpr int PER = T::NT / 4;  // n-tiles per wave (a constant index keeps Vb in registers)
+#pragma unroll
+      for (int nt = 0; nt < T::NT; nt += 2) {
+        if (nt / PER != wave) continue;  // wave-uniform
+        const f16x4 va = v_operand<FMT, D>(Vb, nt, lane), vb = v_operand<FMT, D>(Vb, nt + 1, lane);
+        lds_put16(dst + (uint32_t)(((nt >> 1) * 64 + lane) * 16),
+                  make_uint4(bitcast<uint2>(va).x, bitcast<uint2>(va).y, bitcast<uint2>(vb).x, bitcast<uint2>(vb).y));
+      }
+    };
     if (wave == 0) {
 #pragma unroll
       for (int k = 0; k < S - 1; ++k)
         if (k < nk) stage_block<FMT, D>(ring0 + k * T::STAGE, head0, geo, bt_row, k, lane);
     }
+    if constexpr (PP::VSH) {
+      if (nk > 0) {
+        if (wave == 0) wait_staged<T::NDMA, S>(min(S - 2, nk - 1));
+        __syncthreads();
+        expand_v(0);
+      }
+    }
     Buf<FMT, D> A;
     int st = 0;
     for (int k = 0; k < nk; ++k) {
-      if (wave == 0) wait_staged<T::NDMA, S>(min(S - 2, nk - 1 - k));
+      if constexpr (PP::VSH) {
+        if (wave == 0 && k + 1 < nk) wait_staged<T::NDMA, S>(min(S - 3, nk - 2 - k));
+      } else {
+        if (wave == 0) wait_staged<T::NDMA, S>(min(S - 2, nk - 1 - k));
+      }
       __syncthreads();
       if (wave == 0 && k + S - 1 < nk)
         stage_block<FMT, D>(ring0 + ((st + S - 1) % S) * T::STAGE, head0, geo, bt_row, k + S - 1, lane);
       const uint32_t stg = ring0 + st * T::STAGE;
       st = st + 1 == S ? 0 : st + 1;
+      if constexpr (PP::VSH) {
+        if (k + 1 < nk) expand_v(k + 1);
+      }
       if (!has_rows) continue;
       const int t0 = 16 * k;
       read_stage_k<FMT, D>(A, stg, lane);
@@ -198,7 +239,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(Geometry geo, DecodeArg
       float sc[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) sc[e] = (t0 + 4 * g + e <= limit) ? Sx[e] * crow : NEG_INF;
-      read_stage_v<FMT, D>(A, stg, lane);
+      if constexpr (!PP::VSH) read_stage_v<FMT, D>(A, stg, lane);
       // online softmax with the lazy running maximum (decode kernel's rule)
       const float bm = max_over_g(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
       if (__any(bm > m_run + RESCALE_SLACK)) {
@@ -222,11 +263,27 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(Geometry geo, DecodeArg
         l_run += p[e];
       }
       const f16x4 P = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
-      if (t0 + 16 > L) clear_tail<FMT, D>(A, L - t0, g);
+      if constexpr (PP::VSH) {
+        const uint32_t src = vexp0 + (k & 1) * PP::VBUF + lane * 16;
 #pragma unroll
-      for (int nt = 0; nt < T::NT; ++nt) {
-        if ((nt & 3) == 0) __builtin_amdgcn_sched_barrier(0);
-        O[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(P, v_operand<FMT, D>(A, nt, lane), O[nt], 0, 0, 0);
+        for (int h = 0; h < T::NT / 8; ++h) {  // 8 n-tiles (4 pairs) per read
+          uint4 v4[4];
+          uint32_t none[1];
+          lds_read_part<4, 1024, 0>(v4, none, src + h * 4096, 0);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const uint2 w = (i & 1) ? make_uint2(v4[i >> 1].z, v4[i >> 1].w) : make_uint2(v4[i >> 1].x, v4[i >> 1].y);
+            O[8 * h + i] = __builtin_amdgcn_mfma_f32_16x16x16f16(P, bitcast<f16x4>(w), O[8 * h + i], 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+        if (t0 + 16 > L) clear_tail<FMT, D>(A, L - t0, g);
+#pragma unroll
+        for (int nt = 0; nt < T::NT; ++nt) {
+          if ((nt & 3) == 0) __builtin_amdgcn_sched_barrier(0);
+          O[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(P, v_operand<FMT, D>(A, nt, lane), O[nt], 0, 0, 0);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
