@@ -17,7 +17,12 @@ int8_g64       8       per 64 consecutive values: s = f16(amax / 127),
 e4m3_row       8       one FP16 scale per row: s = f16(amax / 448),
                        c = E4M3(x / s)
 e2m1_g16       4       per 16 values: s = UE4M3(amax / 6), c = E2M1(x / s);
-                       K and V rotated first (NVFP4-G16 entry)
+                       K and V rotated first (NVFP4-G16 entry).  Two-level
+                       form: x is first divided by a per-tensor fp32 scale
+                       g (IEEE fp32), so values decode to g * s * c; g = 1
+                       is the single-level format (the NVFP4 checkpoints the
+                       pages mention pair the 16-value FP8 scales with one
+                       fp32 scale per tensor)
 e4m3_mx32      8       per 32 values: one UE8M0 byte (OCP MX rule),
                        c = E4M3(x / 2^(byte-127)) (TokenSpeed ``mxfp8``)
 e4m3_tensor    8       c = E4M3(x / s) with one fp32 scale per tensor from
@@ -127,6 +132,11 @@ def encode_rows(codec, rotated, rows, tensor_scale=1.0):
         c = np.where(s32 == 0, np.uint8(0), S.e4m3_encode(np.where(s32 == 0, 0, q)))
         return c.reshape(x.shape).astype(np.uint8), sbits
     if codec == "e2m1_g16":
+        g = np.float32(tensor_scale)
+        assert g > 0
+        x = (x / g).astype(np.float32)  # exact when g = 1
+        xg = _group_view(x, codec)
+        amax = np.max(np.abs(xg), axis=-1)
         sb = S.ue4m3_encode((amax / np.float32(6.0)).astype(np.float32))
         s32 = S.e4m3_decode(sb).astype(np.float32)[..., None]
         with np.errstate(divide="ignore", invalid="ignore"):
@@ -171,6 +181,8 @@ def decode_rows(codec, rotated, codes, scales, tensor_scale=1.0, stored_domain=F
             s = S.ue8m0_decode(scales)
         cg = _group_view(c, codec)
         v = (cg * s[..., None]).reshape(c.shape)
+        if codec == "e2m1_g16":
+            v = v * float(np.float32(tensor_scale))  # the two-level form's per-tensor scale
     if rotated and not stored_domain:
         v = unrotate_f64(v)
     return v

@@ -194,6 +194,58 @@ def test_fp8_tensor_unit_scale_is_plain_e4m3():
     assert np.array_equal(c, S.e4m3_encode(x))
 
 
+# ------------------------------------------------- two-level NVFP4 (fp32 per-tensor scale)
+
+@pytest.mark.parametrize("rotated", [False, True])
+def test_two_level_nvfp4_power_of_two_scale_is_an_exact_rescaling(rotated):
+    """Dividing by a global scale 2^-5 first is the same as encoding x * 2^5
+    with no global scale: same code and block-scale bytes (a misplaced scale,
+    say applied after the block scale, or multiplied, breaks this)."""
+    rng = np.random.default_rng(31)
+    x = (rng.standard_normal((16, 256)) * 0.05).astype(np.float32)
+    c2, s2 = F.encode_rows("e2m1_g16", rotated, x, tensor_scale=2.0 ** -5)
+    c1, s1 = F.encode_rows("e2m1_g16", rotated, (x * np.float32(32.0)).astype(np.float32), tensor_scale=1.0)
+    assert np.array_equal(c2, c1) and np.array_equal(s2, s1)
+    # and the decoded values carry the global scale back
+    v2 = F.decode_rows("e2m1_g16", rotated, c2, s2, tensor_scale=2.0 ** -5)
+    v1 = F.decode_rows("e2m1_g16", rotated, c1, s1, tensor_scale=1.0)
+    assert np.allclose(v2, v1 / 32.0, rtol=0, atol=1e-12)
+
+
+def test_two_level_nvfp4_round_trip_with_a_non_power_of_two_scale():
+    """x = g * s_b * c built from codes, block scales (each group holding a
+    +-6 code, so amax / 6 = s_b) and g = 3: encoding with g and decoding give
+    x back exactly."""
+    rng = np.random.default_rng(32)
+    n, D, g = 8, 256, np.float32(3.0)
+    c = S.e2m1_decode(rng.integers(0, 16, (n, D)))
+    c = c.reshape(n, D // 16, 16)
+    c[:, :, 0] = np.where(rng.integers(0, 2, (n, D // 16)) > 0, 6.0, -6.0)
+    sb = S.e4m3_decode(rng.integers(0x08, 0x60, (n, D // 16)).astype(np.uint8))
+    x = (g * sb[..., None] * c).reshape(n, D).astype(np.float32)
+    assert np.array_equal(x.astype(np.float64), (3.0 * sb[..., None] * c).reshape(n, D))  # exact in fp32
+    codes, scales = F.encode_rows("e2m1_g16", False, x, tensor_scale=float(g))
+    back = F.decode_rows("e2m1_g16", False, codes, scales, tensor_scale=float(g))
+    assert np.array_equal(back, x.astype(np.float64))
+    assert np.array_equal(S.e4m3_decode(scales), sb)
+
+
+def test_two_level_nvfp4_global_scale_from_the_tensor_max_keeps_block_scales_in_range():
+    """With g = amax / (6 * 448) over the (rotated) tensor, no block scale
+    saturates and the group holding the maximum uses the top of the UE4M3
+    range, which is what the second level is for."""
+    rng = np.random.default_rng(33)
+    x = (rng.standard_normal((64, 256)) * 1e3).astype(np.float32)
+    amax = np.float32(np.abs(Hd.fwht256_f32(x)).max())
+    g = float(np.float32(amax / np.float32(6.0 * 448.0)))
+    codes, scales = F.encode_rows("e2m1_g16", True, x, tensor_scale=g)
+    sv = S.e4m3_decode(scales)
+    assert sv.max() <= 448.0 and sv.max() >= 256.0
+    # without the second level, these values saturate the block scales
+    _, s1 = F.encode_rows("e2m1_g16", True, x, tensor_scale=1.0)
+    assert S.e4m3_decode(s1).max() == 448.0
+
+
 # ------------------------------------------------------------------ layout
 
 @pytest.mark.parametrize("bits,D", [(16, 256), (16, 128), (8, 256), (8, 128), (4, 256)])
