@@ -59,7 +59,7 @@ FLUSH_BYTES = 1 << 30          # read before each timed step: 4x the 256 MB MALL
 RATE_BYTES = 4 << 30           # buffer of the streaming-rate measurement
 COPY_BYTES = RATE_BYTES // 2   # bytes each way of the probe's copy
 APPEND_CHUNK = 2048
-APPEND_FORMATS = ["K8V4", "BF16", "INT8_G64", "FP8_ROW", "NVFP4_G16", "FP8_TENSOR"]
+APPEND_FORMATS = ["K8V4", "BF16", "INT8_G64", "FP8_ROW", "NVFP4_G16", "FP8_TENSOR", "NVFP4_G16/2L"]
 CSRC = os.path.join(ROOT, "decode_attention_quant_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_traffic.json")
 METRIC = "decode-attn effective KV GB/s (% of HBM peak) per kv-dtype; quant-append tok/s"
@@ -68,7 +68,7 @@ WORKLOADS = {
     "batched": dict(config=2, formats=["INT8_G64", "FP8_ROW", "FP8_TENSOR"],
                     label="batched decode: 32 sequences x U[8192,32768] cached tokens, 24 q / 4 kv heads, "
                           "head_dim 256, 64-token pages"),
-    "long": dict(config=3, formats=["NVFP4_G16"],
+    "long": dict(config=3, formats=["NVFP4_G16", "NVFP4_G16/2L"],
                  label="long-context decode: 1 sequence x 262144 tokens, 24 q / 4 kv heads, head_dim 256"),
     "long8": dict(config="3b", formats=["NVFP4_G16"],
                   label="long-context decode: 8 sequences x 65536 tokens, 24 q / 4 kv heads, head_dim 256"),
@@ -81,6 +81,13 @@ WORKLOADS = {
                  label="tiny decode: 1 sequence x 1024 tokens, 4 q / 2 kv heads, head_dim 256"),
 }
 
+def parse_label(label):
+    """'NVFP4_G16/2L' -> ('NVFP4_G16', True): a format, and whether its NVFP4
+    planes take a calibrated per-tensor (second-level) scale."""
+    fmt, _, mod = label.partition("/")
+    return fmt, mod == "2L"
+
+
 def kv_bytes_per_token(d):
     return kvq.page_bytes(d) // (d.page_size * d.num_kv_heads)
 
@@ -88,8 +95,9 @@ def kv_bytes_per_token(d):
 class Setup:
     """One workload resident on the GPU: pool, tables, and the step's inputs."""
 
-    def __init__(self, config, fmt):
-        self.case = c = W.make_case(config, fmt, device="cuda")
+    def __init__(self, config, label):
+        fmt, two_level = parse_label(label)
+        self.case = c = W.make_case(config, fmt, device="cuda", two_level=two_level)
         self.desc = kvq.desc(c.fmt, c.D, c.P, c.H_kv, c.num_pages, c.k_scale, c.v_scale)
         self.pool = kvq.alloc_pool(self.desc)
         kvq.quantize_append(self.desc, self.pool, c.k, c.v, c.slot_mapping)  # fill the cache
@@ -216,11 +224,12 @@ def append_chunk_bench(formats, stream, probe, reps=10):
     workload (64 sequences, chunks starting mid-page): tok/s and GB/s moved,
     against the HBM roof T * H_kv * (4 D + bytes_per_token) / 8 TB/s."""
     res = {}
-    for fmt in formats:
-        c = W.make_case(4, fmt, device="cuda", reserve=APPEND_CHUNK)
+    for label in formats:
+        fmt, two_level = parse_label(label)
+        c = W.make_case(4, fmt, device="cuda", reserve=APPEND_CHUNK, two_level=two_level)
         c.k = c.v = None  # only the new chunk is written
         d = kvq.desc(c.fmt, c.D, c.P, c.H_kv, c.num_pages, 1.0, 1.0)
-        if fmt == "FP8_TENSOR":  # the cached tensors' calibrated scales
+        if fmt == "FP8_TENSOR" or two_level:  # the cached tensors' calibrated scales
             d = kvq.desc(c.fmt, c.D, c.P, c.H_kv, c.num_pages, c.k_scale, c.v_scale)
         pool = kvq.alloc_pool(d)
         k, v, slots = W.append_chunk(c, APPEND_CHUNK, device="cuda")
@@ -240,10 +249,10 @@ def append_chunk_bench(formats, stream, probe, reps=10):
             torch.cuda.synchronize()
         ms = float(np.median([e[0].elapsed_time(e[1]) for e in ts]))
         roof = HBM_PEAK_GBS * 1e9 / (c.H_kv * (4 * c.D + bpt))
-        res[fmt] = {"tokens": T, "ms": ms, "tok_per_s": T / (ms * 1e-3), "GB_per_s": moved / (ms * 1e-3) / 1e9,
+        res[label] = {"tokens": T, "ms": ms, "tok_per_s": T / (ms * 1e-3), "GB_per_s": moved / (ms * 1e-3) / 1e9,
                     "roof_tok_per_s": roof, "frac_of_roof": T / (ms * 1e-3) / roof}
         print("[bench] append %s: %d tokens in %.3f ms, %.1f M tok/s (%.1f%% of the HBM roof), %.0f GB/s" % (
-            fmt, T, ms, T / ms / 1e3, 100 * res[fmt]["frac_of_roof"], res[fmt]["GB_per_s"]),
+            label, T, ms, T / ms / 1e3, 100 * res[label]["frac_of_roof"], res[label]["GB_per_s"]),
             file=sys.stderr, flush=True)
         del pool, k, v, slots, c
         torch.cuda.empty_cache()

@@ -19,10 +19,8 @@ kvq_status check_desc(const kvq_cache_desc* d) {
   if (d->format < 0 || d->format >= F_COUNT) return KVQ_ERR_INVALID_ARGUMENT;
   if (d->num_kv_heads < 1 || d->num_pages < 1 || d->head_dim < 1 || d->page_size < 1) return KVQ_ERR_INVALID_ARGUMENT;
   if (!supported(d->format, d->head_dim, d->page_size)) return KVQ_ERR_UNSUPPORTED;
-  if (d->format == F_FP8_TENSOR) {
-    if (!(d->k_scale > 0.0f) || !(d->v_scale > 0.0f) || !isfinite(d->k_scale) || !isfinite(d->v_scale))
-      return KVQ_ERR_INVALID_ARGUMENT;
-  }
+  if (k_tensor_scaled(d->format) && (!(d->k_scale > 0.0f) || !isfinite(d->k_scale))) return KVQ_ERR_INVALID_ARGUMENT;
+  if (v_tensor_scaled(d->format) && (!(d->v_scale > 0.0f) || !isfinite(d->v_scale))) return KVQ_ERR_INVALID_ARGUMENT;
   return KVQ_OK;
 }
 
@@ -97,8 +95,8 @@ DecodeArgs base_args(const kvq_cache_desc* d, const Plan& p, int32_t batch, int3
   a.seq_lens = seq_lens;
   a.B = batch; a.n_q = n_q; a.H_q = H_q; a.G = H_q / d->num_kv_heads; a.R = p.R;
   a.max_pages = max_pages; a.nwg = p.nwg;
-  a.qk_scale = softmax_scale * 1.4426950408889634f * (d->format == F_FP8_TENSOR ? d->k_scale : 1.0f);
-  a.v_out_scale = d->format == F_FP8_TENSOR ? d->v_scale : 1.0f;
+  a.qk_scale = softmax_scale * 1.4426950408889634f * (k_tensor_scaled(d->format) ? d->k_scale : 1.0f);
+  a.v_out_scale = v_tensor_scaled(d->format) ? d->v_scale : 1.0f;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   a.ws_cum = reinterpret_cast<int32_t*>(ws);
   a.ws_ml = reinterpret_cast<float*>(ws + p.cum_bytes);
@@ -310,8 +308,8 @@ kvq_status kvq_prefill_attention(const kvq_cache_desc* desc, const void* pool, c
   a.seq_lens = seq_lens;
   a.B = batch; a.n_q = n_q; a.H_q = num_q_heads; a.G = (int32_t)G; a.R = (int32_t)R;
   a.max_pages = max_pages_per_seq;
-  a.qk_scale = softmax_scale * 1.4426950408889634f * (desc->format == F_FP8_TENSOR ? desc->k_scale : 1.0f);
-  a.v_out_scale = desc->format == F_FP8_TENSOR ? desc->v_scale : 1.0f;
+  a.qk_scale = softmax_scale * 1.4426950408889634f * (k_tensor_scaled(desc->format) ? desc->k_scale : 1.0f);
+  a.v_out_scale = v_tensor_scaled(desc->format) ? desc->v_scale : 1.0f;
   a.out = out;
   a.lse = lse;
   return hip_status(launch_prefill(geo_of(desc), a, stream));

@@ -47,7 +47,7 @@ __device__ __forceinline__ float stored_value(const uint8_t* codes, const uint8_
     const float s = e4m3_value(scales[pos]);
     const float mag[8] = {0.f, 0.5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f};
     const float c = (code & 8) ? -mag[code & 7] : mag[code & 7];
-    return c * s;
+    return c * s * tensor_scale;  // exact: the two-level form's scale, 1 for single level
   } else {  // C_E4MX
     return ldexpf(e4m3_value(code), (int)scales[t * G + grp] - 127);
   }

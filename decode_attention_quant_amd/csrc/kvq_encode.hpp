@@ -301,6 +301,19 @@ __device__ __forceinline__ void store_k_codes(uint8_t* codes, const uint32_t* w,
   }
 }
 
+// Two-level NVFP4: the (rotated) row is divided by the per-tensor scale g
+// before its groups are scaled, in IEEE fp32 (div_scale's quotient is the
+// IEEE one wherever it can reach a code or a group maximum that is not
+// flushed to a zero scale); g = 1 leaves the row unchanged.
+template <int N>
+__device__ __forceinline__ void divide_by_tensor_scale(float (&x)[N], float g) {
+  if (g == 1.0f) return;  // uniform
+  const float r = __fdiv_rn(1.0f, g);
+  const bool fast = g >= 0x1p-30f && g <= 0x1p30f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = fast ? div_scale(x[i], g, r) : __fdiv_rn(x[i], g);
+}
+
 // ---------------------------------------------------------------- one plane
 
 template <int C, int D, bool ROT, int PLANE>
@@ -312,6 +325,7 @@ __device__ __forceinline__ void encode_plane(float (&x)[D / 4], int q, uint8_t* 
     static_assert(D == 256, "the rotation is 256-point");
     fwht256_quad(x, q);
   }
+  if constexpr (C == C_E2G16) divide_by_tensor_scale(x, tensor_scale);
   Codes<C, E> out;
   if constexpr (C == C_F16) {
 #pragma unroll
@@ -532,6 +546,10 @@ __device__ __forceinline__ void v_row_group(uint8_t* __restrict__ pool, const ui
       static_assert(D == 256, "the rotation is 256-point");
       fwht256_row16(x[0], j);
       fwht256_row16(x[1], j);
+    }
+    if constexpr (C == C_E2G16) {
+      divide_by_tensor_scale(x[0], v_scale);
+      divide_by_tensor_scale(x[1], v_scale);
     }
     if constexpr (C == C_F16) {
 #pragma unroll

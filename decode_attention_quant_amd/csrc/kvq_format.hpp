@@ -74,6 +74,10 @@ KVQ_HD constexpr int v_codec(int f) {
 }
 KVQ_HD constexpr bool k_rotated(int f) { return f == F_INT8_G64 || f == F_NVFP4_G16; }
 KVQ_HD constexpr bool v_rotated(int f) { return f == F_NVFP4_G16 || f == F_K8V4; }
+// Planes with a per-tensor fp32 scale (the descriptor's k_scale / v_scale):
+// FP8-tensor, and the two-level form of the NVFP4 planes (1 = single level).
+KVQ_HD constexpr bool k_tensor_scaled(int f) { return f == F_FP8_TENSOR || f == F_NVFP4_G16; }
+KVQ_HD constexpr bool v_tensor_scaled(int f) { return f == F_FP8_TENSOR || f == F_NVFP4_G16 || f == F_K8V4; }
 
 KVQ_HD constexpr int codec_bits(int c) { return (c == C_BF16 || c == C_F16) ? 16 : c == C_E2G16 ? 4 : 8; }
 // group size along head_dim (0 = no per-row scales; -1 = whole row)

@@ -57,6 +57,7 @@ typedef enum kvq_status {
  *  KVQ_INT8_G64    int8 + fp16 scale per 64 values, K rot | same, V not rot   [528]
  *  KVQ_FP8_ROW     E4M3 + one fp16 scale per row | same            [516]
  *  KVQ_NVFP4_G16   E2M1 + UE4M3 scale per 16, rot | same, rot      [288]
+ *                  (two-level: x / k_scale, x / v_scale first)
  *  KVQ_K8V4        K as FP8_ROW | V as NVFP4_G16 (rot)             [402]
  *  KVQ_MXFP8       E4M3 + UE8M0 scale per 32 | same                [528; 264 at D=128]
  *  KVQ_FP8_TENSOR  E4M3 of x / k_scale | E4M3 of x / v_scale       [512]
@@ -82,8 +83,16 @@ typedef enum kvq_format {
  *  page_size     tokens per page: 64 or 128 (the pages use 64, and 128 for mxfp8).
  *  num_kv_heads  H_kv >= 1.
  *  num_pages     pages in the pool (> 0).
- *  k_scale, v_scale  FP8_TENSOR only: the per-tensor fp32 scales (> 0,
- *                finite); 1.0 is the "unit scale".  Ignored otherwise.
+ *  k_scale, v_scale  per-tensor fp32 scales (> 0, finite) of the K / V
+ *                planes that have one, ignored for the others:
+ *                FP8_TENSOR: E4M3 of x / scale; 1.0 is the "unit scale".
+ *                NVFP4_G16 (K and V) and K8V4 (V): the second level of
+ *                two-level NVFP4, one fp32 scale per tensor above the
+ *                16-value UE4M3 ones (a reading: the pages give NVFP4's
+ *                16-value groups and leave any higher level open): the
+ *                rotated row is divided by it in IEEE fp32 before its
+ *                group scales are taken, and decoding multiplies it back.
+ *                1.0 is the single-level format.
  */
 typedef struct kvq_cache_desc {
   int32_t format;

@@ -20,9 +20,9 @@ e2m1_g16       4       per 16 values: s = UE4M3(amax / 6), c = E2M1(x / s);
                        K and V rotated first (NVFP4-G16 entry).  Two-level
                        form: x is first divided by a per-tensor fp32 scale
                        g (IEEE fp32), so values decode to g * s * c; g = 1
-                       is the single-level format (the NVFP4 checkpoints the
-                       pages mention pair the 16-value FP8 scales with one
-                       fp32 scale per tensor)
+                       is the single-level format (a reading: the pages
+                       give NVFP4's 16-value groups and leave any level
+                       above them open)
 e4m3_mx32      8       per 32 values: one UE8M0 byte (OCP MX rule),
                        c = E4M3(x / 2^(byte-127)) (TokenSpeed ``mxfp8``)
 e4m3_tensor    8       c = E4M3(x / s) with one fp32 scale per tensor from

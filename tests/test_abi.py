@@ -71,10 +71,16 @@ def test_desc_validation():
         (kvq.desc(6, 256, 64, 2, 4, 0.0, 1.0), 1),            # tensor scale must be > 0
         (kvq.desc(6, 256, 64, 2, 4, 1.0, float("inf")), 1),
         (kvq.desc(6, 256, 64, 2, 4, float("nan"), 1.0), 1),
+        (kvq.desc(3, 256, 64, 2, 4, 0.0, 1.0), 1),            # two-level NVFP4: both scales > 0
+        (kvq.desc(3, 256, 64, 2, 4, 1.0, -2.0), 1),
+        (kvq.desc(4, 256, 64, 2, 4, 1.0, float("nan")), 1),   # K8V4: its NVFP4 V scale
     ]
     for d, want in bad:
         assert _status("kvq_page_bytes", ctypes.byref(d), ctypes.byref(out)) == want
     assert _status("kvq_page_bytes", None, ctypes.byref(out)) == 1
+    # scales a format does not use are ignored (K8V4's FP8-row K, FP8-row)
+    for d in (kvq.desc(4, 256, 64, 2, 4, -5.0, 1.0), kvq.desc(2, 256, 64, 2, 4, 0.0, float("nan"))):
+        assert _status("kvq_page_bytes", ctypes.byref(d), ctypes.byref(out)) == 0
     d = kvq.desc(0, 256, 64, 2, 4)
     assert _status("kvq_page_bytes", ctypes.byref(d), None) == 1
 

@@ -15,7 +15,10 @@ Recipe:
 * K's 4 special channels are multiplied by 20 (configs 1-4: "outlier
   channels") or replaced by Student-t(3) draws (config 5);
 * the softmax scale is 1 / sqrt(head_dim);
-* the per-tensor FP8 scale, when calibrated, is fl32(amax|tensor| / 448).
+* the per-tensor FP8 scale, when calibrated, is fl32(amax|tensor| / 448);
+  the per-tensor scale of two-level NVFP4 planes, when asked for, is
+  fl32(amax|tensor| / 2688) (6 x 448: the largest E2M1 code times the largest
+  UE4M3 scale).
 
 The shapes come from the decode scenarios the pages discuss: GQA with 24
 query / 4 KV heads at head_dim 256 and long contexts (NInfer guide, Qwen
@@ -97,13 +100,15 @@ def _bf16_normal(shape, gen, device):
 
 
 def make_case(config, fmt, device="cpu", B=None, lengths=None, n_q=None, extra_pages=0,
-              calibrate_tensor_scale=True, reserve=0):
+              calibrate_tensor_scale=True, reserve=0, two_level=False):
     """Draw one decode workload.
 
     ``B``/``lengths`` override the config's batch and lengths (lengths may be
     an explicit list, or a spec tuple) so that the same recipe yields small
     cases the oracle finishes quickly.  ``reserve`` extra token slots per
     sequence are given pages (for later appends) without being drawn.
+    ``two_level`` calibrates the per-tensor scales of the NVFP4 planes
+    (NVFP4_G16's K and V, K8V4's V).
     """
     cfg = CONFIGS[config]
     fmt_id = FORMAT_IDS[fmt] if isinstance(fmt, str) else int(fmt)
@@ -149,6 +154,10 @@ def make_case(config, fmt, device="cpu", B=None, lengths=None, n_q=None, extra_p
     if fmt_id == FORMAT_IDS["FP8_TENSOR"] and calibrate_tensor_scale and T:
         k_scale = float(np.float32(k.float().abs().max().item()) / np.float32(448.0))
         v_scale = float(np.float32(v.float().abs().max().item()) / np.float32(448.0))
+    if two_level and T and fmt_id in (FORMAT_IDS["NVFP4_G16"], FORMAT_IDS["K8V4"]):
+        if fmt_id == FORMAT_IDS["NVFP4_G16"]:
+            k_scale = float(np.float32(k.float().abs().max().item()) / np.float32(2688.0))
+        v_scale = float(np.float32(v.float().abs().max().item()) / np.float32(2688.0))
     return Case(config, fmt_id, D, P, B, H_q, H_kv, n_q, lens.astype(np.int32), bt, total,
                 q, k, v, torch.as_tensor(slots.astype(np.int32), device=device),
                 1.0 / math.sqrt(D), k_scale, v_scale, seq, pos, reserve)
