@@ -25,6 +25,11 @@ e2m1_g16       4       per 16 values: s = UE4M3(amax / 6), c = E2M1(x / s);
                        above them open)
 e4m3_mx32      8       per 32 values: one UE8M0 byte (OCP MX rule),
                        c = E4M3(x / 2^(byte-127)) (TokenSpeed ``mxfp8``)
+e2m1_mx32      4       per 32 values: one UE8M0 byte (OCP MX rule with E2M1's
+                       largest exponent 2), c = E2M1(x / 2^(byte-127)),
+                       saturating; K and V rotated first (MXFP4 KV: the
+                       pages' mxfp4 micro-scaling format applied to the cache,
+                       rotated like their NVFP4 KV; a reading)
 e4m3_tensor    8       c = E4M3(x / s) with one fp32 scale per tensor from
                        the caller (Qwen FP8-KV article: per-tensor
                        symmetric ``kv_cache_scheme``; TokenSpeed
@@ -52,6 +57,7 @@ CODECS = {
     "e4m3_row": (8, "row", "f16"),
     "e2m1_g16": (4, 16, "ue4m3"),
     "e4m3_mx32": (8, 32, "ue8m0"),
+    "e2m1_mx32": (4, 32, "ue8m0"),
     "e4m3_tensor": (8, None, None),
 }
 SCALE_BYTES = {None: 0, "f16": 2, "ue4m3": 1, "ue8m0": 1}
@@ -65,6 +71,7 @@ FORMATS = {
     4: ("K8V4", "e4m3_row", "e2m1_g16", False, True),
     5: ("MXFP8", "e4m3_mx32", "e4m3_mx32", False, False),
     6: ("FP8_TENSOR", "e4m3_tensor", "e4m3_tensor", False, False),
+    7: ("MXFP4", "e2m1_mx32", "e2m1_mx32", True, True),
 }
 FORMAT_IDS = {v[0]: k for k, v in FORMATS.items()}
 
@@ -143,6 +150,11 @@ def encode_rows(codec, rotated, rows, tensor_scale=1.0):
             q = (xg / s32).astype(np.float32)
         c = np.where(s32 == 0, np.uint8(0), S.e2m1_encode(np.where(s32 == 0, 0, q)))
         return c.reshape(x.shape).astype(np.uint8), sb
+    if codec == "e2m1_mx32":
+        sb = S.ue8m0_from_amax(amax, emax=2)
+        X = S.ue8m0_decode(sb).astype(np.float32)[..., None]  # exact powers of two
+        q = (xg / X).astype(np.float32)
+        return S.e2m1_encode(q).reshape(x.shape).astype(np.uint8), sb
     if codec == "e4m3_mx32":
         sb = S.ue8m0_from_amax(amax)
         X = S.ue8m0_decode(sb).astype(np.float32)[..., None]  # exact powers of two
@@ -169,7 +181,7 @@ def decode_rows(codec, rotated, codes, scales, tensor_scale=1.0, stored_domain=F
         bits, group, stype = CODECS[codec]
         if codec == "int8_g64":
             c = codes.astype(np.uint8).view(np.int8).astype(np.float64)
-        elif codec == "e2m1_g16":
+        elif codec in ("e2m1_g16", "e2m1_mx32"):
             c = S.e2m1_decode(codes)
         else:
             c = S.e4m3_decode(codes)

@@ -122,7 +122,7 @@ def scale_pos(codec, plane, D, t, grp):
     grp = np.asarray(grp)
     if stype == "f16":
         return (t * G + grp) * 2
-    if stype == "ue4m3" and plane == "V":
+    if F.CODECS[codec][0] == 4 and plane == "V":  # 4-bit V: a group's 4 tokens together
         return (t // 4) * 4 * G + grp * 4 + (t % 4)
     return t * G + grp
 

@@ -137,18 +137,19 @@ def e2m1_encode(x):
 
 # ----------------------------------------------------------------- UE8M0
 
-def ue8m0_from_amax(amax):
+def ue8m0_from_amax(amax, emax=8):
     """Shared exponent byte of an MX block (TokenSpeed ``mxfp8``: one UE8M0
-    scale per 32 head_dim elements).
+    scale per 32 head_dim elements; ``mxfp4``: the 4-bit micro-scaling format).
 
     The page only names the scale type; the rule is the public OCP MX one:
-    X = 2^(floor(log2 amax) - emax) with emax = 8 for E4M3, stored biased
-    by 127 and clamped to [0, 254].  amax = 0 gives byte 0.
-    floor(log2 amax) comes from frexp, which is exact.
+    X = 2^(floor(log2 amax) - emax) with emax the element format's largest
+    exponent (8 for E4M3, 2 for E2M1), stored biased by 127 and clamped to
+    [0, 254].  amax = 0 gives byte 0.  floor(log2 amax) comes from frexp,
+    which is exact.
     """
     a = np.asarray(amax, dtype=np.float32).astype(np.float64)
     mant, ex = np.frexp(np.where(a > 0, a, 1.0))
-    b = np.clip(ex - 1 - 8 + 127, 0, 254)
+    b = np.clip(ex - 1 - emax + 127, 0, 254)
     return np.where(a > 0, b, 0).astype(np.uint8)
 
 

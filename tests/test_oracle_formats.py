@@ -58,7 +58,14 @@ def test_m_kv_formula_for_bf16_pool():
     assert pages * geo.page_bytes == 2 * B * layers * H_kv * S_ * d * 2
 
 
-@pytest.mark.parametrize("fmt", range(7))
+def test_mxfp4_bytes_per_token():
+    """E2M1 codes plus one UE8M0 byte per 32 values, K and V: 2 (128 + 8) =
+    272 B per token and kv head at head_dim 256, below NVFP4's 288."""
+    assert F.token_bytes(F.FORMAT_IDS["MXFP4"], 256) == 272
+    assert F.token_bytes(F.FORMAT_IDS["MXFP4"], 256) < F.token_bytes(F.FORMAT_IDS["NVFP4_G16"], 256)
+
+
+@pytest.mark.parametrize("fmt", range(8))
 @pytest.mark.parametrize("P", [64, 128])
 def test_page_is_exactly_per_token_bytes(fmt, P):
     D = 128 if fmt == 5 else 256
@@ -84,6 +91,12 @@ def _grid_values(codec, rng, n, D):
         c = S.e2m1_decode(rng.integers(0, 16, (n, D)))
         qmax = 6.0
         s = S.e4m3_decode(rng.integers(8, 100, (n, D // g)))
+    elif codec == "e2m1_mx32":
+        c = S.e2m1_decode(rng.integers(0, 16, (n, D)))
+        s = np.exp2(rng.integers(-20, 10, (n, D // g)).astype(np.float64))
+        cg = c.reshape(n, D // g, g)
+        cg[..., 0] = rng.choice([4.0, 6.0], (n, D // g))  # amax / X in [4, 8): the exponent the MX rule picks
+        return (cg * s[..., None]).reshape(n, D).astype(np.float32), c, s
     else:  # e4m3_mx32
         c = S.e4m3_decode(rng.integers(0, 127, (n, D))) * rng.choice([-1, 1], (n, D))
         s = np.exp2(rng.integers(-20, 10, (n, D // g)).astype(np.float64))
@@ -95,7 +108,7 @@ def _grid_values(codec, rng, n, D):
     return (cg * s[..., None]).reshape(n, D).astype(np.float32), c, s
 
 
-@pytest.mark.parametrize("codec", ["int8_g64", "e4m3_row", "e2m1_g16", "e4m3_mx32"])
+@pytest.mark.parametrize("codec", ["int8_g64", "e4m3_row", "e2m1_g16", "e4m3_mx32", "e2m1_mx32"])
 def test_round_trip_of_representable_rows(codec):
     rng = np.random.default_rng(21)
     x, c, s = _grid_values(codec, rng, 50, 256)
@@ -106,7 +119,8 @@ def test_round_trip_of_representable_rows(codec):
     assert np.array_equal(back, x.astype(np.float64))
 
 
-@pytest.mark.parametrize("codec", ["int8_g64", "e4m3_row", "e2m1_g16", "e4m3_mx32", "e4m3_tensor", "f16"])
+@pytest.mark.parametrize("codec", ["int8_g64", "e4m3_row", "e2m1_g16", "e4m3_mx32", "e2m1_mx32", "e4m3_tensor",
+                                   "f16"])
 def test_error_bound_half_a_grid_step(codec):
     rng = np.random.default_rng(22)
     x = (rng.standard_normal((200, 256)) * np.exp(rng.uniform(-3, 3, (200, 1)))).astype(np.float32)
@@ -132,6 +146,14 @@ def test_error_bound_half_a_grid_step(codec):
         sc = S.e4m3_decode(scales)[..., None]
         step = np.where(xg / sc < 2, 0.5, np.where(xg / sc < 4, 1.0, 2.0)) * sc
         assert np.all(eg <= 0.5 * step + amax * 2.0 ** -4)  # scale rounding may clip the top
+    elif codec == "e2m1_mx32":  # amax / X in [4, 8): the grid step is X/2, X or 2X; above 6 X saturates
+        X = S.ue8m0_decode(scales)[..., None]
+        r = xg / X
+        assert np.all((r[..., :].max(axis=-1) >= 4) & (r.max(axis=-1) < 8))
+        step = np.where(r < 2, 0.5, np.where(r < 4, 1.0, 2.0)) * X
+        clip = np.maximum(xg - 6.0 * X, 0.0)
+        assert np.all(eg <= 0.5 * step + clip)
+        assert np.any(clip > 0)
     elif codec == "e4m3_row":  # 3 mantissa bits; scale rounding clips at most amax 2^-11
         assert np.all(eg <= xg * 2.0 ** -4 + amax * 2.0 ** -9)
     else:  # MX: amax / X lies in [256, 512), so values above 448 X saturate
