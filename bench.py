@@ -59,7 +59,7 @@ FLUSH_BYTES = 1 << 30          # read before each timed step: 4x the 256 MB MALL
 RATE_BYTES = 4 << 30           # buffer of the streaming-rate measurement
 COPY_BYTES = RATE_BYTES // 2   # bytes each way of the probe's copy
 APPEND_CHUNK = 2048
-APPEND_FORMATS = ["K8V4", "BF16", "INT8_G64", "FP8_ROW", "NVFP4_G16", "FP8_TENSOR", "NVFP4_G16/2L"]
+APPEND_FORMATS = ["K8V4", "BF16", "INT8_G64", "FP8_ROW", "NVFP4_G16", "FP8_TENSOR", "NVFP4_G16/2L", "MXFP4"]
 CSRC = os.path.join(ROOT, "decode_attention_quant_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_traffic.json")
 METRIC = "decode-attn effective KV GB/s (% of HBM peak) per kv-dtype; quant-append tok/s"
@@ -68,7 +68,7 @@ WORKLOADS = {
     "batched": dict(config=2, formats=["INT8_G64", "FP8_ROW", "FP8_TENSOR"],
                     label="batched decode: 32 sequences x U[8192,32768] cached tokens, 24 q / 4 kv heads, "
                           "head_dim 256, 64-token pages"),
-    "long": dict(config=3, formats=["NVFP4_G16", "NVFP4_G16/2L"],
+    "long": dict(config=3, formats=["NVFP4_G16", "NVFP4_G16/2L", "MXFP4"],
                  label="long-context decode: 1 sequence x 262144 tokens, 24 q / 4 kv heads, head_dim 256"),
     "long8": dict(config="3b", formats=["NVFP4_G16"],
                   label="long-context decode: 8 sequences x 65536 tokens, 24 q / 4 kv heads, head_dim 256"),

@@ -15,7 +15,8 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvq.so")
 
-FORMATS = {"BF16": 0, "INT8_G64": 1, "FP8_ROW": 2, "NVFP4_G16": 3, "K8V4": 4, "MXFP8": 5, "FP8_TENSOR": 6}
+FORMATS = {"BF16": 0, "INT8_G64": 1, "FP8_ROW": 2, "NVFP4_G16": 3, "K8V4": 4, "MXFP8": 5, "FP8_TENSOR": 6,
+           "MXFP4": 7}
 FORMAT_NAMES = {v: k for k, v in FORMATS.items()}
 DEQUANT_STORED_DOMAIN = 1
 SPLIT_WRITE_WHOLE_UNITS = 1

@@ -116,6 +116,7 @@ hipError_t launch_append(uint8_t* pool, const uint16_t* k, const uint16_t* v, in
   KVQ_APPEND_CASE(F_FP8_TENSOR, 128) KVQ_APPEND_CASE(F_FP8_TENSOR, 256)
   KVQ_APPEND_CASE(F_MXFP8, 128) KVQ_APPEND_CASE(F_MXFP8, 256)
   KVQ_APPEND_CASE(F_INT8_G64, 256) KVQ_APPEND_CASE(F_NVFP4_G16, 256) KVQ_APPEND_CASE(F_K8V4, 256)
+  KVQ_APPEND_CASE(F_MXFP4, 256)
 #undef KVQ_APPEND_CASE
   return hipErrorInvalidValue;
 }

@@ -16,14 +16,14 @@ namespace kvq {
 #define KVQ_FOR_EACH_DECODE(X)                                                                     \
   X(F_BF16, 128) X(F_BF16, 256) X(F_FP8_ROW, 128) X(F_FP8_ROW, 256) X(F_FP8_TENSOR, 128)          \
   X(F_FP8_TENSOR, 256) X(F_MXFP8, 128) X(F_MXFP8, 256) X(F_INT8_G64, 256) X(F_NVFP4_G16, 256)   \
-  X(F_K8V4, 256)
+  X(F_K8V4, 256) X(F_MXFP4, 256)
 
 template <int FMT, int D>
 struct DT {
   static constexpr int KC = k_codec(FMT), VC = v_codec(FMT);
   static constexpr int KBITS = codec_bits(KC), VBITS = codec_bits(VC);
   static constexpr bool QI8 = KC == C_I8G64;    // Q.K on the int8 matrix cores, q in two int8 pieces
-  static constexpr bool QF16 = KC == C_E2G16;   // Q.K in f16, q split into f16 hi + lo
+  static constexpr bool QF16 = KC == C_E2G16 || KC == C_E2MX;  // Q.K in f16, q split into f16 hi + lo
   static constexpr bool QROT = k_rotated(FMT);  // q is rotated first (K was)
   static constexpr bool VROT = v_rotated(FMT);
   static constexpr int KSTEPS = D / 32;
@@ -57,8 +57,12 @@ struct DT {
   static constexpr int NT = D / 16;
   static constexpr int KCH = D * KBITS / 512;                       // 16-B K chunks per lane per block
   static constexpr int VCH = VBITS * NT / 32;                       // 16-B V chunks per lane per block
-  static constexpr int KSW = KC == C_E4ROW ? 2 : KC == C_I8G64 ? 8 : KC == C_E4MX ? D / 32 : KC == C_E2G16 ? 4 : 0;
-  static constexpr int VSW = VC == C_E4ROW ? 2 : VC == C_I8G64 ? 8 : VC == C_E4MX ? D / 32 : VC == C_E2G16 ? 16 : 0;
+  static constexpr int KSW = KC == C_E4ROW ? 2 : KC == C_I8G64 ? 8 : KC == C_E4MX ? D / 32 : KC == C_E2G16 ? 4
+                           : KC == C_E2MX ? D / 128 : 0;
+  static constexpr int VSW = VC == C_E4ROW ? 2 : VC == C_I8G64 ? 8 : VC == C_E4MX ? D / 32 : VC == C_E2G16 ? 16
+                           : VC == C_E2MX ? D / 32 : 0;
+  // K scale bytes of token c16 (4-bit K: the lane's own token, all groups)
+  static constexpr int KS_LANE_BYTES = KC == C_E2G16 ? 16 : KC == C_E2MX ? D / 32 : 0;
   static constexpr int G = n_groups(KC, D) > 0 ? n_groups(KC, D) : 1;
 };
 
@@ -119,7 +123,7 @@ __device__ __forceinline__ void load_k(Buf<FMT, D>& buf, const uint8_t* head0, c
   for (int i = 0; i < T::KCH; ++i) buf.k[i] = *reinterpret_cast<const uint4*>(kc + i * 1024 + lane * 16);
   if constexpr (T::KSW > 0) {
     const uint8_t* ks = ba.hb + geo.off_ks + (int64_t)ba.bip * geo.kscale_blk;
-    const int off = T::KC == C_E2G16 ? c16 * 16 : g * (4 * T::KSW);
+    const int off = T::KS_LANE_BYTES > 0 ? c16 * T::KS_LANE_BYTES : g * (4 * T::KSW);
     load_words(buf.ks, ks + off);
   }
 }
@@ -331,7 +335,7 @@ template <int FMT, int D>
 __device__ __forceinline__ void read_stage_k(Buf<FMT, D>& buf, uint32_t stage, int lane) {
   using T = DT<FMT, D>;
   const int g = lane >> 4, c16 = lane & 15;
-  const uint32_t sa = stage + T::SKS + (T::KC == C_E2G16 ? c16 * 16 : g * (4 * T::KSW));
+  const uint32_t sa = stage + T::SKS + (T::KS_LANE_BYTES > 0 ? c16 * T::KS_LANE_BYTES : g * (4 * T::KSW));
   lds_read_part<T::KCH, 1024, T::KSW>(buf.k, buf.ks, stage + T::SK + lane * 16, sa);
 }
 
@@ -386,6 +390,20 @@ __device__ __forceinline__ f16x8 e2m1x8_f16(uint32_t w) {
   r.y = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1));
   r.z = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2));
   r.w = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3));
+  return bitcast<f16x8>(r);
+}
+
+// 8 E2M1 codes times 2^(byte - 127) (UE8M0): the scaled conversion adds the
+// scale's exponent, so the f16 result is exact while code x scale stays in
+// f16 range.  Byte 0 is taken as 2^-126 (the conversion needs a normal fp32
+// scale); such a group holds values far below f16's range either way.
+__device__ __forceinline__ f16x8 e2m1x8_f16_mx(uint32_t w, uint32_t byte) {
+  const float sc = __uint_as_float((byte > 1u ? byte : 1u) << 23);
+  uint4 r;
+  r.x = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 0));
+  r.y = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 1));
+  r.z = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 2));
+  r.w = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 3));
   return bitcast<f16x8>(r);
 }
 
@@ -497,6 +515,21 @@ __device__ __forceinline__ f32x4 qk_block(const Buf<FMT, D>& buf, const Q& qo, i
       }
     }
     S += Slo;
+  } else if constexpr (T::KC == C_E2MX) {
+    // one UE8M0 per 32 values = per k-step, of the lane's token (lane % 16),
+    // applied by the conversion itself; q' as f16 hi + lo as for NVFP4
+    f32x4 Slo = zero;
+#pragma unroll
+    for (int i = 0; i < T::KCH; ++i) {
+#pragma unroll
+      for (int hh = 0; hh < 4; ++hh) {
+        const int kk = 4 * i + hh;
+        const f16x8 a = e2m1x8_f16_mx(word(buf.k[i], hh), (buf.ks[kk >> 2] >> (8 * (kk & 3))) & 0xFFu);
+        S = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bitcast<f16x8>(qo.get(kk, 0)), S, 0, 0, 0);
+        Slo = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bitcast<f16x8>(qo.get(kk, 1)), Slo, 0, 0, 0);
+      }
+    }
+    S += Slo;
   }
   return S;
 }
@@ -548,6 +581,25 @@ __device__ __forceinline__ f16x4 v_operand(const Buf<FMT, D>& buf, int nt, int l
     const uint32_t s23 = __builtin_amdgcn_perm(buf.vs[6 + (grp >> 1)], buf.vs[4 + (grp >> 1)], sel);
     a *= bitcast<f16x2>(s01);
     b *= bitcast<f16x2>(s23);
+    return f16x4{a[0], a[1], b[0], b[1]};
+  } else if constexpr (T::VC == C_E2MX) {
+    // codes as for NVFP4; the UE8M0 of tokens 4g .. 4g + 3 for group nt / 2
+    // (byte e of word nt / 2) as exact f16 powers of two (in f16 range)
+    const uint32_t w = word(buf.v[nt >> 3], (nt & 7) >> 1);
+    f16x2 a, b;
+    if (nt & 1) {
+      a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+      b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+    } else {
+      a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+      b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+    }
+    const uint32_t sw = buf.vs[nt >> 1];
+    auto pow2 = [](uint32_t byte) { return __uint_as_float(byte << 23); };  // 2^(byte - 127); 0 for byte 0
+    const f16x2 s01 = __builtin_amdgcn_cvt_pkrtz(pow2(sw & 0xFFu), pow2((sw >> 8) & 0xFFu));
+    const f16x2 s23 = __builtin_amdgcn_cvt_pkrtz(pow2((sw >> 16) & 0xFFu), pow2(sw >> 24));
+    a *= s01;
+    b *= s23;
     return f16x4{a[0], a[1], b[0], b[1]};
   } else {  // C_E2G16: bytes 2 (nt & 1) and 2 (nt & 1) + 1 of word (nt & 7) / 2 of chunk nt / 8
             // hold tokens (4g, 4g + 1) and (4g + 2, 4g + 3) of column n, the earlier token low
@@ -649,7 +701,7 @@ __device__ __forceinline__ void clear_tail(Buf<FMT, D>& buf, int nvalid, int g) 
 #pragma unroll
       for (int w = 0; w < WPT; ++w)
         if (e >= nv) buf.vs[e * WPT + w] = 0u;
-  } else if constexpr (T::VC == C_E2G16) {
+  } else if constexpr (T::VC == C_E2G16 || T::VC == C_E2MX) {  // byte e of each word: token 4g + e
 #pragma unroll
     for (int w = 0; w < T::VSW; ++w) buf.vs[w] &= bmask;
   }

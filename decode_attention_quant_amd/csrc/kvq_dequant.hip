@@ -48,6 +48,11 @@ __device__ __forceinline__ float stored_value(const uint8_t* codes, const uint8_
     const float mag[8] = {0.f, 0.5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f};
     const float c = (code & 8) ? -mag[code & 7] : mag[code & 7];
     return c * s * tensor_scale;  // exact: the two-level form's scale, 1 for single level
+  } else if constexpr (C == C_E2MX) {
+    const int pos = PLANE == 1 ? ((t >> 2) * 4 * G + grp * 4 + (t & 3)) : (t * G + grp);
+    const float mag[8] = {0.f, 0.5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f};
+    const float c = (code & 8) ? -mag[code & 7] : mag[code & 7];
+    return ldexpf(c, (int)scales[pos] - 127);
   } else {  // C_E4MX
     return ldexpf(e4m3_value(code), (int)scales[t * G + grp] - 127);
   }
@@ -127,6 +132,7 @@ hipError_t launch_dequant_page(const Geometry& geo, const uint8_t* pool, int64_t
   KVQ_DQ_CASE(F_FP8_TENSOR, 128) KVQ_DQ_CASE(F_FP8_TENSOR, 256)
   KVQ_DQ_CASE(F_MXFP8, 128) KVQ_DQ_CASE(F_MXFP8, 256)
   KVQ_DQ_CASE(F_INT8_G64, 256) KVQ_DQ_CASE(F_NVFP4_G16, 256) KVQ_DQ_CASE(F_K8V4, 256)
+  KVQ_DQ_CASE(F_MXFP4, 256)
 #undef KVQ_DQ_CASE
   return hipErrorInvalidValue;
 }

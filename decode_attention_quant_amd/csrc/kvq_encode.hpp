@@ -217,9 +217,10 @@ __device__ __forceinline__ void group_scale(float amax, float& s, float& r, uint
   } else if constexpr (C == C_E2G16) {
     sbits = e4m3_code(__fdiv_rn(amax, 6.0f));  // amax >= 0: the sign bit stays 0
     s = e4m3_value(sbits);
-  } else {  // C_E4MX: OCP MX shared exponent floor(log2 amax) - 8, biased by 127
+  } else {  // C_E4MX, C_E2MX: OCP MX shared exponent floor(log2 amax) - emax, biased by 127
+    constexpr int EMAX = C == C_E4MX ? 8 : 2;  // largest exponent of E4M3, E2M1
     const int e = __builtin_amdgcn_frexp_expf(amax) - 1;
-    int b = e - 8 + 127;
+    int b = e - EMAX + 127;
     b = b < 0 ? 0 : (b > 254 ? 254 : b);
     sbits = amax > 0.0f ? (uint32_t)b : 0u;
     s = 1.0f;  // unused: the codes divide by 2^(sbits - 127) exactly with ldexp
@@ -252,17 +253,17 @@ __device__ __forceinline__ void encode_group(const float* x, float s, float r, u
       w = e4m3_pair<true>(w, v[2], v[3]);
       out.w[(base + i) / 4] = (C == C_E4ROW && !(s > 0.0f)) ? 0u : w;
     }
-  } else {  // C_E2G16
+  } else {  // C_E2G16, C_E2MX
 #pragma unroll
     for (int i = 0; i < N; i += 8) {
       float v[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = div_scale(x[i + j], s, r);
+      for (int j = 0; j < 8; ++j) v[j] = C == C_E2MX ? ldexpf(x[i + j], 127 - (int)sbits) : div_scale(x[i + j], s, r);
       uint32_t w = e2m1_pair<0>(0u, v[0], v[1]);
       w = e2m1_pair<1>(w, v[2], v[3]);
       w = e2m1_pair<2>(w, v[4], v[5]);
       w = e2m1_pair<3>(w, v[6], v[7]);
-      out.w[(base + i) / 8] = s > 0.0f ? w : 0u;
+      out.w[(base + i) / 8] = (C == C_E2MX || s > 0.0f) ? w : 0u;
     }
   }
 }
@@ -568,13 +569,13 @@ __device__ __forceinline__ void v_row_group(uint8_t* __restrict__ pool, const ui
         for (int h2 = 0; h2 < 2; ++h2) {
           const float amax = max_over_lanes<GS / F>(abs_max<F>(x[h2]));
           group_scale<C>(amax, s[h2], r[h2], sb[2 * pr + h2]);
-          if constexpr (C != C_E4MX)
+          if constexpr (!mx_scaled(C))
             if (!(s[h2] > 0.0f))
               keep &= BITS == 4 ? ~(0x000F000Fu << (8 * pr + 4 * h2)) : ~(0xFFu << (8 * (2 * pr + h2)));
         }
       }
       auto quot = [&](int h2, float xv) -> float {
-        if constexpr (C == C_E4MX) return ldexpf(xv, 127 - (int)sb[2 * pr + h2]);
+        if constexpr (mx_scaled(C)) return ldexpf(xv, 127 - (int)sb[2 * pr + h2]);
         else return fast ? div_scale(xv, s[h2], r[h2]) : __fdiv_rn(xv, s[h2]);
       };
       if constexpr (BITS == 8) {
@@ -680,7 +681,7 @@ __device__ __forceinline__ void v_row_group(uint8_t* __restrict__ pool, const ui
     if constexpr (scale_bytes(C) > 0) {
       if (lead) {
         const int tb = off & 15;  // block-local slot of token 0
-        if constexpr (C == C_E2G16) {  // V UE4M3 of tokens 4 gv + e at gv*4G + grp*4 + e
+        if constexpr (BITS == 4) {  // 4-bit V scales of tokens 4 gv + e at gv*4G + grp*4 + e
           *reinterpret_cast<uint32_t*>(scales + gv * 4 * G + grp * 4) = sb[0] | (sb[1] << 8) | (sb[2] << 16) | (sb[3] << 24);
         } else if constexpr (scale_bytes(C) == 2) {
 #pragma unroll
@@ -733,7 +734,7 @@ __device__ __forceinline__ void v_row_group(uint8_t* __restrict__ pool, const ui
           const int t = off & 15;
           uint8_t* scales = pool + page * geo.page_bytes + (int64_t)head * geo.head_bytes + geo.off_vs +
                             (int64_t)(off >> 4) * geo.vscale_blk;
-          if constexpr (C == C_E2G16) scales[(t >> 2) * 4 * G + grp * 4 + (t & 3)] = (uint8_t)sb[e];
+          if constexpr (BITS == 4) scales[(t >> 2) * 4 * G + grp * 4 + (t & 3)] = (uint8_t)sb[e];
           else if constexpr (scale_bytes(C) == 2) *reinterpret_cast<uint16_t*>(scales + (t * G + grp) * 2) = (uint16_t)sb[e];
           else scales[t * G + grp] = (uint8_t)sb[e];
         }
@@ -768,7 +769,7 @@ __device__ __forceinline__ void v_row_group(uint8_t* __restrict__ pool, const ui
       }
       if constexpr (scale_bytes(C) > 0) {
         if (lead) {
-          if constexpr (C == C_E2G16) scales[gv * 4 * G + grp * 4 + te] = (uint8_t)sb[e];
+          if constexpr (BITS == 4) scales[gv * 4 * G + grp * 4 + te] = (uint8_t)sb[e];
           else if constexpr (scale_bytes(C) == 2) *reinterpret_cast<uint16_t*>(scales + (t * G + grp) * 2) = (uint16_t)sb[e];
           else scales[t * G + grp] = (uint8_t)sb[e];
         }

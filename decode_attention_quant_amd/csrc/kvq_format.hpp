@@ -36,8 +36,9 @@
 //   column n of n-tile jt; for 4-bit codes each byte converts straight into
 //   the f16 pair (4g + 2p, 4g + 2p + 1) of one operand register.
 //
-//   Scales, G groups per row: fp16 scales at (t*G + grp)*2; UE8M0 and the K
-//   UE4M3 bytes at t*G + grp; V UE4M3 bytes at (t/4)*4G + grp*4 + t%4.
+//   Scales, G groups per row: fp16 scales at (t*G + grp)*2; byte scales of
+//   K planes and of 8-bit V planes at t*G + grp; byte scales of 4-bit V
+//   planes (UE4M3, UE8M0) at (t/4)*4G + grp*4 + t%4.
 #pragma once
 #include <stdint.h>
 
@@ -57,35 +58,38 @@ enum Codec : int {
   C_E2G16 = 4,   // e2m1, ue4m3 scale per 16
   C_E4MX = 5,    // e4m3, ue8m0 scale per 32
   C_E4TEN = 6,   // e4m3, one fp32 scale per tensor (argument)
+  C_E2MX = 7,    // e2m1, ue8m0 scale per 32
 };
 
 enum Format : int {
   F_BF16 = 0, F_INT8_G64 = 1, F_FP8_ROW = 2, F_NVFP4_G16 = 3, F_K8V4 = 4, F_MXFP8 = 5, F_FP8_TENSOR = 6,
-  F_COUNT = 7
+  F_MXFP4 = 7, F_COUNT = 8
 };
 
 KVQ_HD constexpr int k_codec(int f) {
   return f == F_BF16 ? C_BF16 : f == F_INT8_G64 ? C_I8G64 : f == F_FP8_ROW ? C_E4ROW
-       : f == F_NVFP4_G16 ? C_E2G16 : f == F_K8V4 ? C_E4ROW : f == F_MXFP8 ? C_E4MX : C_E4TEN;
+       : f == F_NVFP4_G16 ? C_E2G16 : f == F_K8V4 ? C_E4ROW : f == F_MXFP8 ? C_E4MX : f == F_MXFP4 ? C_E2MX : C_E4TEN;
 }
 KVQ_HD constexpr int v_codec(int f) {
   return f == F_BF16 ? C_F16 : f == F_INT8_G64 ? C_I8G64 : f == F_FP8_ROW ? C_E4ROW
-       : f == F_NVFP4_G16 ? C_E2G16 : f == F_K8V4 ? C_E2G16 : f == F_MXFP8 ? C_E4MX : C_E4TEN;
+       : f == F_NVFP4_G16 ? C_E2G16 : f == F_K8V4 ? C_E2G16 : f == F_MXFP8 ? C_E4MX : f == F_MXFP4 ? C_E2MX : C_E4TEN;
 }
-KVQ_HD constexpr bool k_rotated(int f) { return f == F_INT8_G64 || f == F_NVFP4_G16; }
-KVQ_HD constexpr bool v_rotated(int f) { return f == F_NVFP4_G16 || f == F_K8V4; }
+KVQ_HD constexpr bool k_rotated(int f) { return f == F_INT8_G64 || f == F_NVFP4_G16 || f == F_MXFP4; }
+KVQ_HD constexpr bool v_rotated(int f) { return f == F_NVFP4_G16 || f == F_K8V4 || f == F_MXFP4; }
 // Planes with a per-tensor fp32 scale (the descriptor's k_scale / v_scale):
 // FP8-tensor, and the two-level form of the NVFP4 planes (1 = single level).
 KVQ_HD constexpr bool k_tensor_scaled(int f) { return f == F_FP8_TENSOR || f == F_NVFP4_G16; }
 KVQ_HD constexpr bool v_tensor_scaled(int f) { return f == F_FP8_TENSOR || f == F_NVFP4_G16 || f == F_K8V4; }
 
-KVQ_HD constexpr int codec_bits(int c) { return (c == C_BF16 || c == C_F16) ? 16 : c == C_E2G16 ? 4 : 8; }
+KVQ_HD constexpr int codec_bits(int c) { return (c == C_BF16 || c == C_F16) ? 16 : (c == C_E2G16 || c == C_E2MX) ? 4 : 8; }
+// the scale is a power of two (UE8M0 byte): codes are scaled exactly by ldexp
+KVQ_HD constexpr bool mx_scaled(int c) { return c == C_E4MX || c == C_E2MX; }
 // group size along head_dim (0 = no per-row scales; -1 = whole row)
 KVQ_HD constexpr int codec_group(int c) {
-  return c == C_I8G64 ? 64 : c == C_E4ROW ? -1 : c == C_E2G16 ? 16 : c == C_E4MX ? 32 : 0;
+  return c == C_I8G64 ? 64 : c == C_E4ROW ? -1 : c == C_E2G16 ? 16 : (c == C_E4MX || c == C_E2MX) ? 32 : 0;
 }
 KVQ_HD constexpr int scale_bytes(int c) {
-  return (c == C_I8G64 || c == C_E4ROW) ? 2 : (c == C_E2G16 || c == C_E4MX) ? 1 : 0;
+  return (c == C_I8G64 || c == C_E4ROW) ? 2 : (c == C_E2G16 || c == C_E4MX || c == C_E2MX) ? 1 : 0;
 }
 KVQ_HD constexpr int n_groups(int c, int D) {
   return codec_group(c) == 0 ? 0 : codec_group(c) < 0 ? 1 : D / codec_group(c);

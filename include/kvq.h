@@ -61,9 +61,10 @@ typedef enum kvq_status {
  *  KVQ_K8V4        K as FP8_ROW | V as NVFP4_G16 (rot)             [402]
  *  KVQ_MXFP8       E4M3 + UE8M0 scale per 32 | same                [528; 264 at D=128]
  *  KVQ_FP8_TENSOR  E4M3 of x / k_scale | E4M3 of x / v_scale       [512]
+ *  KVQ_MXFP4       E2M1 + UE8M0 scale per 32, rot | same, rot      [272]
  * Scales are computed from the group's absolute maximum: fp16(amax/127),
  * fp16(amax/448), UE4M3(amax/6), and the OCP MX exponent
- * floor(log2 amax) - 8; every element is then rounded to nearest-even from
+ * floor(log2 amax) - 8 (E4M3) or - 2 (E2M1); every element is then rounded to nearest-even from
  * x / scale computed in IEEE fp32 with the stored scale, saturating at the
  * format maximum.  The encoding is bit-exact and deterministic. */
 typedef enum kvq_format {
@@ -73,13 +74,15 @@ typedef enum kvq_format {
   KVQ_NVFP4_G16 = 3,
   KVQ_K8V4 = 4,
   KVQ_MXFP8 = 5,
-  KVQ_FP8_TENSOR = 6
+  KVQ_FP8_TENSOR = 6,
+  KVQ_MXFP4 = 7
 } kvq_format;
 
 /* One layer's KV cache.
  *  format        kvq_format value.
  *  head_dim      D: 128 or 256 for BF16, FP8_ROW, FP8_TENSOR, MXFP8;
- *                256 for INT8_G64, NVFP4_G16, K8V4 (the rotation is 256-point).
+ *                256 for INT8_G64, NVFP4_G16, K8V4, MXFP4 (the rotation is
+ *                256-point).
  *  page_size     tokens per page: 64 or 128 (the pages use 64, and 128 for mxfp8).
  *  num_kv_heads  H_kv >= 1.
  *  num_pages     pages in the pool (> 0).

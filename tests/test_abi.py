@@ -41,11 +41,11 @@ def test_status_strings():
     assert lib.kvq_status_string(99) == b"unknown status"
 
 
-@pytest.mark.parametrize("fmt", range(7))
+@pytest.mark.parametrize("fmt", range(8))
 @pytest.mark.parametrize("D,P", [(128, 64), (256, 64), (256, 128), (128, 128)])
 def test_page_bytes_match_the_oracle_layout(fmt, D, P):
     d = kvq.desc(fmt, D, P, 3, 10, 0.5, 0.5)
-    rotated = fmt in (1, 3, 4)
+    rotated = fmt in (1, 3, 4, 7)
     if rotated and D != 256:
         with pytest.raises(kvq.KvqError) as e:
             kvq.page_bytes(d)
@@ -61,7 +61,7 @@ def _status(fn, *args):
 def test_desc_validation():
     out = ctypes.c_size_t()
     bad = [
-        (kvq.desc(7, 256, 64, 2, 4), 1),       # unknown format
+        (kvq.desc(8, 256, 64, 2, 4), 1),       # unknown format
         (kvq.desc(-1, 256, 64, 2, 4), 1),
         (kvq.desc(0, 256, 64, 0, 4), 1),       # no kv heads
         (kvq.desc(0, 256, 64, 2, 0), 1),       # no pages

@@ -15,7 +15,7 @@ pytestmark = pytest.mark.gpu
 # (format, config whose shapes it borrows, head_dim override)
 CASES = [
     ("BF16", 1, None), ("FP8_ROW", 1, None), ("INT8_G64", 2, None), ("FP8_ROW", 2, None), ("FP8_TENSOR", 2, None),
-    ("NVFP4_G16", 3, None), ("K8V4", 4, None), ("MXFP8", 5, None),
+    ("NVFP4_G16", 3, None), ("K8V4", 4, None), ("MXFP8", 5, None), ("MXFP4", 3, None), ("MXFP4", 4, None),
 ]
 
 
@@ -81,7 +81,7 @@ def _adversarial_rows(D, rng):
     return np.stack(rows)
 
 
-@pytest.mark.parametrize("fmt", ["INT8_G64", "FP8_ROW", "NVFP4_G16", "K8V4", "MXFP8", "FP8_TENSOR", "BF16"])
+@pytest.mark.parametrize("fmt", ["INT8_G64", "FP8_ROW", "NVFP4_G16", "K8V4", "MXFP8", "FP8_TENSOR", "BF16", "MXFP4"])
 def test_append_adversarial_rows_bit_exact(fmt):
     require_gpu()
     D, P, H = 256, 64, 2
@@ -136,7 +136,7 @@ def c_len(cfg):
     return 200 if cfg != 5 else 300
 
 
-@pytest.mark.parametrize("fmt,cfg", [("INT8_G64", 2), ("NVFP4_G16", 3), ("K8V4", 4)])
+@pytest.mark.parametrize("fmt,cfg", [("INT8_G64", 2), ("NVFP4_G16", 3), ("K8V4", 4), ("MXFP4", 3)])
 def test_dequant_page_original_domain(fmt, cfg):
     c = W.make_case(cfg, fmt, device="cpu", B=1, lengths=[128])
     bl = build(c)
@@ -148,7 +148,7 @@ def test_dequant_page_original_domain(fmt, cfg):
 
 
 @pytest.mark.parametrize("fmt,cfg", [("K8V4", 4), ("NVFP4_G16", 3), ("INT8_G64", 2), ("FP8_ROW", 2),
-                                     ("FP8_TENSOR", 2), ("BF16", 1), ("MXFP8", 5)])
+                                     ("FP8_TENSOR", 2), ("BF16", 1), ("MXFP8", 5), ("MXFP4", 3)])
 def test_append_chunks_at_any_offset(fmt, cfg):
     """Prefill chunks appended after cached prefixes start at every alignment
     inside a 16-slot block and a 4-slot slab (consecutive slots, shifted),
@@ -171,7 +171,7 @@ def test_append_chunks_at_any_offset(fmt, cfg):
 
 
 @pytest.mark.parametrize("fmt,cfg", [("NVFP4_G16", 3), ("K8V4", 4), ("INT8_G64", 2), ("FP8_ROW", 2), ("MXFP8", 5),
-                                     ("BF16", 1)])
+                                     ("BF16", 1), ("MXFP4", 4)])
 def test_append_slots_in_random_order(fmt, cfg):
     """One call writes every slot of a few pages in random input order, so the
     tokens that share a slab (and, for 4-bit V, a byte) sit in different rows
@@ -198,7 +198,7 @@ def test_append_slots_in_random_order(fmt, cfg):
                                                                         ref[diff[:8]])
 
 
-@pytest.mark.parametrize("fmt,cfg", [("NVFP4_G16", 3), ("K8V4", 4), ("FP8_ROW", 2)])
+@pytest.mark.parametrize("fmt,cfg", [("NVFP4_G16", 3), ("K8V4", 4), ("FP8_ROW", 2), ("MXFP4", 3)])
 def test_single_token_steps_and_rewrites(fmt, cfg):
     """Decode-style appends of one token per sequence, step after step (the
     even and odd tokens of each 4-bit V byte pair arrive in different calls),

@@ -26,6 +26,8 @@ CASES = [
     (3, "NVFP4_G16", 2, [2100, 900]),
     (4, "K8V4", 6, [1500, 20, 640, 129, 2000, 777]),
     (5, "MXFP8", 3, [700, 260, 128]),
+    (3, "MXFP4", 2, [2100, 901]),
+    (4, "MXFP4", 5, [1500, 21, 640, 129, 777]),
 ]
 
 
@@ -59,7 +61,8 @@ def test_fp8_tensor_unit_scale():
     assert_close(out, ref, "fp8 tensor unit scale")
 
 
-@pytest.mark.parametrize("fmt,cfg", [("FP8_ROW", 2), ("NVFP4_G16", 3), ("MXFP8", 5), ("K8V4", 4), ("INT8_G64", 2)])
+@pytest.mark.parametrize("fmt,cfg", [("FP8_ROW", 2), ("NVFP4_G16", 3), ("MXFP8", 5), ("K8V4", 4), ("INT8_G64", 2),
+                                     ("MXFP4", 3)])
 def test_edge_lengths(fmt, cfg):
     lens = [0, 1, 15, 16, 17, 63, 64, 65, 127, 128, 129, 3]
     c = W.make_case(cfg, fmt, device="cpu", B=len(lens), lengths=lens)
@@ -83,7 +86,8 @@ def test_mtp_short_sequences():
     assert np.all(out[0, :2] == 0)
 
 
-@pytest.mark.parametrize("fmt,cfg", [("INT8_G64", 2), ("NVFP4_G16", 3), ("MXFP8", 5), ("K8V4", 4)])
+@pytest.mark.parametrize("fmt,cfg", [("INT8_G64", 2), ("NVFP4_G16", 3), ("MXFP8", 5), ("K8V4", 4),
+                                     ("MXFP4", 3)])
 def test_workgroup_sweep_and_phases(fmt, cfg):
     """Any number of split workgroups (ranges that cut units anywhere, one
     workgroup holding many units, empty workgroups) gives the same answer,
@@ -186,7 +190,7 @@ def test_combine_over_a_hundred_partials():
 
 
 @pytest.mark.parametrize("fmt,cfg", [("NVFP4_G16", 3), ("FP8_ROW", 2), ("INT8_G64", 2), ("K8V4", 4), ("MXFP8", 5),
-                                     ("BF16", 1)])
+                                     ("BF16", 1), ("MXFP4", 3)])
 def test_scores_that_climb_and_jump(fmt, cfg):
     """Keys scaled up along each sequence (up to 6x at the end) with a few
     6x spikes late on: the running maximum climbs block after block and

@@ -60,6 +60,7 @@ CASES = [
     (4, "K8V4", [150, 400, 7], 29),
     (5, "MXFP8", [200, 61], 70),
     (5, "BF16", [200, 61], 70),
+    (3, "MXFP4", [260, 33], 41),
 ]
 
 
@@ -87,7 +88,7 @@ def test_prefill_short_and_empty_sequences():
     assert np.all(out[1, :14] == 0) and np.all(np.isneginf(lse[1, :14]))
 
 
-@pytest.mark.parametrize("fmt,cfg", [("K8V4", 4), ("MXFP8", 5), ("INT8_G64", 2)])
+@pytest.mark.parametrize("fmt,cfg", [("K8V4", 4), ("MXFP8", 5), ("INT8_G64", 2), ("MXFP4", 3)])
 def test_prefill_agrees_with_decode(fmt, cfg):
     """Where both apply (few query tokens), prefill and decode compute the same
     attention.  They differ in how the blocks are grouped (decode's four waves

@@ -72,6 +72,7 @@ CASES = [
     (3, "NVFP4_G16", [2099, 900, 15]),           # odd positions: 4-bit V byte pairs half filled
     (4, "K8V4", [1500, 19, 640, 128, 2001, 776]),
     (5, "MXFP8", [700, 258, 124, 2]),            # n_q = 4: the 4 new tokens cross a block at 124 + 4
+    (3, "MXFP4", [2099, 900, 15]),
 ]
 
 
@@ -120,7 +121,7 @@ def test_fused_step_short_and_empty_sequences():
     assert np.all(outs[1][0][0, :2] == 0)  # queries before position 0 see nothing
 
 
-@pytest.mark.parametrize("fmt,cfg", [("NVFP4_G16", 3), ("K8V4", 4), ("INT8_G64", 2)])
+@pytest.mark.parametrize("fmt,cfg", [("NVFP4_G16", 3), ("K8V4", 4), ("INT8_G64", 2), ("MXFP4", 3)])
 def test_fused_steps_in_a_row(fmt, cfg):
     """Three steps in a row, each appending one token per sequence, so the
     4-bit V byte pairs are completed by a later launch."""
@@ -138,7 +139,8 @@ def test_fused_steps_in_a_row(fmt, cfg):
         c.reserve -= 1
 
 
-@pytest.mark.parametrize("fmt,cfg", [("NVFP4_G16", 3), ("MXFP8", 5), ("K8V4", 4), ("FP8_ROW", 2), ("INT8_G64", 2)])
+@pytest.mark.parametrize("fmt,cfg", [("NVFP4_G16", 3), ("MXFP8", 5), ("K8V4", 4), ("FP8_ROW", 2), ("INT8_G64", 2),
+                                     ("MXFP4", 3)])
 @pytest.mark.parametrize("nwg", [1, 3])
 def test_fused_step_with_long_ranges(fmt, cfg, nwg):
     """Few split workgroups, so each wave walks tens of blocks and its block

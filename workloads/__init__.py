@@ -32,7 +32,7 @@ import math
 import numpy as np
 import torch
 
-FORMAT_IDS = {"BF16": 0, "INT8_G64": 1, "FP8_ROW": 2, "NVFP4_G16": 3, "K8V4": 4, "MXFP8": 5, "FP8_TENSOR": 6}
+FORMAT_IDS = {"BF16": 0, "INT8_G64": 1, "FP8_ROW": 2, "NVFP4_G16": 3, "K8V4": 4, "MXFP8": 5, "FP8_TENSOR": 6, "MXFP4": 7}
 
 CONFIGS = {
     1: dict(name="tiny decode", B=1, H_q=4, H_kv=2, D=256, n_q=1, P=64,
