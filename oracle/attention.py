@@ -79,16 +79,36 @@ def attend(q, K, V, scale, n_q):
     return out, lse
 
 
+def quantize_query_mxfp8(q):
+    """The query rounded to MXFP8 along head_dim, as float64 values.
+
+    The pages quantize only the cache.  This is an optional mode of ours (a
+    reading, not the pages' method): the query is put in the same MXFP8
+    format as an MXFP8 cache's K (TokenSpeed article, ``--kv-cache-dtype``
+    section: E4M3 elements, one UE8M0 scale per 32 head_dim elements), so
+    that q . k is a product of two block-scaled FP8 operands.  Each row is
+    encoded and decoded by the cache's own MXFP8 codec; a row's values are
+    its bf16 values, unscaled (the softmax scale is applied to the product).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    rows = q.reshape(-1, q.shape[-1]).astype(np.float32)  # bf16 values: exact in float32
+    codes, scales = F.encode_rows("e4m3_mx32", False, rows)
+    return F.decode_rows("e4m3_mx32", False, codes, scales).reshape(q.shape)
+
+
 def attention_ref(geo, pool, q_bits, block_table, seq_lens, softmax_scale, n_q,
-                  k_scale=1.0, v_scale=1.0, only=None):
+                  k_scale=1.0, v_scale=1.0, only=None, q_mxfp8=False):
     """Decode attention over the paged pool.
 
     q_bits: bf16 bits [B][n_q][H_q][D].  Returns float64 out [B][n_q][H_q][D]
     and lse [B][n_q][H_q].  ``only`` optionally restricts the work to a list
     of (b, kv_head) pairs (other entries stay NaN) so that single outputs of
-    very large problems can be computed one by one.
+    very large problems can be computed one by one.  ``q_mxfp8`` replaces
+    the query by ``quantize_query_mxfp8(q)`` first; nothing else changes.
     """
     q = bf16_bits_to_f32(np.asarray(q_bits, dtype=np.uint16)).astype(np.float64)
+    if q_mxfp8:
+        q = quantize_query_mxfp8(q)
     B, nq, H_q, D = q.shape
     G = H_q // geo.H_kv
     out = np.full((B, nq, H_q, D), np.nan)
