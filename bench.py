@@ -74,7 +74,7 @@ WORKLOADS = {
                   label="long-context decode: 8 sequences x 65536 tokens, 24 q / 4 kv heads, head_dim 256"),
     "mixed": dict(config=4, formats=["K8V4"],
                   label="mixed-length decode: 64 sequences x logU[1K,128K] tokens, 24 q / 4 kv heads, head_dim 256"),
-    "mtp": dict(config=5, formats=["MXFP8"],
+    "mtp": dict(config=5, formats=["MXFP8", "MXFP8/QMX"],
                 label="MTP decode: 256 sequences x 4096 tokens, 4 query tokens, MHA 32 heads, head_dim 128, "
                       "128-token pages"),
     "tiny": dict(config=1, formats=["BF16", "FP8_ROW"],
@@ -82,10 +82,11 @@ WORKLOADS = {
 }
 
 def parse_label(label):
-    """'NVFP4_G16/2L' -> ('NVFP4_G16', True): a format, and whether its NVFP4
-    planes take a calibrated per-tensor (second-level) scale."""
+    """'NVFP4_G16/2L' -> ('NVFP4_G16', True, False): a format, whether its
+    NVFP4 planes take a calibrated per-tensor (second-level) scale, and
+    ('MXFP8/QMX') whether decode runs in the query-MXFP8 mode."""
     fmt, _, mod = label.partition("/")
-    return fmt, mod == "2L"
+    return fmt, mod == "2L", mod == "QMX"
 
 
 def kv_bytes_per_token(d):
@@ -96,7 +97,8 @@ class Setup:
     """One workload resident on the GPU: pool, tables, and the step's inputs."""
 
     def __init__(self, config, label):
-        fmt, two_level = parse_label(label)
+        fmt, two_level, qmx = parse_label(label)
+        self.flags = kvq.SPLIT_WRITE_WHOLE_UNITS | (kvq.SPLIT_Q_MXFP8 if qmx else 0)
         self.case = c = W.make_case(config, fmt, device="cuda", two_level=two_level)
         self.desc = kvq.desc(c.fmt, c.D, c.P, c.H_kv, c.num_pages, c.k_scale, c.v_scale)
         self.pool = kvq.alloc_pool(self.desc)
@@ -130,17 +132,17 @@ class Setup:
         rec(0)
         if fused:
             kvq.decode_step_split(self.desc, self.pool, self.k_new, self.v_new, self.q, self.bt, self.sl,
-                                  c.softmax_scale, self.ws, flags=kvq.SPLIT_WRITE_WHOLE_UNITS, out=self.out,
+                                  c.softmax_scale, self.ws, flags=self.flags, out=self.out,
                                   lse=self.lse, stream=stream)
         else:
             kvq.quantize_append(self.desc, self.pool, self.k_new.view(-1, c.H_kv, c.D),
                                 self.v_new.view(-1, c.H_kv, c.D), self.slot_new, stream=stream)
             rec(1)
             kvq.decode_split(self.desc, self.pool, self.q, self.bt, self.sl, c.softmax_scale, self.ws,
-                             flags=kvq.SPLIT_WRITE_WHOLE_UNITS, out=self.out, lse=self.lse, stream=stream)
+                             flags=self.flags, out=self.out, lse=self.lse, stream=stream)
         rec(2)
         kvq.decode_combine(self.desc, c.B, c.n_q, c.H_q, c.max_pages, self.sl, self.ws, self.out, self.lse,
-                           flags=kvq.SPLIT_WRITE_WHOLE_UNITS, stream=stream)
+                           flags=self.flags, stream=stream)
         rec(3)
 
 
@@ -225,7 +227,7 @@ def append_chunk_bench(formats, stream, probe, reps=10):
     against the HBM roof T * H_kv * (4 D + bytes_per_token) / 8 TB/s."""
     res = {}
     for label in formats:
-        fmt, two_level = parse_label(label)
+        fmt, two_level, _ = parse_label(label)
         c = W.make_case(4, fmt, device="cuda", reserve=APPEND_CHUNK, two_level=two_level)
         c.k = c.v = None  # only the new chunk is written
         d = kvq.desc(c.fmt, c.D, c.P, c.H_kv, c.num_pages, 1.0, 1.0)

@@ -20,6 +20,7 @@ FORMATS = {"BF16": 0, "INT8_G64": 1, "FP8_ROW": 2, "NVFP4_G16": 3, "K8V4": 4, "M
 FORMAT_NAMES = {v: k for k, v in FORMATS.items()}
 DEQUANT_STORED_DOMAIN = 1
 SPLIT_WRITE_WHOLE_UNITS = 1
+SPLIT_Q_MXFP8 = 2  # MXFP8 caches: q rounded to MXFP8, Q.K on the block-scaled fp8 MFMA
 
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP runtime error"}
 

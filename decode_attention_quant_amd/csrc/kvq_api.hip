@@ -175,9 +175,10 @@ static kvq_status decode_run(const kvq_cache_desc* desc, const void* pool, const
                              const int32_t* seq_lens, float softmax_scale, int32_t nwg_req, bool write_direct,
                              bool run_split, bool run_combine, float* out, float* lse, void* workspace,
                              size_t workspace_bytes, hipStream_t stream, const void* k_new = nullptr,
-                             const void* v_new = nullptr) {
+                             const void* v_new = nullptr, bool q_mx = false) {
   kvq_status st = check_decode_shape(desc, batch, n_q, H_q, max_pages);
   if (st != KVQ_OK) return st;
+  if (q_mx && desc->format != KVQ_MXFP8) return KVQ_ERR_UNSUPPORTED;
   if (!isfinite(softmax_scale)) return KVQ_ERR_INVALID_ARGUMENT;
   if (nwg_req < 0) return KVQ_ERR_INVALID_ARGUMENT;
   if (batch == 0) return KVQ_OK;
@@ -199,6 +200,7 @@ static kvq_status decode_run(const kvq_cache_desc* desc, const void* pool, const
   a.q = static_cast<const uint16_t*>(q_bf16);
   a.block_table = block_table;
   a.write_direct = write_direct ? 1 : 0;
+  a.q_mx = q_mx ? 1 : 0;
   a.out = out;
   a.lse = lse;
   if (k_new != nullptr) {  // fused step
@@ -247,7 +249,7 @@ kvq_status kvq_decode_step_split(const kvq_cache_desc* desc, void* pool, const v
                                  const int32_t* seq_lens, float softmax_scale, int32_t num_workgroups,
                                  int32_t flags, float* out, float* lse, void* workspace, size_t workspace_bytes,
                                  hipStream_t stream) {
-  if ((flags & ~KVQ_SPLIT_WRITE_WHOLE_UNITS) != 0) return KVQ_ERR_INVALID_ARGUMENT;
+  if ((flags & ~(KVQ_SPLIT_WRITE_WHOLE_UNITS | KVQ_SPLIT_Q_MXFP8)) != 0) return KVQ_ERR_INVALID_ARGUMENT;
   kvq_status st = check_decode_shape(desc, batch, n_q, num_q_heads, max_pages_per_seq);
   if (st != KVQ_OK) return st;
   if ((num_q_heads / desc->num_kv_heads) * n_q > 16) return KVQ_ERR_UNSUPPORTED;
@@ -258,7 +260,7 @@ kvq_status kvq_decode_step_split(const kvq_cache_desc* desc, void* pool, const v
   const bool whole = (flags & KVQ_SPLIT_WRITE_WHOLE_UNITS) != 0;
   return decode_run(desc, pool, q_bf16, batch, n_q, num_q_heads, block_table, max_pages_per_seq, seq_lens,
                     softmax_scale, num_workgroups, whole, true, false, whole ? out : nullptr, whole ? lse : nullptr,
-                    workspace, workspace_bytes, stream, k_new_bf16, v_new_bf16);
+                    workspace, workspace_bytes, stream, k_new_bf16, v_new_bf16, (flags & KVQ_SPLIT_Q_MXFP8) != 0);
 }
 
 kvq_status kvq_decode_split(const kvq_cache_desc* desc, const void* pool, const void* q_bf16, int32_t batch,
@@ -266,18 +268,20 @@ kvq_status kvq_decode_split(const kvq_cache_desc* desc, const void* pool, const 
                             int32_t max_pages_per_seq, const int32_t* seq_lens, float softmax_scale,
                             int32_t num_workgroups, int32_t flags, float* out, float* lse, void* workspace,
                             size_t workspace_bytes, hipStream_t stream) {
-  if ((flags & ~KVQ_SPLIT_WRITE_WHOLE_UNITS) != 0) return KVQ_ERR_INVALID_ARGUMENT;
+  if ((flags & ~(KVQ_SPLIT_WRITE_WHOLE_UNITS | KVQ_SPLIT_Q_MXFP8)) != 0) return KVQ_ERR_INVALID_ARGUMENT;
   const bool whole = (flags & KVQ_SPLIT_WRITE_WHOLE_UNITS) != 0;
   return decode_run(desc, pool, q_bf16, batch, n_q, num_q_heads, block_table, max_pages_per_seq, seq_lens,
                     softmax_scale, num_workgroups, whole, true, false, whole ? out : nullptr,
-                    whole ? lse : nullptr, workspace, workspace_bytes, stream);
+                    whole ? lse : nullptr, workspace, workspace_bytes, stream, nullptr, nullptr,
+                    (flags & KVQ_SPLIT_Q_MXFP8) != 0);
 }
 
 kvq_status kvq_decode_combine(const kvq_cache_desc* desc, int32_t batch, int32_t n_q, int32_t num_q_heads,
                               int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t num_workgroups,
                               int32_t flags, const void* workspace, size_t workspace_bytes, float* out, float* lse,
                               hipStream_t stream) {
-  if ((flags & ~KVQ_SPLIT_WRITE_WHOLE_UNITS) != 0) return KVQ_ERR_INVALID_ARGUMENT;
+  // KVQ_SPLIT_Q_MXFP8 changes only the split phase: accepted and ignored here
+  if ((flags & ~(KVQ_SPLIT_WRITE_WHOLE_UNITS | KVQ_SPLIT_Q_MXFP8)) != 0) return KVQ_ERR_INVALID_ARGUMENT;
   return decode_run(desc, nullptr, nullptr, batch, n_q, num_q_heads, nullptr, max_pages_per_seq, seq_lens, 1.0f,
                     num_workgroups, (flags & KVQ_SPLIT_WRITE_WHOLE_UNITS) != 0, false, true, out, lse,
                     const_cast<void*>(workspace), workspace_bytes, stream);

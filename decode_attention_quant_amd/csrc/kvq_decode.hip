@@ -64,10 +64,10 @@ __device__ __forceinline__ void append_new_tokens(const DecodeArgs& a, const Geo
       const int64_t tok = tok0 + i;
       uint32_t raw[D / 8];
       enc::load_k_row<D>(raw, a.k_new + (tok * geo.H_kv + h) * D + q * (D / 4));
-      enc::encode_k_row<FMT, D>(a.pool_w, raw, slot_of(tok), geo, h, a.enc_k_scale, q);
+      enc::encode_k_row<base_format(FMT), D>(a.pool_w, raw, slot_of(tok), geo, h, a.enc_k_scale, q);
     }
   }
-  enc::v_row_group<FMT, D>(a.pool_w, a.v_new, slot_of, geo, a.enc_v_scale, h, lane & 15,
+  enc::v_row_group<base_format(FMT), D>(a.pool_w, a.v_new, slot_of, geo, a.enc_v_scale, h, lane & 15,
                            tok0 + ilo + 4 * (lane >> 4), tok0 + ilo, tok0 + ihi);
 }
 
@@ -263,7 +263,59 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
     qo.lds = qst;
     uint4 qv[T::QSTEPS * T::QPIECES];
     constexpr int E = D / 64;
-    if constexpr (!T::QROT) {
+    if constexpr (T::QMX) {
+      // q rounded to MXFP8 in the block-scaled MFMA's lane order (see
+      // lds_read_qmx): for MFMA s, lane (g, r) holds d = 128 s + 16 g + [0, 16)
+      // (half 0: MX group 4 s + g / 2) and d = 128 s + 64 + 16 g + [0, 16)
+      // (half 1: group 4 s + 2 + g / 2); the other 16 values of both groups
+      // are in lane (g ^ 1, r).
+      const uint16_t* qp = a.q + (((int64_t)b * a.n_q + qi) * a.H_q + qh) * D;
+      uint4 qraw[4 * T::QSTEPS];
+#pragma unroll
+      for (int i = 0; i < 4 * T::QSTEPS; ++i) {
+        uint4 q4 = make_uint4(0, 0, 0, 0);
+        if (row_ok) q4 = *reinterpret_cast<const uint4*>(qp + 128 * (i >> 2) + 64 * ((i >> 1) & 1) + 16 * g + 8 * (i & 1));
+        qraw[i] = q4;
+      }
+      stage_first();
+#pragma unroll
+      for (int s = 0; s < T::QSTEPS; ++s) {
+        uint32_t sb[2], w[8];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          float x[16];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const uint4 v = qraw[4 * s + 2 * hh + u];
+            const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              x[8 * u + 2 * j] = bf16_to_f32(vw[j] & 0xFFFFu);
+              x[8 * u + 2 * j + 1] = bf16_to_f32(vw[j] >> 16);
+            }
+          }
+          float am = 0.f;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) am = fmaxf(am, fabsf(x[j]));
+          am = fmaxf(am, __shfl_xor(am, 16));  // the group's other half
+          float unused_s, unused_r;
+          enc::group_scale<C_E4MX>(am, unused_s, unused_r, sb[hh]);
+#pragma unroll
+          for (int j = 0; j < 16; j += 4) {
+            const int sh = 127 - (int)sb[hh];
+            const uint32_t lo = enc::e4m3_pair<false>(0u, ldexpf(x[j], sh), ldexpf(x[j + 1], sh));
+            w[4 * hh + j / 4] = enc::e4m3_pair<true>(lo, ldexpf(x[j + 2], sh), ldexpf(x[j + 3], sh));
+          }
+        }
+        qv[2 * s] = make_uint4(w[0], w[1], w[2], w[3]);
+        qv[2 * s + 1] = make_uint4(w[4], w[5], w[6], w[7]);
+        // lane block g gives the scale of group 4 s + g: blocks 0 and 3 hold
+        // it (half 0, half 1), blocks 1 and 2 hold each other's
+        const uint32_t send = g == 2 ? sb[0] : sb[1];
+        const uint32_t got = (uint32_t)__shfl((int)send, g == 1 ? lane + 16 : g == 2 ? lane - 16 : lane);
+        qo.qsc[s] = g == 0 ? sb[0] : g == 3 ? sb[1] : got;
+      }
+    } else if constexpr (!T::QROT) {
       const uint16_t* qp = a.q + (((int64_t)b * a.n_q + qi) * a.H_q + qh) * D;
 #pragma unroll
       for (int kk = 0; kk < T::QSTEPS; ++kk) {
@@ -759,6 +811,22 @@ hipError_t decode_split_occupancy(const Geometry& geo, int B, int R, int* blocks
 hipError_t launch_decode_split(const Geometry& geo, const DecodeArgs& a, hipStream_t stream) {
   const int tiles = (a.R + 15) / 16;
   const size_t lds = decode_split_lds_bytes(geo, a.B, a.R);
+  if (a.q_mx) {  // the variant keeps the MXFP8 kernel's LDS layout
+    if (geo.fmt != F_MXFP8) return hipErrorInvalidValue;
+#define KVQ_QMX_CASE(DD)                                                                                      \
+  if (geo.D == DD) {                                                                                          \
+    if (a.pool_w != nullptr)                                                                                  \
+      hipLaunchKernelGGL((decode_split_kernel<F_MXFP8 | VARIANT_QMX, DD, true>), dim3(a.nwg, tiles), dim3(256), lds, \
+                         stream, geo, a);                                                                     \
+    else                                                                                                      \
+      hipLaunchKernelGGL((decode_split_kernel<F_MXFP8 | VARIANT_QMX, DD, false>), dim3(a.nwg, tiles), dim3(256), lds, \
+                         stream, geo, a);                                                                     \
+    return hipGetLastError();                                                                                 \
+  }
+    KVQ_QMX_CASE(128) KVQ_QMX_CASE(256)
+#undef KVQ_QMX_CASE
+    return hipErrorInvalidValue;
+  }
 #define KVQ_SPLIT_CASE(F, DD)                                                                                 \
   if (geo.fmt == F && geo.D == DD) {                                                                          \
     if (a.pool_w != nullptr)                                                                                  \

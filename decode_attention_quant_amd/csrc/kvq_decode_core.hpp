@@ -26,9 +26,12 @@ struct DT {
   static constexpr bool QF16 = KC == C_E2G16 || KC == C_E2MX;  // Q.K in f16, q split into f16 hi + lo
   static constexpr bool QROT = k_rotated(FMT);  // q is rotated first (K was)
   static constexpr bool VROT = v_rotated(FMT);
+  // Q.K on the block-scaled fp8 MFMA, q rounded to MXFP8 (MXFP8 cache only)
+  static constexpr bool QMX = (FMT & VARIANT_QMX) != 0;
+  static_assert(!QMX || KC == C_E4MX, "the query-MXFP8 variant reads an MXFP8 cache");
   static constexpr int KSTEPS = D / 32;
-  static constexpr int QSTEPS = QI8 ? D / 64 : D / 32;  // MFMA k-steps of Q.K
-  static constexpr int QPIECES = (QI8 || QF16) ? 2 : 1;
+  static constexpr int QSTEPS = QMX ? D / 128 : QI8 ? D / 64 : D / 32;  // MFMA k-steps of Q.K
+  static constexpr int QPIECES = (QI8 || QF16 || QMX) ? 2 : 1;  // QMX: 32 fp8 codes = two 16-byte pieces
   // Bytes of one 16-token block in each plane, and their place in an LDS
   // stage (the four plane regions back to back).
   static constexpr int KB = code_block_bytes(KC, D), KSB = scale_block_bytes(KC, D);
@@ -46,6 +49,7 @@ struct DT {
   static constexpr int RING_FIT = RING_LDS / (4 * STAGE);
   static constexpr int RING_S = RING_FIT > 4 ? 4 : RING_FIT;
   static constexpr bool RING = RING_S >= 2 && FMT != F_INT8_G64;
+  static_assert(!QMX || RING, "the query-MXFP8 variant reads K from the LDS ring");
   // Without the ring: Q operands in LDS (one ds_read_b128 per k-step) where
   // registers would otherwise spill.
   static constexpr bool QLDS = !RING;
@@ -57,8 +61,9 @@ struct DT {
   static constexpr int NT = D / 16;
   static constexpr int KCH = D * KBITS / 512;                       // 16-B K chunks per lane per block
   static constexpr int VCH = VBITS * NT / 32;                       // 16-B V chunks per lane per block
-  static constexpr int KSW = KC == C_E4ROW ? 2 : KC == C_I8G64 ? 8 : KC == C_E4MX ? D / 32 : KC == C_E2G16 ? 4
-                           : KC == C_E2MX ? D / 128 : 0;
+  // (QMX: one scale byte per 128-value MFMA, one word each)
+  static constexpr int KSW = QMX ? D / 128 : KC == C_E4ROW ? 2 : KC == C_I8G64 ? 8 : KC == C_E4MX ? D / 32
+                           : KC == C_E2G16 ? 4 : KC == C_E2MX ? D / 128 : 0;
   static constexpr int VSW = VC == C_E4ROW ? 2 : VC == C_I8G64 ? 8 : VC == C_E4MX ? D / 32 : VC == C_E2G16 ? 16
                            : VC == C_E2MX ? D / 32 : 0;
   // K scale bytes of token c16 (4-bit K: the lane's own token, all groups)
@@ -329,14 +334,60 @@ __device__ __forceinline__ void lds_read_part(uint4 (&c)[NC], uint32_t (&w)[SW >
 #undef KVQ_W
 }
 
+// Operands of the block-scaled 16x16x128 fp8 MFMA, for NS MFMAs (128
+// head_dim values each).  The instruction's lane layout (measured): lane
+// 16 i + x holds row x (A: token, B: query row) at MFMA k = 16 i + j in bytes
+// j < 16 and k = 64 + 16 i + (j - 16) in bytes j >= 16, and gives the scale of
+// k-block m = i (k in [32 i, 32 i + 32)) for row x.  MFMA s takes
+// d = 128 s + k, so k-block m is the MX group 4 s + m.  From the K tile order
+// (8 values of k-step kk for token t per 8-byte run, at byte
+// (kk / 2) * 1024 + (g' * 16 + t) * 16 + (kk % 2) * 8), the lane's four 8-byte
+// runs of MFMA s are at (2 s + hh) * 1024 + ((2 (i % 2) + u) * 16 + t) * 16
+// + (i / 2) * 8 (bytes 8 (2 hh + u) ..), and its scale is the byte of token t,
+// group 4 s + i.  One asm block that waits for its own reads (see
+// lds_read_part).
+template <int NS>
+__device__ __forceinline__ void lds_read_qmx(uint4 (&c)[2 * NS], uint32_t (&w)[NS], uint32_t ca, uint32_t sa) {
+  static_assert(NS == 1 || NS == 2, "head_dim 128 or 256");
+#define KVQ_R8(o, off) "ds_read_b64 %" #o ", %" #off "\n\t"
+  uint2 r[4 * NS];
+  if constexpr (NS == 1) {
+    asm volatile("ds_read_b64 %0, %5\n\tds_read_b64 %1, %5 offset:256\n\t"
+                 "ds_read_b64 %2, %5 offset:1024\n\tds_read_b64 %3, %5 offset:1280\n\t"
+                 "ds_read_u8 %4, %6\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(w[0])
+                 : "v"(ca), "v"(sa) : "memory");
+  } else {
+    asm volatile("ds_read_b64 %0, %10\n\tds_read_b64 %1, %10 offset:256\n\t"
+                 "ds_read_b64 %2, %10 offset:1024\n\tds_read_b64 %3, %10 offset:1280\n\t"
+                 "ds_read_b64 %4, %10 offset:2048\n\tds_read_b64 %5, %10 offset:2304\n\t"
+                 "ds_read_b64 %6, %10 offset:3072\n\tds_read_b64 %7, %10 offset:3328\n\t"
+                 "ds_read_u8 %8, %11\n\tds_read_u8 %9, %11 offset:4\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+                   "=&v"(r[7]), "=&v"(w[0]), "=&v"(w[1])
+                 : "v"(ca), "v"(sa) : "memory");
+  }
+#undef KVQ_R8
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    c[2 * s] = make_uint4(r[4 * s].x, r[4 * s].y, r[4 * s + 1].x, r[4 * s + 1].y);
+    c[2 * s + 1] = make_uint4(r[4 * s + 2].x, r[4 * s + 2].y, r[4 * s + 3].x, r[4 * s + 3].y);
+  }
+}
+
 // The K codes and scales of the block in `stage`, in the registers and lane
-// order load_k would give.
+// order load_k would give (QMX: in the block-scaled MFMA's order).
 template <int FMT, int D>
 __device__ __forceinline__ void read_stage_k(Buf<FMT, D>& buf, uint32_t stage, int lane) {
   using T = DT<FMT, D>;
   const int g = lane >> 4, c16 = lane & 15;
-  const uint32_t sa = stage + T::SKS + (T::KS_LANE_BYTES > 0 ? c16 * T::KS_LANE_BYTES : g * (4 * T::KSW));
-  lds_read_part<T::KCH, 1024, T::KSW>(buf.k, buf.ks, stage + T::SK + lane * 16, sa);
+  if constexpr (T::QMX) {
+    lds_read_qmx<D / 128>(buf.k, buf.ks, stage + T::SK + ((2 * (g & 1)) * 16 + c16) * 16 + (g >> 1) * 8,
+                          stage + T::SKS + c16 * (D / 32) + g);
+  } else {
+    const uint32_t sa = stage + T::SKS + (T::KS_LANE_BYTES > 0 ? c16 * T::KS_LANE_BYTES : g * (4 * T::KSW));
+    lds_read_part<T::KCH, 1024, T::KSW>(buf.k, buf.ks, stage + T::SK + lane * 16, sa);
+  }
 }
 
 // The V codes and scales of the block in `stage`, as load_v would give them.
@@ -419,6 +470,7 @@ struct QOps {
   // int8 coarse, fine), as raw 16-byte lane values, in registers or in LDS
   using T = DT<FMT, D>;
   uint4 reg[IN_LDS ? 1 : T::QSTEPS * T::QPIECES];
+  uint32_t qsc[T::QMX ? T::QSTEPS : 1];  // QMX: q's UE8M0 this lane gives MFMA s (in bits 0..7)
   const uint4* lds;
   int lane;
   __device__ __forceinline__ uint4 get(int kk, int p) const {
@@ -434,7 +486,18 @@ __device__ __forceinline__ f32x4 qk_block(const Buf<FMT, D>& buf, const Q& qo, i
   using T = DT<FMT, D>;
   f32x4 S = {0.f, 0.f, 0.f, 0.f};
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (T::KC == C_BF16) {
+  if constexpr (T::QMX) {
+    // E4M3 x E4M3 with both UE8M0 scales applied by the instruction (A and B
+    // format 0 = E4M3; scale byte 0 of each lane's word)
+#pragma unroll
+    for (int s = 0; s < T::QSTEPS; ++s) {
+      const uint4 k0 = buf.k[2 * s], k1 = buf.k[2 * s + 1];
+      const uint4 q0 = qo.get(s, 0), q1 = qo.get(s, 1);
+      const i32x8 a = {(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w, (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
+      const i32x8 bq = {(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, (int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w};
+      S = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bq, S, 0, 0, 0, (int)buf.ks[s], 0, (int)qo.qsc[s]);
+    }
+  } else if constexpr (T::KC == C_BF16) {
     // two independent accumulator chains (even / odd k-steps)
     f32x4 S1 = zero;
 #pragma unroll

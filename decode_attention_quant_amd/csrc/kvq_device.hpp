@@ -17,6 +17,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
 typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
 
 template <typename To, typename From>
 __device__ __forceinline__ To bitcast(const From& f) {

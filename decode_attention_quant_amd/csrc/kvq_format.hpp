@@ -66,20 +66,37 @@ enum Format : int {
   F_MXFP4 = 7, F_COUNT = 8
 };
 
+// Kernel variant tag (a template argument, never a descriptor's format):
+// F_MXFP8 | VARIANT_QMX is the MXFP8 cache read with the query rounded to
+// MXFP8 too and Q.K on the block-scaled fp8 matrix cores.  The format
+// predicates below look at the format bits only.
+constexpr int VARIANT_QMX = 0x100;
+KVQ_HD constexpr int base_format(int f) { return f & 0xFF; }
+
 KVQ_HD constexpr int k_codec(int f) {
+  f = base_format(f);
   return f == F_BF16 ? C_BF16 : f == F_INT8_G64 ? C_I8G64 : f == F_FP8_ROW ? C_E4ROW
        : f == F_NVFP4_G16 ? C_E2G16 : f == F_K8V4 ? C_E4ROW : f == F_MXFP8 ? C_E4MX : f == F_MXFP4 ? C_E2MX : C_E4TEN;
 }
 KVQ_HD constexpr int v_codec(int f) {
+  f = base_format(f);
   return f == F_BF16 ? C_F16 : f == F_INT8_G64 ? C_I8G64 : f == F_FP8_ROW ? C_E4ROW
        : f == F_NVFP4_G16 ? C_E2G16 : f == F_K8V4 ? C_E2G16 : f == F_MXFP8 ? C_E4MX : f == F_MXFP4 ? C_E2MX : C_E4TEN;
 }
-KVQ_HD constexpr bool k_rotated(int f) { return f == F_INT8_G64 || f == F_NVFP4_G16 || f == F_MXFP4; }
-KVQ_HD constexpr bool v_rotated(int f) { return f == F_NVFP4_G16 || f == F_K8V4 || f == F_MXFP4; }
+KVQ_HD constexpr bool k_rotated(int f) {
+  return base_format(f) == F_INT8_G64 || base_format(f) == F_NVFP4_G16 || base_format(f) == F_MXFP4;
+}
+KVQ_HD constexpr bool v_rotated(int f) {
+  return base_format(f) == F_NVFP4_G16 || base_format(f) == F_K8V4 || base_format(f) == F_MXFP4;
+}
 // Planes with a per-tensor fp32 scale (the descriptor's k_scale / v_scale):
 // FP8-tensor, and the two-level form of the NVFP4 planes (1 = single level).
-KVQ_HD constexpr bool k_tensor_scaled(int f) { return f == F_FP8_TENSOR || f == F_NVFP4_G16; }
-KVQ_HD constexpr bool v_tensor_scaled(int f) { return f == F_FP8_TENSOR || f == F_NVFP4_G16 || f == F_K8V4; }
+KVQ_HD constexpr bool k_tensor_scaled(int f) {
+  return base_format(f) == F_FP8_TENSOR || base_format(f) == F_NVFP4_G16;
+}
+KVQ_HD constexpr bool v_tensor_scaled(int f) {
+  return base_format(f) == F_FP8_TENSOR || base_format(f) == F_NVFP4_G16 || base_format(f) == F_K8V4;
+}
 
 KVQ_HD constexpr int codec_bits(int c) { return (c == C_BF16 || c == C_F16) ? 16 : (c == C_E2G16 || c == C_E2MX) ? 4 : 8; }
 // the scale is a power of two (UE8M0 byte): codes are scaled exactly by ldexp

@@ -33,6 +33,7 @@ struct DecodeArgs {
   float* out;                 // [B][n_q][H_q][D]
   float* lse;                 // [B][n_q][H_q], nullable
   int32_t write_direct;       // 1: finish units held by one workgroup in the split kernel
+  int32_t q_mx;               // 1: MXFP8 cache read with q rounded to MXFP8 (block-scaled fp8 Q.K)
   // Fused decode step (pool_w non-null): before reading a block, the split
   // workgroup that owns it encodes and stores the new tokens in it, the n_q
   // newest positions L_b - n_q .. L_b - 1 of each sequence, whose slots come

@@ -215,8 +215,19 @@ kvq_status kvq_decode_step(const kvq_cache_desc* desc, void* pool, const void* k
  * workgroup is finished by the split phase (written to out / lse, which
  * kvq_decode_split then needs) and the combine skips it; this is what
  * kvq_decode_attention does.  Without it every unit leaves partials.
- * kvq_decode_split takes out / lse only for that flag (NULL otherwise). */
+ * kvq_decode_split takes out / lse only for that flag (NULL otherwise).
+ * flags & KVQ_SPLIT_Q_MXFP8 (KVQ_MXFP8 caches only, else
+ * KVQ_ERR_UNSUPPORTED): a numerics mode of this library, not of the pages,
+ * which quantize only the cache.  Each query row is first rounded to the
+ * cache's own MXFP8 format (TokenSpeed article, --kv-cache-dtype section:
+ * E4M3 values, one UE8M0 scale per 32 head_dim values, by the OCP MX rule
+ * X = 2^(floor(log2 amax) - 8), round to nearest even, saturating at
+ * 448 X), so that q . k runs on the block-scaled fp8 matrix cores with both
+ * scales applied by the instruction; the result is the attention of the
+ * rounded query (kvq_decode_combine accepts and ignores the flag).  It
+ * applies to kvq_decode_split and kvq_decode_step_split. */
 #define KVQ_SPLIT_WRITE_WHOLE_UNITS 1
+#define KVQ_SPLIT_Q_MXFP8 2
 kvq_status kvq_decode_split(const kvq_cache_desc* desc, const void* pool, const void* q_bf16,
                             int32_t batch, int32_t n_q, int32_t num_q_heads,
                             const int32_t* block_table, int32_t max_pages_per_seq,

@@ -141,7 +141,14 @@ def test_decode_validation_enqueues_nothing():
     assert call(scale=float("nan")) == 1
     assert call(wsb=100) == 3
     assert call(Hq=22) == 1            # not a multiple of H_kv
-    assert call(flags=2) == 1          # unknown flag
+    assert call(flags=4) == 1          # unknown flag
+    assert call(flags=2) == 2          # the query-MXFP8 mode needs an MXFP8 cache
+    assert call(flags=3) == 2
+    mx = kvq.desc(5, 128, 128, 32, 100)
+    assert lib.kvq_decode_split(ctypes.byref(mx), ok, ok, 0, 4, 32, ok, 10, ok, 0.1, 4, 2, None, None, ok,
+                                1 << 30, None) == 0  # accepted (empty batch: nothing to do)
+    assert lib.kvq_decode_combine(ctypes.byref(mx), 0, 4, 32, 10, ok, 4, 3, ok, 1 << 30, ok, None, None) == 0
+    assert lib.kvq_decode_combine(ctypes.byref(mx), 0, 4, 32, 10, ok, 4, 4, ok, 1 << 30, ok, None, None) == 1
     assert call(flags=1, out=None) == 1  # finishing whole units needs out
     bad = kvq.desc(3, 128, 64, 4, 100)
     assert lib.kvq_decode_split(ctypes.byref(bad), ok, ok, 2, 1, 24, ok, 10, ok, 0.1, 4, 0, None, None, ok,
