@@ -237,9 +237,10 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
     const cint32* bt_row = as_const(a.block_table) + (int64_t)b * a.max_pages;
 
     // ---- start-up latencies overlap: the page numbers of this wave's first
-    //      blocks and the query rows are loaded together; a rotated query
-    //      is transformed as soon as it lands, and the copies of the first
-    //      S - 1 blocks go out before the rest of the query setup
+    //      blocks and the query rows are loaded together, and the first
+    //      blocks' copies go out before the query setup (for a rotated query
+    //      on a ring, only the first block's: the others would stall the
+    //      wave while the memory queues are full, so they follow the setup)
     //      All of these loads are issued on every path (indexes past the end
     //      are clamped to valid ones, whose data is then not used), so that
     //      the compiler can count them exactly and does not drain every
@@ -252,10 +253,13 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
       for (int k = 0; k < T::RING_S - 1; ++k)
         pre[k] = block_addr(head0, geo, bt_row, min(blk0 + wave + 4 * k, blk0 + nblk - 1));
     }
-    auto stage_first = [&]() {  // blocks k >= nk land in stages that are never read
+    // copies of this wave's blocks k0 .. k1 - 1 (blocks k >= nk land in
+    // stages that are never read)
+    auto stage_first = [&](int k0, int k1) {
       if constexpr (T::RING) {
 #pragma unroll
-        for (int k = 0; k < T::RING_S - 1; ++k) stage_block_at<FMT, D>(ring0 + k * T::STAGE, pre[k], geo, lane);
+        for (int k = 0; k < T::RING_S - 1; ++k)
+          if (k >= k0 && k < k1) stage_block_at<FMT, D>(ring0 + k * T::STAGE, pre[k], geo, lane);
       }
     };
     QOps<FMT, D> qo;
@@ -277,7 +281,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
         if (row_ok) q4 = *reinterpret_cast<const uint4*>(qp + 128 * (i >> 2) + 64 * ((i >> 1) & 1) + 16 * g + 8 * (i & 1));
         qraw[i] = q4;
       }
-      stage_first();
+      stage_first(0, T::RING_S - 1);
 #pragma unroll
       for (int s = 0; s < T::QSTEPS; ++s) {
         uint32_t sb[2], w[8];
@@ -323,7 +327,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
         if (row_ok) q4 = *reinterpret_cast<const uint4*>(qp + 32 * kk + 8 * g);
         qv[kk] = q4;
       }
-      stage_first();
+      stage_first(0, T::RING_S - 1);
       // Take the query operands here, not at their first use inside the
       // block loop: a register load still pending at the loop entry makes
       // the compiler wait for every load (vmcnt 0) in each iteration, which
@@ -338,13 +342,31 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
       // above while the first blocks are in flight; otherwise row `row` of
       // the merge area.  max|q'| of row `row` goes to qexp[row].
       static_assert(E == 4, "the rotation is 256-point");
-      uint2 qraw[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      auto qrow_ptr = [&](int i) -> const uint16_t* {
         const int row = wave + 4 * i < Rt ? wave + 4 * i : 0;  // rows past Rt load row 0, unused
         const int rr2 = 16 * rt + row;
         const int i2 = rr2 / a.G, h2 = h * a.G + (rr2 - i2 * a.G);
-        qraw[i] = *reinterpret_cast<const uint2*>(a.q + (((int64_t)b * a.n_q + i2) * a.H_q + h2) * D + E * lane);
+        return a.q + (((int64_t)b * a.n_q + i2) * a.H_q + h2) * D;
+      };
+      uint2 qraw[4];
+      if constexpr (T::RING) {
+        // The raw rows come in by the same direct copies as the blocks, into
+        // the last stage of this wave's ring (row wave + 4 i at byte 512 i,
+        // two rows per copy), and the first block's copies go out right
+        // behind them.  Copies complete in order, so an explicit wait for
+        // all but the block's leaves those in flight: a register load here
+        // would make the compiler wait for every copy issued after it.
+        const uint32_t qstage = ring0 + (T::RING_S - 1) * T::STAGE;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          __builtin_amdgcn_global_load_lds((gbl_void_t*)(qrow_ptr(2 * j + (lane >> 5)) + 8 * (lane & 31)),
+                                           (lds_void_t*)(uintptr_t)(qstage + 1024 * j), 16, 0, 0);
+        stage_first(0, 1);
+        wait_vmcnt<T::NDMA>();
+        lds_get_rows4(qstage + 8 * lane, qraw);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qraw[i] = *reinterpret_cast<const uint2*>(qrow_ptr(i) + E * lane);
       }
       float xq[4][E], amx[4];
 #pragma unroll
@@ -356,12 +378,10 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
           float am = 0.f;
 #pragma unroll
           for (int e = 0; e < E; ++e) { xq[i][e] *= 0.0625f; am = fmaxf(am, fabsf(xq[i][e])); }
-#pragma unroll
-          for (int m = 1; m < 64; m <<= 1) am = fmaxf(am, __shfl_xor(am, m));
+          am = wave_max(am);
           amx[i] = am;
         }
       }
-      stage_first();
       const uint32_t qexp_a = (uint32_t)(uintptr_t)(void*)qexp;
       auto qrow_a = [&](int row) -> uint32_t {  // LDS byte address of row `row` (ring formats)
         return (uint32_t)(uintptr_t)(void*)sm_o +
@@ -445,6 +465,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
           qv[2 * kk + 1] = bitcast<uint4>(ql16);
         }
       }
+      // the other first blocks, once the query no longer needs the wave
+      stage_first(1, T::RING_S - 1);
     }
     if constexpr (T::QLDS) {
       __syncthreads();  // every wave has finished reading qrot / the previous segment's store

@@ -176,7 +176,7 @@ __device__ __forceinline__ void copy_plane(uint32_t dst, const uint8_t* src, int
                                      (lds_void_t*)(uintptr_t)(dst + c * 1024), 16, 0, 0);
   constexpr int REM = BYTES % 1024;
   if constexpr (REM > 0) {
-    if (lane < REM / 16)
+    if (lane < REM / 16)  // lane 0 always copies: the instruction is always issued
       __builtin_amdgcn_global_load_lds((gbl_void_t*)(src + (BYTES / 1024) * 1024 + lane * 16),
                                        (lds_void_t*)(uintptr_t)(dst + (BYTES / 1024) * 1024), 16, 0, 0);
   }
@@ -218,6 +218,12 @@ __device__ __forceinline__ void lds_get8(uint32_t addr, float (&x)[8]) {
                : "=&v"(lo), "=&v"(hi) : "v"(addr) : "memory");
   x[0] = __uint_as_float(lo.x); x[1] = __uint_as_float(lo.y); x[2] = __uint_as_float(lo.z); x[3] = __uint_as_float(lo.w);
   x[4] = __uint_as_float(hi.x); x[5] = __uint_as_float(hi.y); x[6] = __uint_as_float(hi.z); x[7] = __uint_as_float(hi.w);
+}
+// Four 8-byte reads at addr + 512 i (i < 4), waiting for them.
+__device__ __forceinline__ void lds_get_rows4(uint32_t addr, uint2 (&x)[4]) {
+  asm volatile("ds_read_b64 %0, %4\n\tds_read_b64 %1, %4 offset:512\n\tds_read_b64 %2, %4 offset:1024\n\t"
+               "ds_read_b64 %3, %4 offset:1536\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]) : "v"(addr) : "memory");
 }
 __device__ __forceinline__ float lds_get1(uint32_t addr) {
   uint32_t v;
@@ -683,8 +689,31 @@ __device__ __forceinline__ f16x4 v_operand(const Buf<FMT, D>& buf, int nt, int l
 }
 
 // ----------------------------------------------------------- 64-lane FWHT
-// Unnormalized-order-free Hadamard (any fp32 order is fine on the read
-// path): lane l holds elements E*l .. E*l+E-1 of a 64*E vector.
+
+// One butterfly stage across lanes M apart: the lower lane of each pair
+// keeps x + partner and the upper one partner - x, each rounded once.
+// M <= 8 is a DPP permutation inside a row of 16 lanes; M = 16 and 32 use
+// the swap instructions, which leave the lower lane's value in result 0
+// and the upper lane's in result 1, in both lanes of the pair.
+template <int M>
+__device__ __forceinline__ float xlane_butterfly(float x, int lane) {
+  const float sg = (lane & M) ? -1.0f : 1.0f;
+  if constexpr (M <= 8) {
+    return __builtin_fmaf(sg, x, lane_xor<M>(x));
+  } else {
+    static_assert(M == 16 || M == 32, "");
+    const uint32_t v = bitcast<uint32_t>(x);
+    const auto s = M == 16 ? __builtin_amdgcn_permlane16_swap(v, v, false, false)
+                           : __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return __builtin_fmaf(sg, bitcast<float>((uint32_t)s[1]), bitcast<float>((uint32_t)s[0]));
+  }
+}
+
+// Unnormalized Hadamard of a 64*E vector, lane l holding elements
+// E*l .. E*l+E-1 (any fp32 order is fine on the read path).  No LDS: the
+// cross-lane stages are register permutations, so a transform costs a few
+// dozen instructions instead of a chain of LDS round trips.  Needs the
+// whole wave active.
 template <int E>
 __device__ __forceinline__ void fwht_wave(float (&x)[E], int lane) {
 #pragma unroll
@@ -697,13 +726,13 @@ __device__ __forceinline__ void fwht_wave(float (&x)[E], int lane) {
         x[i + h] = a - b;
       }
 #pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const bool upper = (lane & m) != 0;
-#pragma unroll
-    for (int i = 0; i < E; ++i) {
-      const float p = __shfl_xor(x[i], m);
-      x[i] = upper ? (p - x[i]) : (x[i] + p);
-    }
+  for (int i = 0; i < E; ++i) {
+    x[i] = xlane_butterfly<1>(x[i], lane);
+    x[i] = xlane_butterfly<2>(x[i], lane);
+    x[i] = xlane_butterfly<4>(x[i], lane);
+    x[i] = xlane_butterfly<8>(x[i], lane);
+    x[i] = xlane_butterfly<16>(x[i], lane);
+    x[i] = xlane_butterfly<32>(x[i], lane);
   }
 }
 
@@ -715,6 +744,15 @@ __device__ __forceinline__ float max_over_g(float x) {
   x = fmaxf(bitcast<float>((uint32_t)a[0]), bitcast<float>((uint32_t)a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(bitcast<uint32_t>(x), bitcast<uint32_t>(x), false, false);
   return fmaxf(bitcast<float>((uint32_t)b[0]), bitcast<float>((uint32_t)b[1]));
+}
+
+// Maximum over the whole wave (every lane gets it); needs the whole wave active.
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, lane_xor<1>(x));
+  x = fmaxf(x, lane_xor<2>(x));
+  x = fmaxf(x, lane_xor<4>(x));
+  x = fmaxf(x, lane_xor<8>(x));
+  return max_over_g(x);
 }
 
 // Slack of the running maximum, in log2 units (see pv_phase).

@@ -55,4 +55,36 @@ __device__ __forceinline__ float e4m3_value(uint32_t code) {
   return __builtin_amdgcn_cvt_pk_f32_fp8((int)code, false)[0];
 }
 
+// ----------------------------------------------------------- DPP lane exchange
+
+constexpr int QUAD_XOR1 = 0xB1;  // DPP quad_perm [1, 0, 3, 2]
+constexpr int QUAD_XOR2 = 0x4E;  // DPP quad_perm [2, 3, 0, 1]
+constexpr int ROW_SHL4 = 0x104;  // lane i reads lane i + 4 of its row of 16
+constexpr int ROW_SHR4 = 0x114;  // lane i reads lane i - 4
+constexpr int ROW_ROR8 = 0x128;  // lane i reads lane (i + 8) mod 16
+
+template <int CTRL>
+__device__ __forceinline__ float quad_swap(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// The value of lane (i ^ M) of the same row of 16 lanes, M in {1, 2, 4, 8}.
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) {
+  if constexpr (M == 1) return quad_swap<QUAD_XOR1>(v);
+  else if constexpr (M == 2) return quad_swap<QUAD_XOR2>(v);
+  else if constexpr (M == 8) return quad_swap<ROW_ROR8>(v);
+  else {
+    static_assert(M == 4, "");
+    // lanes 0-3 and 8-11 (banks 0, 2) read i + 4; lanes 4-7 and 12-15 read i - 4
+    const int lo = __builtin_amdgcn_update_dpp(0, __float_as_int(v), ROW_SHL4, 0xF, 0x5, false);
+    return __int_as_float(__builtin_amdgcn_update_dpp(lo, __float_as_int(v), ROW_SHR4, 0xF, 0xA, false));
+  }
+}
+
+template <int M>
+__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v) {
+  return __float_as_uint(lane_xor<M>(__uint_as_float(v)));
+}
+
 }  // namespace kvq

@@ -121,8 +121,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(Geometry geo, DecodeArg
         float am = 0.f;
 #pragma unroll
         for (int i = 0; i < E; ++i) { xq[i] *= 0.0625f; am = fmaxf(am, fabsf(xq[i])); }
-#pragma unroll
-        for (int m = 1; m < 64; m <<= 1) am = fmaxf(am, __shfl_xor(am, m));
+        am = wave_max(am);
 #pragma unroll
         for (int i = 0; i < E; ++i) wbuf[r * D + E * lane + i] = xq[i];
         if (lane == 0) hdr[32 + 8 * pass + r] = am;
