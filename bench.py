@@ -35,6 +35,7 @@ what the same counters read for the probe's copy kernel of known size.
 """
 
 import argparse
+import gc
 import csv
 import glob
 import hashlib
@@ -192,6 +193,18 @@ def time_steps(s, steps, warmup, stream, probe=None, fused=True):
     With a probe, its cache-evicting read runs before each step, outside
     the step's events; the wall time between the first and last step then
     includes those reads."""
+    # no garbage collection while steps are being launched: a collector pause
+    # between the launches of one step would show up as GPU idle time inside
+    # its events (seen as single steps of tens of ms)
+    gc.collect()
+    gc.disable()
+    try:
+        return _time_steps(s, steps, warmup, stream, probe, fused)
+    finally:
+        gc.enable()
+
+
+def _time_steps(s, steps, warmup, stream, probe, fused):
     with torch.cuda.stream(stream):
         for _ in range(warmup):
             if probe is not None:

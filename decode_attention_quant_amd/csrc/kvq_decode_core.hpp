@@ -42,13 +42,13 @@ struct DT {
   static constexpr int NDMA = (KB + 1023) / 1024 + (KSB + 1023) / 1024 + (VB + 1023) / 1024 + (VSB + 1023) / 1024;
   // Blocks are staged through a per-wave ring of RING_S blocks in LDS,
   // RING_S - 1 of them in flight while one is consumed, where that fits in
-  // RING_LDS bytes per workgroup (two workgroups per CU).  INT8-G64 keeps
-  // its register pipeline: with q in two int8 pieces its loop is shorter
-  // than the ring's extra LDS reads and waits cost (measured).
+  // RING_LDS bytes per workgroup (two workgroups per CU).  (INT8-G64 first
+  // measured faster on its register pipeline; with the start-up and pacing
+  // of the current kernel the ring is 4% faster for it too.)
   static constexpr int RING_LDS = 72 * 1024;
   static constexpr int RING_FIT = RING_LDS / (4 * STAGE);
   static constexpr int RING_S = RING_FIT > 4 ? 4 : RING_FIT;
-  static constexpr bool RING = RING_S >= 2 && FMT != F_INT8_G64;
+  static constexpr bool RING = RING_S >= 2;
   static_assert(!QMX || RING, "the query-MXFP8 variant reads K from the LDS ring");
   // Without the ring: Q operands in LDS (one ds_read_b128 per k-step) where
   // registers would otherwise spill.
