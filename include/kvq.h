@@ -268,7 +268,13 @@ kvq_status kvq_prefill_attention(const kvq_cache_desc* desc, const void* pool, c
                                  hipStream_t stream);
 
 /* The plan kvq_decode_attention uses for this problem on the current device:
- * split workgroups and partial slots. */
+ * split workgroups and partial slots.  The planned grid is one workgroup
+ * per (sequence, kv head) unit when a unit holds at most 256 blocks of 16
+ * tokens (max_pages_per_seq x page_size / 16) and there are at least as
+ * many units as the device holds workgroups at once (CUs x resident
+ * workgroups per CU); otherwise one whole round of resident workgroups, or
+ * two rounds when the units hold more than 256 blocks per resident
+ * workgroup. */
 kvq_status kvq_decode_plan(const kvq_cache_desc* desc, int32_t batch, int32_t n_q,
                            int32_t num_q_heads, int32_t max_pages_per_seq,
                            int32_t* num_workgroups, int32_t* num_slots);
