@@ -141,3 +141,56 @@ def test_full_size_query_mxfp8_mode():
         ref, ref_lse = oracle_unit(c, geo, pool, b, h, q_mxfp8=True)
         assert_close(o_all[b, :, h * G:(h + 1) * G, :], ref, "full-size MTP query-MXFP8 unit (%d, %d)" % (b, h))
         assert_lse_close(l_all[b, :, h * G:(h + 1) * G], ref_lse, "full-size MTP query-MXFP8 unit (%d, %d)" % (b, h))
+
+
+def test_full_size_chunk_append_and_prefill():
+    """The bench's prefill workload at full size: 64 sequences of the mixed
+    K8V4 cache each get a 2048-token chunk appended (the quant-append
+    measurement), then the chunk's queries attend causally over the cache
+    (the prefill measurement).  For sampled units the chunk's stored bytes
+    are checked against the oracle's encoding, and sampled query rows
+    against the oracle's attention."""
+    require_gpu()
+    chunk = 2048
+    note("full-size prefill case")
+    c = W.make_case(4, "K8V4", device="cuda", n_q=chunk, reserve=chunk)
+    geo = OL.Geometry(c.fmt, c.D, c.P, c.H_kv)
+    d = kvq.desc(c.fmt, c.D, c.P, c.H_kv, c.num_pages, c.k_scale, c.v_scale)
+    pool = kvq.alloc_pool(d)
+    kvq.quantize_append(d, pool, c.k, c.v, c.slot_mapping)
+    k, v, slots = W.append_chunk(c, chunk, device="cuda")
+    note("full-size chunk append", k.shape[0], "tokens")
+    kvq.quantize_append(d, pool, k, v, slots)
+    lens = c.seq_lens.astype(np.int64) + chunk
+    bt = torch.as_tensor(c.block_table, device="cuda")
+    sl = torch.as_tensor(lens.astype(np.int32), device="cuda")
+    out = torch.full(c.q.shape, float("nan"), device="cuda")
+    note("full-size prefill")
+    kvq.prefill_attention(d, pool, c.q, bt, sl, c.softmax_scale, out=out)
+    torch.cuda.synchronize()
+    G = c.H_q // c.H_kv
+    starts = np.concatenate([[0], np.cumsum(c.seq_lens.astype(np.int64))])
+    for b, h in sampled_units(c):
+        L0, L = int(c.seq_lens[b]), int(lens[b])
+        note("oracle prefill unit", (b, h), "cached", L0)
+        kb = np.concatenate([W.bf16_bits(c.k[starts[b]:starts[b + 1], h]), W.bf16_bits(k[b * chunk:(b + 1) * chunk, h])])
+        vb = np.concatenate([W.bf16_bits(c.v[starts[b]:starts[b + 1], h]), W.bf16_bits(v[b * chunk:(b + 1) * chunk, h])])
+        kc, ks = OF.encode_rows(geo.kc, geo.k_rot, bf16_bits_to_f32(kb), c.k_scale)
+        vc, vs = OF.encode_rows(geo.vc, geo.v_rot, bf16_bits_to_f32(vb), c.v_scale)
+        # the chunk's bytes as stored by the GPU
+        npg = -(-L // c.P)
+        pages = c.block_table[b, :npg].astype(np.int64)
+        mini = pool.view(c.num_pages, -1)[torch.as_tensor(pages, device="cuda")].cpu().numpy().reshape(-1)
+        new = np.arange(L0, L)
+        got = OL.read_rows(mini, geo, new, h)
+        for name, g, r in zip(("K codes", "K scales", "V codes", "V scales"), got, (kc, ks, vc, vs)):
+            assert np.array_equal(np.asarray(g).astype(np.int64), np.asarray(r)[L0:].astype(np.int64)), \
+                "chunk of unit (%d, %d): %s differ" % (b, h, name)
+        K = OF.decode_rows(geo.kc, geo.k_rot, kc, ks, c.k_scale)
+        V = OF.decode_rows(geo.vc, geo.v_rot, vc, vs, c.v_scale)
+        q = bf16_bits_to_f32(W.bf16_bits(c.q[b, :, h * G:(h + 1) * G, :])).astype(np.float64)
+        o = out[b, :, h * G:(h + 1) * G, :].cpu().numpy()
+        for i in (0, chunk // 2 + 7, chunk - 1):  # query i sits at position L0 + i
+            p = L0 + i
+            ref, _ = OA.attend(q[i:i + 1], K[:p + 1], V[:p + 1], c.softmax_scale, 1)
+            assert_close(o[i:i + 1], ref, "full-size prefill unit (%d, %d) query %d" % (b, h, i))
