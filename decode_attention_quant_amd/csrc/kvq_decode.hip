@@ -408,14 +408,16 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
       if constexpr (T::RING) __builtin_amdgcn_s_barrier();
       else __syncthreads();
       // 8 consecutive elements d0 .. d0 + 7 of this lane's row r
-      auto row8 = [&](int d0, float (&x)[8]) {
-        if constexpr (T::RING) {
-          lds_get8(qrow_a(r) + 4 * d0, x);
-        } else {
+      // xr[k][e] = element 32 k + 8 g + e of this lane's row r (all at once)
+      float xr[8][8];
+      if constexpr (T::RING) {
+        lds_get_8x8(qrow_a(r) + 32 * g, xr);
+      } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = sm_o[r * D + d0 + e];
-        }
-      };
+        for (int k = 0; k < 8; ++k)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xr[k][e] = sm_o[r * D + 32 * k + 8 * g + e];
+      }
       float am = 0.f;
       if (row_ok) {
         if constexpr (T::RING) am = lds_get1(qexp_a + 4 * r);
@@ -429,14 +431,11 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
 #pragma unroll
         for (int kk = 0; kk < T::QSTEPS; ++kk) {
           uint32_t w1[4] = {0, 0, 0, 0}, w2[4] = {0, 0, 0, 0};
-          float xa[8], xb[8];
           // k-slot 16g + j of int8 k-step kk <-> d as laid out in the K chunk:
           // j < 8 at 64 kk + 8 g + j, else at 64 kk + 32 + 8 g + (j - 8)
-          row8(64 * kk + 8 * g, xa);
-          row8(64 * kk + 32 + 8 * g, xb);
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
-            const float v = row_ok ? (j < 8 ? xa[j] : xb[j - 8]) * inv : 0.f;
+            const float v = row_ok ? (j < 8 ? xr[2 * kk][j] : xr[2 * kk + 1][j - 8]) * inv : 0.f;
             const float c1 = fmaxf(fminf(rintf(v), 127.f), -127.f);
             const float c2 = fmaxf(fminf(rintf((v - c1) * 254.0f), 127.f), -127.f);
             w1[j >> 2] |= ((uint32_t)(int)c1 & 0xFFu) << (8 * (j & 3));
@@ -452,12 +451,10 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
         if (row_ok) crow = a.qk_scale * ldexpf(1.0f, ex - 8);
 #pragma unroll
         for (int kk = 0; kk < T::QSTEPS; ++kk) {
-          float x8[8];
-          row8(32 * kk + 8 * g, x8);
           f16x8 qh16, ql16;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float v = row_ok ? ldexpf(x8[e], 8 - ex) : 0.f;
+            const float v = row_ok ? ldexpf(xr[kk][e], 8 - ex) : 0.f;
             qh16[e] = (_Float16)v;
             ql16[e] = (_Float16)(v - (float)qh16[e]);
           }
@@ -620,8 +617,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
     // ---- merge the 4 waves (the workgroup waits on its barriers: above the
     //      other workgroup's streaming waves, below a starting segment)
     __builtin_amdgcn_s_setprio(2);
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
+    l_run = sum_over_g(l_run);
     if (lane < 16) {
       sm_m[wave * 16 + lane] = m_run;
       sm_l[wave * 16 + lane] = l_run;
@@ -641,15 +637,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
       }
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < Rt * D; idx += 256) {
-      float o = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < 4; ++ww) o += sm_o[ww * Rt * D + idx];
-      sm_o[idx] = o;  // wave-0 slot of this element; read by this thread only
-    }
-    __syncthreads();
 
-    // ---- write: one wave per row
+    // ---- write: one wave per row, summing the 4 waves' rescaled parts
     const bool direct = whole && a.write_direct;
     for (int row = wave; row < Rt; row += 4) {
       float M = NEG_INF;
@@ -665,6 +654,10 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
       float xo[E];
 #pragma unroll
       for (int i = 0; i < E; ++i) xo[i] = sm_o[row * D + E * lane + i];
+#pragma unroll
+      for (int ww = 1; ww < 4; ++ww)
+#pragma unroll
+        for (int i = 0; i < E; ++i) xo[i] += sm_o[(ww * Rt + row) * D + E * lane + i];
       if (!direct) {
         const int64_t prow = (int64_t)(u + w) * a.R + rr2;
         float* op = a.ws_o + prow * D + E * lane;

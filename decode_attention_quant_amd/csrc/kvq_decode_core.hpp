@@ -212,13 +212,31 @@ __device__ __forceinline__ void lds_put4(uint32_t addr, float x0, float x1, floa
 __device__ __forceinline__ void lds_put1(uint32_t addr, float x) {
   asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(addr), "v"(__float_as_uint(x)) : "memory");
 }
-__device__ __forceinline__ void lds_get8(uint32_t addr, float (&x)[8]) {
-  uint4 lo, hi;
-  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:16\n\ts_waitcnt lgkmcnt(0)"
-               : "=&v"(lo), "=&v"(hi) : "v"(addr) : "memory");
-  x[0] = __uint_as_float(lo.x); x[1] = __uint_as_float(lo.y); x[2] = __uint_as_float(lo.z); x[3] = __uint_as_float(lo.w);
-  x[4] = __uint_as_float(hi.x); x[5] = __uint_as_float(hi.y); x[6] = __uint_as_float(hi.z); x[7] = __uint_as_float(hi.w);
+// x[k][0..7] = the 8 floats at addr + 128 k (k < 8): 16 reads, one wait.
+__device__ __forceinline__ void lds_get_8x8(uint32_t addr, float (&x)[8][8]) {
+  uint4 r[16];
+  asm volatile("ds_read_b128 %0, %16\n\tds_read_b128 %1, %16 offset:16\n\t"
+               "ds_read_b128 %2, %16 offset:128\n\tds_read_b128 %3, %16 offset:144\n\t"
+               "ds_read_b128 %4, %16 offset:256\n\tds_read_b128 %5, %16 offset:272\n\t"
+               "ds_read_b128 %6, %16 offset:384\n\tds_read_b128 %7, %16 offset:400\n\t"
+               "ds_read_b128 %8, %16 offset:512\n\tds_read_b128 %9, %16 offset:528\n\t"
+               "ds_read_b128 %10, %16 offset:640\n\tds_read_b128 %11, %16 offset:656\n\t"
+               "ds_read_b128 %12, %16 offset:768\n\tds_read_b128 %13, %16 offset:784\n\t"
+               "ds_read_b128 %14, %16 offset:896\n\tds_read_b128 %15, %16 offset:912\n\t"
+               "s_waitcnt lgkmcnt(0)"
+               : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+                 "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]),
+                 "=&v"(r[14]), "=&v"(r[15])
+               : "v"(addr) : "memory");
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint4 lo = r[2 * k], hi = r[2 * k + 1];
+    x[k][0] = __uint_as_float(lo.x); x[k][1] = __uint_as_float(lo.y); x[k][2] = __uint_as_float(lo.z);
+    x[k][3] = __uint_as_float(lo.w); x[k][4] = __uint_as_float(hi.x); x[k][5] = __uint_as_float(hi.y);
+    x[k][6] = __uint_as_float(hi.z); x[k][7] = __uint_as_float(hi.w);
+  }
 }
+
 // Four 8-byte reads at addr + 512 i (i < 4), waiting for them.
 __device__ __forceinline__ void lds_get_rows4(uint32_t addr, uint2 (&x)[4]) {
   asm volatile("ds_read_b64 %0, %4\n\tds_read_b64 %1, %4 offset:512\n\tds_read_b64 %2, %4 offset:1024\n\t"
@@ -355,7 +373,6 @@ __device__ __forceinline__ void lds_read_part(uint4 (&c)[NC], uint32_t (&w)[SW >
 template <int NS>
 __device__ __forceinline__ void lds_read_qmx(uint4 (&c)[2 * NS], uint32_t (&w)[NS], uint32_t ca, uint32_t sa) {
   static_assert(NS == 1 || NS == 2, "head_dim 128 or 256");
-#define KVQ_R8(o, off) "ds_read_b64 %" #o ", %" #off "\n\t"
   uint2 r[4 * NS];
   if constexpr (NS == 1) {
     asm volatile("ds_read_b64 %0, %5\n\tds_read_b64 %1, %5 offset:256\n\t"
@@ -373,7 +390,6 @@ __device__ __forceinline__ void lds_read_qmx(uint4 (&c)[2 * NS], uint32_t (&w)[N
                    "=&v"(r[7]), "=&v"(w[0]), "=&v"(w[1])
                  : "v"(ca), "v"(sa) : "memory");
   }
-#undef KVQ_R8
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     c[2 * s] = make_uint4(r[4 * s].x, r[4 * s].y, r[4 * s + 1].x, r[4 * s + 1].y);
@@ -744,6 +760,15 @@ __device__ __forceinline__ float max_over_g(float x) {
   x = fmaxf(bitcast<float>((uint32_t)a[0]), bitcast<float>((uint32_t)a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(bitcast<uint32_t>(x), bitcast<uint32_t>(x), false, false);
   return fmaxf(bitcast<float>((uint32_t)b[0]), bitcast<float>((uint32_t)b[1]));
+}
+
+// Sum over the four lanes 16 g + c (g = 0..3) that share c (same swaps as
+// max_over_g; every lane gets the sum).
+__device__ __forceinline__ float sum_over_g(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(bitcast<uint32_t>(x), bitcast<uint32_t>(x), false, false);
+  x = bitcast<float>((uint32_t)a[0]) + bitcast<float>((uint32_t)a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(bitcast<uint32_t>(x), bitcast<uint32_t>(x), false, false);
+  return bitcast<float>((uint32_t)b[0]) + bitcast<float>((uint32_t)b[1]);
 }
 
 // Maximum over the whole wave (every lane gets it); needs the whole wave active.

@@ -12,7 +12,7 @@ import torch
 
 import decode_attention_quant_amd as kvq
 import workloads as W
-from _gpu_common import (assert_close, assert_lse_close, build, note, oracle_attention, W_name)
+from _gpu_common import (assert_close, assert_lse_close, build, note, oracle_attention, require_gpu, W_name)
 
 pytestmark = pytest.mark.gpu
 
@@ -208,3 +208,17 @@ def test_scores_that_climb_and_jump(fmt, cfg):
     ref, ref_lse = oracle_attention(bl)
     assert_close(out, ref, "climbing scores " + W_name(c))
     assert_lse_close(lse, ref_lse, "climbing scores " + W_name(c))
+
+
+def test_planned_grid_is_whole_rounds_or_one_per_unit():
+    """The planner's grid: whole rounds of resident workgroups (one, or two
+    when the cache's upper bound exceeds 256 blocks per resident workgroup),
+    or one workgroup per unit for many units of at most 256 blocks."""
+    require_gpu()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    one, _ = kvq.decode_plan(kvq.desc(3, 256, 64, 4, 4097), 1, 1, 24, 4096)        # 4 units x 16384 blocks
+    two, _ = kvq.decode_plan(kvq.desc(3, 256, 64, 4, 16385), 32, 1, 24, 512)       # 128 units x 2048 blocks
+    assert one % cus == 0 and one // cus >= 1
+    assert two == 2 * one
+    per_unit, slots = kvq.decode_plan(kvq.desc(5, 128, 128, 32, 8193), 256, 4, 32, 32)  # 8192 units x 256 blocks
+    assert per_unit == 256 * 32 and slots == 2 * 256 * 32
