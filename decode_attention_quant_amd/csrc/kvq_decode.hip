@@ -26,12 +26,20 @@
 //     INT8-G64        int8 K x rotated q in two int8 digits (16x16x64 i8),
 //                     group scale on each 64-wide integer partial sum
 //     NVFP4 (K)       E2M1 x UE4M3 -> f16 (exact) x rotated q as f16 hi + lo
+//     MXFP4 (K)       E2M1 x 2^e -> f16 by the scaled conversion (exact) x
+//                     rotated q as f16 hi + lo
+//     MXFP8, query-MXFP8 mode: E4M3 K x E4M3 q on the block-scaled fp8
+//                     MFMA, both UE8M0 scales applied by the instruction
 //   online softmax in base 2, masking t >= L and the MTP causal rule;
 //   O (16 rows x D) += P . V_blk (16x16x16 f16), P rounded to f16 and V
 //   expanded to f16 with its scale folded in: exact for fp16 V and for
 //   E2M1 x UE4M3; one f16 rounding of code x scale for int8 and E4M3 with
-//   an fp16 scale and for E4M3 x 2^e; the per-tensor V scale multiplies the
-//   output instead.
+//   an fp16 scale and for E4M3 x 2^e; the per-tensor V scale (and the
+//   second level of two-level NVFP4) multiplies the output instead.
+//
+// Blocks reach a wave through its ring of LDS stages (direct global -> LDS
+// copies, S - 1 blocks in flight), except BF16 at head_dim 256, whose
+// blocks do not fit and go through registers.
 #include <hip/hip_runtime.h>
 
 #include "kvq_decode_core.hpp"
