@@ -7,16 +7,20 @@ over every cached page and the cross-split combine.  Inputs are resident in
 HBM before timing starts, and before every timed step a 1 GiB read evicts
 the L2 caches and the 256 MB MALL, so each step streams the cache from HBM
 as it would between two layers of a model (``--no-flush`` times the steps
-back to back instead).  The default workload is the batched decode:
-32 sequences with contexts drawn uniformly from 8K-32K tokens, 24 query /
-4 KV heads, head_dim 256, 64-token pages, for each of INT8-G64, FP8 row-256
-and per-tensor FP8 (the headline value is INT8-G64).
+back to back instead).  By default every decode workload is timed, for each
+of its kv-dtypes, and reported under ``per_workload``: tiny (1 x 1024, BF16
+and FP8 row-256: a latency), batched (32 x U[8K, 32K] tokens, INT8-G64, FP8
+row-256, per-tensor FP8), long (1 x 262144 tokens: NVFP4-G16, two-level
+NVFP4, MXFP4), long8 (8 x 65536, NVFP4-G16), mixed (64 x logU[1K, 128K],
+K8V4) and mtp (256 x 4096, 4 query tokens, MHA, MXFP8 plain and with the
+query rounded to MXFP8).  The headline value is the batched decode's
+INT8-G64 step (24 query / 4 KV heads, head_dim 256, 64-token pages).
 
 The write path is measured on its own workload: one 2048-token prefill chunk
 for each of 64 mixed-length sequences (log-uniform 1K-128K cached tokens,
 chunks starting mid-page), K8V4 first, then the other formats at that shape.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload batched]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload all|batched|long|...]
 
 Prints one JSON line.  ``value`` is effective compressed-KV bandwidth:
 sum_b H_kv * L_b * bytes_per_token / ms_per_step.  ``roofline`` prices the
@@ -161,25 +165,29 @@ class Probe:
         self.p.read(self.buf, self.sink, stream)
 
     def rates(self, stream, reps=10):
-        """Median GB/s of the read scan over 4 GiB and of a 2 GiB copy (read
-        + write counted), on a buffer freed afterwards."""
+        """Median GB/s of the read scan over 4 GiB with plain loads and with
+        the non-temporal hint (the decode copies carry it), and of a 2 GiB
+        copy (read + write counted), on a buffer freed afterwards."""
         buf = torch.ones(RATE_BYTES, dtype=torch.uint8, device="cuda")
-        rd, cp = [], []
+        rd, nt, cp = [], [], []
         with torch.cuda.stream(stream):
             for i in range(reps + 2):
-                e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
                 e[0].record(stream)
                 self.p.read(buf, self.sink, stream)
                 e[1].record(stream)
-                self.p.copy(buf[COPY_BYTES:], buf[:COPY_BYTES], stream)
+                self.p.read(buf, self.sink, stream, nontemporal=True)
                 e[2].record(stream)
+                self.p.copy(buf[COPY_BYTES:], buf[:COPY_BYTES], stream)
+                e[3].record(stream)
                 torch.cuda.synchronize()
                 if i >= 2:
                     rd.append(RATE_BYTES / (e[0].elapsed_time(e[1]) * 1e-3) / 1e9)
-                    cp.append(2 * COPY_BYTES / (e[1].elapsed_time(e[2]) * 1e-3) / 1e9)
+                    nt.append(RATE_BYTES / (e[1].elapsed_time(e[2]) * 1e-3) / 1e9)
+                    cp.append(2 * COPY_BYTES / (e[2].elapsed_time(e[3]) * 1e-3) / 1e9)
         del buf
         torch.cuda.empty_cache()
-        return float(np.median(rd)), float(np.median(cp))
+        return float(np.median(rd)), float(np.median(nt)), float(np.median(cp))
 
 
 def _stats(x):
@@ -445,13 +453,77 @@ def cpu_baseline(s, budget_s=10.0):
                           seqs, tokens, c.H_kv, elapsed)}
 
 
+def run_workload(name, formats, args, stream, flush):
+    """Time the step of every format of one workload.  Returns (per-format
+    records, the first format's Setup kept resident for the caller)."""
+    wl = WORKLOADS[name]
+    per = {}
+    primary = None
+    for fmt in formats:
+        print("[bench] %s %s: building the cache" % (name, fmt), file=sys.stderr, flush=True)
+        s = Setup(wl["config"], fmt)
+        # the step as append + decode (the headline), then as one fused step,
+        # after a few untimed steps of each (the first steps after the cache
+        # is built run slower)
+        for fused in (False, True):
+            time_steps(s, 3, 1, stream, flush, fused=fused)
+        t = time_steps(s, args.steps, args.warmup, stream, flush, fused=False)
+        tf = time_steps(s, args.steps, args.warmup, stream, flush, fused=True)
+        ms = t["step"]["mean"] if flush is not None else t["wall"]
+        ms_f = tf["step"]["mean"] if flush is not None else tf["wall"]
+        c = s.case
+        split_ms = t["split"]["mean"]
+        achieved = s.kv_bytes / (split_ms * 1e-3) / 1e9
+        fmt_base = parse_label(fmt)[0]
+        res = {
+            "GB_per_s": s.kv_bytes / (ms * 1e-3) / 1e9,
+            "pct_of_hbm_peak": 100.0 * s.kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "ms_per_step": ms,
+            "step_us": 1000.0 * ms,
+            "step_ms": t["step"], "wall_ms_per_step": t["wall"],
+            "kv_bytes": s.kv_bytes,
+            "bytes_per_token": s.bpt,
+            "new_tokens_per_step": c.B * c.n_q,
+            "split_kernel_ms": t["split"], "combine_ms": t["combine"], "step_append_ms": t["append"],
+            "split_workgroups": s.nwg, "partial_slots": s.slots,
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBS,
+                         "kernel": "decode_split_kernel<%d, %d, false> (%s)" % (kvq.FORMATS[fmt_base], c.D, fmt),
+                         "kernel_ms": split_ms, "algorithmic_bytes_per_launch": s.kv_bytes},
+            "fused_step": {
+                "GB_per_s": s.kv_bytes / (ms_f * 1e-3) / 1e9,
+                "pct_of_hbm_peak": 100.0 * s.kv_bytes / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "ms_per_step": ms_f, "step_ms": tf["step"],
+                "split_kernel_ms": tf["split"], "combine_ms": tf["combine"]},
+        }
+        per[fmt] = res
+        print("[bench] %s %s: %.1f GB/s (%.1f%% of peak), step %.3f ms = append %.3f + split %.3f (p10 %.3f p90 "
+              "%.3f, %.1f%% of peak) + combine %.3f | fused step %.1f GB/s: %.3f ms = split storing the new tokens "
+              "%.3f + combine %.3f" % (
+                  name, fmt, res["GB_per_s"], res["pct_of_hbm_peak"], ms, t["append"]["mean"],
+                  split_ms, t["split"]["p10"], t["split"]["p90"], 100 * achieved / HBM_PEAK_GBS,
+                  t["combine"]["mean"], res["fused_step"]["GB_per_s"], ms_f, tf["split"]["mean"],
+                  tf["combine"]["mean"]),
+              file=sys.stderr, flush=True)
+        if primary is None:
+            primary = s
+        else:
+            del s
+            torch.cuda.empty_cache()
+    return per, primary
+
+
+HEADLINE = "batched"  # the batched decode workload is the one the metric is quoted on
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="batched", choices=sorted(WORKLOADS))
-    ap.add_argument("--formats", default=None, help="comma-separated subset of the workload's formats")
+    ap.add_argument("--workload", default="all", choices=["all"] + sorted(WORKLOADS),
+                    help="'all' (the default) times every workload and reports the batched one as the headline")
+    ap.add_argument("--formats", default=None, help="comma-separated subset of a single workload's formats")
     ap.add_argument("--append-formats", default=",".join(APPEND_FORMATS),
                     help="formats of the prefill-chunk append measurement, or 'none'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -471,60 +543,30 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.formats and args.workload == "all":
+        print("--formats needs a single --workload", file=sys.stderr)
+        sys.exit(2)
     kvq.library()
-    wl = WORKLOADS[args.workload]
-    formats = args.formats.split(",") if args.formats else wl["formats"]
+    head = HEADLINE if args.workload == "all" else args.workload
+    names = [head] + [n for n in WORKLOADS if n != head] if args.workload == "all" else [head]
     stream = torch.cuda.Stream()
     probe = Probe()
-    read_gbs, copy_gbs = probe.rates(stream)
-    print("[bench] streaming read %.0f GB/s, copy %.0f GB/s (read + write)" % (read_gbs, copy_gbs),
-          file=sys.stderr, flush=True)
+    plain_gbs, read_gbs, copy_gbs = probe.rates(stream)
+    print("[bench] streaming read %.0f GB/s (non-temporal loads; %.0f plain), copy %.0f GB/s (read + write)" % (
+        read_gbs, plain_gbs, copy_gbs), file=sys.stderr, flush=True)
     flush = None if args.no_flush else probe
-    per = {}
+    per_workload = {}
     primary = None
-    for fmt in formats:
-        print("[bench] %s %s: building the cache" % (args.workload, fmt), file=sys.stderr, flush=True)
-        s = Setup(wl["config"], fmt)
-        # the step as append + decode (the headline), then as one fused step,
-        # after a few untimed steps of each (the first steps after the cache
-        # is built run slower)
-        for fused in (False, True):
-            time_steps(s, 3, 1, stream, flush, fused=fused)
-        t = time_steps(s, args.steps, args.warmup, stream, flush, fused=False)
-        tf = time_steps(s, args.steps, args.warmup, stream, flush, fused=True)
-        ms = t["step"]["mean"] if flush is not None else t["wall"]
-        ms_f = tf["step"]["mean"] if flush is not None else tf["wall"]
-        c = s.case
-        res = {
-            "GB_per_s": s.kv_bytes / (ms * 1e-3) / 1e9,
-            "pct_of_hbm_peak": 100.0 * s.kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "ms_per_step": ms,
-            "step_ms": t["step"], "wall_ms_per_step": t["wall"],
-            "kv_bytes": s.kv_bytes,
-            "bytes_per_token": s.bpt,
-            "new_tokens_per_step": c.B * c.n_q,
-            "split_kernel_ms": t["split"], "combine_ms": t["combine"], "step_append_ms": t["append"],
-            "split_workgroups": s.nwg, "partial_slots": s.slots,
-            "fused_step": {
-                "GB_per_s": s.kv_bytes / (ms_f * 1e-3) / 1e9,
-                "pct_of_hbm_peak": 100.0 * s.kv_bytes / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                "ms_per_step": ms_f, "step_ms": tf["step"],
-                "split_kernel_ms": tf["split"], "combine_ms": tf["combine"]},
-        }
-        per[fmt] = res
-        print("[bench] %s %s: %.1f GB/s (%.1f%% of peak), step %.3f ms = append %.3f + split %.3f (p10 %.3f p90 "
-              "%.3f) + combine %.3f | fused step %.1f GB/s: %.3f ms = split storing the new tokens %.3f + "
-              "combine %.3f" % (
-                  args.workload, fmt, res["GB_per_s"], res["pct_of_hbm_peak"], ms, t["append"]["mean"],
-                  t["split"]["mean"], t["split"]["p10"], t["split"]["p90"], t["combine"]["mean"],
-                  res["fused_step"]["GB_per_s"], ms_f, tf["split"]["mean"], tf["combine"]["mean"]),
-              file=sys.stderr, flush=True)
-        if primary is None:
-            primary = (fmt, s, res)
+    for name in names:
+        formats = args.formats.split(",") if args.formats else WORKLOADS[name]["formats"]
+        per, s = run_workload(name, formats, args, stream, flush)
+        per_workload[name] = {"workload": WORKLOADS[name]["label"], "per_kv_dtype": per}
+        if name == head:
+            primary = (formats[0], s, per[formats[0]], per)
         else:
             del s
             torch.cuda.empty_cache()
-    fmt, s, res = primary
+    fmt, s, res, per = primary
     c = s.case
     split_ms = res["split_kernel_ms"]["mean"]
     achieved = s.kv_bytes / (split_ms * 1e-3) / 1e9
@@ -544,23 +586,24 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": wl["label"], "workload_name": args.workload, "kv_dtype": fmt, "batch": c.B,
+        "config": {"workload": WORKLOADS[head]["label"], "workload_name": head, "kv_dtype": fmt, "batch": c.B,
                    "n_q": c.n_q, "num_q_heads": c.H_q, "num_kv_heads": c.H_kv, "head_dim": c.D,
                    "page_size": c.P, "cached_tokens": int(c.seq_lens.astype(np.int64).sum()),
                    "split_workgroups": s.nwg, "cache_flush_between_steps": flush is not None},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(args.workload, fmt),
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(head, fmt),
                      "kernel": "decode_split_kernel<%d, %d, false> (%s)" % (kvq.FORMATS[fmt], c.D, fmt),
                      "kernel_ms": split_ms,
                      "algorithmic_bytes_per_launch": s.kv_bytes,
                      "measured_streaming_read_GBs": read_gbs, "frac_of_measured_read": achieved / read_gbs,
-                     "measured_copy_GBs": copy_gbs},
+                     "measured_plain_load_read_GBs": plain_gbs, "measured_copy_GBs": copy_gbs},
         "pct_of_hbm_peak": res["pct_of_hbm_peak"],
         "quant_append": ({"workload": "64 sequences x one %d-token prefill chunk (mixed lengths 1K-128K, "
                                       "chunks start mid-page), 4 kv heads, head_dim 256" % APPEND_CHUNK,
                           "kv_dtype": append_formats[0], **appends[append_formats[0]],
                           "per_kv_dtype": appends} if appends else None),
         "per_kv_dtype": per,
+        "per_workload": per_workload,
         "prefill_attention": prefill,
     }
     if not args.no_cpu_baseline:

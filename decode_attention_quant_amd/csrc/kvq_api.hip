@@ -170,8 +170,9 @@ kvq_status kvq_decode_plan(const kvq_cache_desc* desc, int32_t batch, int32_t n_
   return KVQ_OK;
 }
 
-kvq_status kvq_decode_workspace_size(const kvq_cache_desc* desc, int32_t batch, int32_t n_q, int32_t num_q_heads,
-                                     int32_t max_pages_per_seq, int32_t num_workgroups, size_t* bytes) {
+kvq_status kvq_decode_workspace_size_for(const kvq_cache_desc* desc, int32_t batch, int32_t n_q,
+                                         int32_t num_q_heads, int32_t max_pages_per_seq, int32_t num_workgroups,
+                                         size_t* bytes) {
   kvq_status st = check_decode_shape(desc, batch, n_q, num_q_heads, max_pages_per_seq);
   if (st != KVQ_OK) return st;
   if (bytes == nullptr) return KVQ_ERR_INVALID_ARGUMENT;
@@ -180,6 +181,11 @@ kvq_status kvq_decode_workspace_size(const kvq_cache_desc* desc, int32_t batch, 
   if (st != KVQ_OK) return st;
   *bytes = p.total();
   return KVQ_OK;
+}
+
+kvq_status kvq_decode_workspace_size(const kvq_cache_desc* desc, int32_t batch, int32_t n_q, int32_t num_q_heads,
+                                     int32_t max_pages_per_seq, size_t* bytes) {
+  return kvq_decode_workspace_size_for(desc, batch, n_q, num_q_heads, max_pages_per_seq, 0, bytes);
 }
 
 static kvq_status decode_run(const kvq_cache_desc* desc, const void* pool, const void* q_bf16, int32_t batch,

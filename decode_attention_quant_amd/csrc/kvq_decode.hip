@@ -370,7 +370,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           __builtin_amdgcn_global_load_lds((gbl_void_t*)(qrow_ptr(2 * j + (lane >> 5)) + 8 * (lane & 31)),
-                                           (lds_void_t*)(uintptr_t)(qstage + 1024 * j), 16, 0, 0);
+                                           (lds_void_t*)(uintptr_t)(qstage + 1024 * j), 16, 0, CPOL_STREAM);
         wait_vmcnt<0>();
         stage_first(0, 1);
         lds_get_rows4(qstage + 8 * lane, qraw);

@@ -204,7 +204,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(Geometry geo, DecodeArg
     if (wave == 0) {
 #pragma unroll
       for (int k = 0; k < S - 1; ++k)
-        if (k < nk) stage_block<FMT, D>(ring0 + k * T::STAGE, head0, geo, bt_row, k, lane);
+        if (k < nk) stage_block<FMT, D, CPOL_REUSE>(ring0 + k * T::STAGE, head0, geo, bt_row, k, lane);
     }
     if constexpr (PP::VSH) {
       if (nk > 0) {
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(Geometry geo, DecodeArg
       }
       __syncthreads();
       if (wave == 0 && k + S - 1 < nk)
-        stage_block<FMT, D>(ring0 + ((st + S - 1) % S) * T::STAGE, head0, geo, bt_row, k + S - 1, lane);
+        stage_block<FMT, D, CPOL_REUSE>(ring0 + ((st + S - 1) % S) * T::STAGE, head0, geo, bt_row, k + S - 1, lane);
       const uint32_t stg = ring0 + st * T::STAGE;
       st = st + 1 == S ? 0 : st + 1;
       if constexpr (PP::VSH) {

@@ -110,10 +110,20 @@ typedef struct kvq_cache_desc {
 /* Bytes of one page: H_kv head blocks of [K codes | K scales | V codes |
  * V scales], each plane padded to 128 bytes (no padding at the supported
  * shapes, so a page is exactly page_size x H_kv x the per-token bytes).
+ * The per-token bytes are those of the NInfer guide's table of the five
+ * formats at head_dim 256 (section on why the KV cache is quantized: BF16
+ * 1024, INT8-G64 528, FP8 row-256 516, NVFP4-G16 288, K8V4 402 bytes per
+ * token), and for the other formats the same count of codes plus scales:
+ * FP8_TENSOR 512, MXFP8 528 (264 at head_dim 128), MXFP4 272.  The pages
+ * are the guide's 64-token pages (128-token blocks for mxfp8, TokenSpeed
+ * article, --kv-cache-dtype section).
  * The pool is num_pages consecutive pages; it must be 128-byte aligned.
  * Inside each plane, tokens are grouped in blocks of 16 stored in the order
  * the decode kernel's matrix-core lanes consume them; the index formulas are
- * spelled out in decode_attention_quant_amd/csrc/kvq_format.hpp. */
+ * spelled out in decode_attention_quant_amd/csrc/kvq_format.hpp.
+ * Errors: KVQ_ERR_INVALID_ARGUMENT for a null pointer or a malformed
+ * descriptor, KVQ_ERR_UNSUPPORTED for a (format, head_dim, page_size) the
+ * library does not build. */
 kvq_status kvq_page_bytes(const kvq_cache_desc* desc, size_t* bytes_per_page);
 
 /* Quantize and store K/V rows (the write path; NInfer guide: every format
@@ -132,14 +142,28 @@ kvq_status kvq_quantize_append(const kvq_cache_desc* desc, void* pool,
                                int64_t num_tokens, const int32_t* slot_mapping,
                                hipStream_t stream);
 
-/* Workspace bytes kvq_decode_attention / kvq_decode_split need for this
- * problem.  num_workgroups = 0 selects the library's own plan (the one
- * kvq_decode_attention uses: as many split workgroups as fit on the device
- * at once, fewer for small problems); a positive value forces that count.
- * Limits: batch <= 4096; (num_q_heads / num_kv_heads) * n_q <= 1024. */
+/* Workspace bytes kvq_decode_attention and kvq_decode_step need for this
+ * problem.  Decode reads every cached K/V of each sequence at every step
+ * (NInfer guide, section on why the KV cache is quantized), so the read of
+ * one (sequence, kv head) is split across workgroups; the workspace holds
+ * each split's partial softmax state (running maximum, denominator and
+ * unnormalized output per query row) until the cross-split reduce merges
+ * them.  The size follows the library's own plan (kvq_decode_plan): as
+ * many split workgroups as fit on the current device at once, fewer for
+ * small problems.
+ * Limits: batch <= 4096; (num_q_heads / num_kv_heads) * n_q <= 1024.
+ * Errors as in kvq_decode_attention's argument checks; bytes must not be
+ * NULL. */
 kvq_status kvq_decode_workspace_size(const kvq_cache_desc* desc, int32_t batch, int32_t n_q,
-                                     int32_t num_q_heads, int32_t max_pages_per_seq,
-                                     int32_t num_workgroups, size_t* bytes);
+                                     int32_t num_q_heads, int32_t max_pages_per_seq, size_t* bytes);
+
+/* The same for a forced split: num_workgroups = 0 selects the library's
+ * own plan (the size kvq_decode_workspace_size gives), a positive value that
+ * many split workgroups, as passed to kvq_decode_split, kvq_decode_step_split
+ * and kvq_decode_combine. */
+kvq_status kvq_decode_workspace_size_for(const kvq_cache_desc* desc, int32_t batch, int32_t n_q,
+                                         int32_t num_q_heads, int32_t max_pages_per_seq,
+                                         int32_t num_workgroups, size_t* bytes);
 
 /* Decode attention over the compressed cache (NInfer guide: each generated
  * token attends over every cached K/V; Qwen FP8-KV article: several query
@@ -153,8 +177,8 @@ kvq_status kvq_decode_workspace_size(const kvq_cache_desc* desc, int32_t batch, 
  *  out           device fp32 [batch][n_q][num_q_heads][head_dim], written.
  *  lse           device fp32 [batch][n_q][num_q_heads] (natural log of the
  *                softmax denominator plus the max score), or NULL.
- *  workspace     device, 256-byte aligned, >= kvq_decode_workspace_size(..., 0, ...)
- *                bytes; its contents on entry do not matter.
+ *  workspace     device, 256-byte aligned, >= kvq_decode_workspace_size bytes;
+ *                its contents on entry do not matter.
  * Query token i of sequence b sits at position seq_lens[b] - n_q + i and
  * attends to positions 0..that one (causal among the new tokens); query
  * head h reads kv head h / (num_q_heads / num_kv_heads).  A query with no

@@ -31,6 +31,11 @@ extern "C" {
  * one particular 32-bit value, so that the loads cannot be optimized away. */
 int kvq_probe_read(const void* src, size_t bytes, void* sink, hipStream_t stream);
 
+/* The same read with the non-temporal hint on every load: the highest read
+ * rate measured for a kernel that streams its data once (the decode
+ * kernels' copies carry the same hint).  It does not evict the caches. */
+int kvq_probe_read_stream(const void* src, size_t bytes, void* sink, hipStream_t stream);
+
 /* dst[0, bytes) = src[0, bytes) (bytes a multiple of 16, both 16-byte
  * aligned, no overlap). */
 int kvq_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);

@@ -101,7 +101,7 @@ def test_append_validation_enqueues_nothing():
 def test_workspace_size_with_forced_workgroups():
     d = kvq.desc(1, 256, 64, 4, 100)
     sz = ctypes.c_size_t()
-    assert _status("kvq_decode_workspace_size", ctypes.byref(d), 3, 1, 24, 10, 7, ctypes.byref(sz)) == 0
+    assert _status("kvq_decode_workspace_size_for", ctypes.byref(d), 3, 1, 24, 10, 7, ctypes.byref(sz)) == 0
     units, nwg, R = 3 * 4, 7, 6
     slots = units + nwg
     a256 = lambda n: (n + 255) // 256 * 256
@@ -109,10 +109,51 @@ def test_workspace_size_with_forced_workgroups():
     bad = [(3, 0, 24, 10, 4), (3, 1, 0, 10, 4), (3, 1, 25, 10, 4), (-1, 1, 24, 10, 4), (3, 1, 24, 0, 4),
            (3, 1, 24, 10, -2)]
     for args in bad:
-        assert _status("kvq_decode_workspace_size", ctypes.byref(d), *args, ctypes.byref(sz)) == 1, args
+        assert _status("kvq_decode_workspace_size_for", ctypes.byref(d), *args, ctypes.byref(sz)) == 1, args
     # too many rows per kv head, or too large a batch
-    assert _status("kvq_decode_workspace_size", ctypes.byref(d), 1, 64, 4 * 32, 10, 4, ctypes.byref(sz)) == 2
-    assert _status("kvq_decode_workspace_size", ctypes.byref(d), 5000, 1, 24, 10, 4, ctypes.byref(sz)) == 2
+    assert _status("kvq_decode_workspace_size_for", ctypes.byref(d), 1, 64, 4 * 32, 10, 4, ctypes.byref(sz)) == 2
+    assert _status("kvq_decode_workspace_size_for", ctypes.byref(d), 5000, 1, 24, 10, 4, ctypes.byref(sz)) == 2
+    # the planned form validates the same arguments before asking the device
+    for args in [a[:4] for a in bad if a[4] >= 0]:
+        assert _status("kvq_decode_workspace_size", ctypes.byref(d), *args, ctypes.byref(sz)) == 1, args
+    assert _status("kvq_decode_workspace_size", ctypes.byref(d), 3, 1, 24, 10, None) == 1
+
+
+# The calls of the boundary as the survey of the pages lists them: name ->
+# parameter types in order (names of parameters are free).
+SURVEY_SIGNATURES = {
+    "kvq_page_bytes": ["const kvq_cache_desc*", "size_t*"],
+    "kvq_quantize_append": ["const kvq_cache_desc*", "void*", "const void*", "const void*", "int64_t",
+                            "const int32_t*", "hipStream_t"],
+    "kvq_decode_workspace_size": ["const kvq_cache_desc*", "int32_t", "int32_t", "int32_t", "int32_t", "size_t*"],
+    "kvq_decode_attention": ["const kvq_cache_desc*", "const void*", "const void*", "int32_t", "int32_t", "int32_t",
+                             "const int32_t*", "int32_t", "const int32_t*", "float", "float*", "float*", "void*",
+                             "size_t", "hipStream_t"],
+    "kvq_dequant_page": ["const kvq_cache_desc*", "const void*", "int64_t", "int32_t", "float*", "float*",
+                         "hipStream_t"],
+    "kvq_status_string": ["kvq_status"],
+}
+
+
+def _header_signatures():
+    text = re.sub(r"/\*.*?\*/", " ", open(HEADER).read(), flags=re.S)
+    sigs = {}
+    for m in re.finditer(r"(kvq_status|const char\*)\s+(kvq_\w+)\s*\(([^)]*)\)\s*;", text):
+        params = []
+        for p in m.group(3).split(","):
+            p = " ".join(p.split())
+            p = re.sub(r"\s*\*\s*", "* ", p).strip()
+            toks = p.split(" ")
+            params.append(" ".join(toks[:-1]).replace(" *", "*").strip())
+        sigs[m.group(2)] = params
+    return sigs
+
+
+def test_boundary_calls_have_the_survey_signatures():
+    sigs = _header_signatures()
+    for name, params in SURVEY_SIGNATURES.items():
+        assert name in sigs, name
+        assert sigs[name] == params, (name, sigs[name])
 
 
 def test_decode_validation_enqueues_nothing():
@@ -189,6 +230,8 @@ def test_probe_rejects_bad_arguments_on_the_host():
     assert lib.kvq_probe_read(fake, 1000, fake, None) == 1          # not whole 1 KB chunks
     assert lib.kvq_probe_read(ctypes.c_void_p((1 << 20) + 8), 1024, fake, None) == 1  # misaligned
     assert lib.kvq_probe_read(fake, 1024, None, None) == 1
+    assert lib.kvq_probe_read_stream(None, 1024, fake, None) == 1
+    assert lib.kvq_probe_read_stream(fake, 1000, fake, None) == 1
     assert lib.kvq_probe_copy(fake, fake, 24, None) == 1            # not whole 16 B words
     assert lib.kvq_probe_copy(None, fake, 32, None) == 1
     assert lib.kvq_probe_read(fake, 0, fake, None) == 0             # empty: nothing to do

@@ -52,6 +52,47 @@ def test_decode_matches_oracle(cfg, fmt, B, lens):
     assert_lse_close(lse, ref_lse, W_name(c))
 
 
+# Query-row shapes beyond the workloads': R = G * n_q rows share a kv head.
+# R = 1 is MHA with one query token; R = 24 is the 24 / 4 GQA group with 4
+# MTP tokens and R = 40 a 40 / 4 group with 4, which take two and three
+# 16-row tiles (the second and third tiles, blockIdx.y > 0, the last one
+# partly filled).  (config, format, n_q, H_q, H_kv)
+ROW_SHAPES = [
+    (1, "BF16", 1, 2, 2), (2, "INT8_G64", 1, 4, 4), (2, "FP8_ROW", 1, 4, 4), (2, "FP8_TENSOR", 1, 4, 4),
+    (3, "NVFP4_G16", 1, 4, 4), (4, "K8V4", 1, 4, 4), (5, "MXFP8", 1, None, None), (3, "MXFP4", 1, 4, 4),
+    (1, "BF16", 4, 24, 4), (2, "INT8_G64", 4, None, None), (2, "FP8_ROW", 4, None, None),
+    (2, "FP8_TENSOR", 4, None, None), (3, "NVFP4_G16", 4, None, None), (4, "K8V4", 4, None, None),
+    (5, "MXFP8", 4, 192, 32), (3, "MXFP4", 4, None, None), (4, "K8V4", 4, 40, 4), (2, "INT8_G64", 4, 40, 4),
+]
+
+
+@pytest.mark.parametrize("cfg,fmt,n_q,H_q,H_kv", ROW_SHAPES)
+def test_query_row_shapes(cfg, fmt, n_q, H_q, H_kv):
+    lens = [700, 130, 3] if cfg != 5 else [700, 258, 3]
+    c = W.make_case(cfg, fmt, device="cpu", B=3, lengths=lens, n_q=n_q, H_q=H_q, H_kv=H_kv)
+    assert (c.H_q // c.H_kv) * c.n_q in (1, 24, 40)
+    bl = build(c)
+    out, lse = run_decode(bl)
+    ref, ref_lse = oracle_attention(bl)
+    assert_close(out, ref, W_name(c))
+    assert_lse_close(lse, ref_lse, W_name(c))
+    # the split path with forced workgroup counts merges every tile's partials
+    q = c.q.cuda()
+    for nwg in (5, 64):
+        ws = kvq.alloc_workspace(kvq.workspace_size(bl.desc, c.B, c.n_q, c.H_q, c.max_pages, nwg))
+        ws.fill_(0xFF)
+        o2 = torch.full((c.B, c.n_q, c.H_q, c.D), float("nan"), device="cuda")
+        l2 = torch.full((c.B, c.n_q, c.H_q), float("nan"), device="cuda")
+        note("row shapes split", W_name(c), "nwg", nwg)
+        kvq.decode_split(bl.desc, bl.pool_gpu, q, bl.bt, bl.sl, c.softmax_scale, ws, num_workgroups=nwg,
+                         flags=kvq.SPLIT_WRITE_WHOLE_UNITS, out=o2, lse=l2)
+        kvq.decode_combine(bl.desc, c.B, c.n_q, c.H_q, c.max_pages, bl.sl, ws, o2, l2, num_workgroups=nwg,
+                           flags=kvq.SPLIT_WRITE_WHOLE_UNITS)
+        torch.cuda.synchronize()
+        assert_close(o2.cpu().numpy(), ref, "%s nwg=%d" % (W_name(c), nwg))
+        assert_lse_close(l2.cpu().numpy(), ref_lse, "%s nwg=%d" % (W_name(c), nwg))
+
+
 def test_fp8_tensor_unit_scale():
     c = W.make_case(2, "FP8_TENSOR", device="cpu", B=2, lengths=[300, 90], calibrate_tensor_scale=False)
     assert c.k_scale == 1.0 and c.v_scale == 1.0

@@ -24,6 +24,7 @@ pytestmark = pytest.mark.gpu
 # (workload config, format): every decode workload at its full size
 CASES = [
     (2, "INT8_G64"),
+    (2, "FP8_ROW"),
     (2, "FP8_TENSOR"),
     (3, "NVFP4_G16"),
     (3, "MXFP4"),

@@ -23,19 +23,20 @@ def test_copy_is_exact():
         assert torch.equal(dst[:n], src) and int(dst[n:].sum()) == 0
 
 
+@pytest.mark.parametrize("nontemporal", [False, True])
 @pytest.mark.parametrize("chunks,where", [(1, 0), (5, 4), (64, 37), (4096 + 3, 4096 + 2)])
-def test_read_reaches_every_chunk(chunks, where):
+def test_read_reaches_every_chunk(chunks, where, nontemporal):
     """A lane whose 16 bytes fold to the marker writes the sink, so placing
     the marker in one chunk shows that chunk was read (the last chunks of a
     size that is not a multiple of four take the kernel's remainder path)."""
     from decode_attention_quant_amd import probe
-    note("probe read", chunks, where)
+    note("probe read", chunks, where, "nt" if nontemporal else "plain")
     buf = torch.zeros(chunks * 256, dtype=torch.int32, device="cuda")
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
-    probe.read(buf, sink)
+    probe.read(buf, sink, nontemporal=nontemporal)
     torch.cuda.synchronize()
     assert int(sink[0]) == 0
     buf[where * 256 + 4 * 9] = torch.tensor(MAGIC, dtype=torch.int64).to(torch.int32)  # lane 9's first word
-    probe.read(buf, sink)
+    probe.read(buf, sink, nontemporal=nontemporal)
     torch.cuda.synchronize()
     assert int(sink[0]) & 0xFFFFFFFF == MAGIC

@@ -84,6 +84,34 @@ def test_fused_step_equals_append_then_decode(cfg, fmt, lens):
     check_step(c, bl, n_new)
 
 
+@pytest.mark.parametrize("cfg,fmt,H_q,H_kv", [(2, "FP8_ROW", 4, 4), (3, "NVFP4_G16", 4, 4), (4, "K8V4", 4, 4),
+                                           (5, "MXFP8", None, None), (2, "INT8_G64", 4, 4)])
+def test_fused_step_single_query_row(cfg, fmt, H_q, H_kv):
+    """G * n_q = 1 (MHA, one query token per step): one live row in the tile."""
+    c = W.make_case(cfg, fmt, device="cpu", B=3, lengths=[700, 129, 14], n_q=1, H_q=H_q, H_kv=H_kv, reserve=1)
+    assert (c.H_q // c.H_kv) * c.n_q == 1
+    bl = build(c)
+    check_step(c, bl, 1)
+
+
+def test_fused_step_rejects_more_than_one_row_tile():
+    """G * n_q = 24 (24 / 4 GQA with 4 MTP tokens) takes two row tiles, so a
+    block has two reading workgroups and the fused step is refused (the
+    separate append + decode serve it); nothing is stored."""
+    c = W.make_case(2, "FP8_ROW", device="cpu", B=2, lengths=[300, 40], n_q=4, reserve=4)
+    bl = build(c, oracle=False)
+    k, v, _ = W.append_chunk(c, 4)
+    sl = torch.as_tensor(c.seq_lens + 4, dtype=torch.int32, device="cuda")
+    pool = bl.pool_gpu.clone()
+    note("fused step, two row tiles: refused")
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.decode_step(bl.desc, pool, k.view(2, 4, c.H_kv, c.D).cuda(), v.view(2, 4, c.H_kv, c.D).cuda(),
+                        c.q.cuda(), bl.bt, sl, c.softmax_scale)
+    assert e.value.status == 2
+    torch.cuda.synchronize()
+    assert torch.equal(pool, bl.pool_gpu)
+
+
 def test_fused_step_short_and_empty_sequences():
     """MTP with sequences shorter than n_q (new tokens at negative positions are
     not stored and see nothing) and one with no tokens at all."""

@@ -100,7 +100,7 @@ def _bf16_normal(shape, gen, device):
 
 
 def make_case(config, fmt, device="cpu", B=None, lengths=None, n_q=None, extra_pages=0,
-              calibrate_tensor_scale=True, reserve=0, two_level=False):
+              calibrate_tensor_scale=True, reserve=0, two_level=False, H_q=None, H_kv=None):
     """Draw one decode workload.
 
     ``B``/``lengths`` override the config's batch and lengths (lengths may be
@@ -108,13 +108,16 @@ def make_case(config, fmt, device="cpu", B=None, lengths=None, n_q=None, extra_p
     cases the oracle finishes quickly.  ``reserve`` extra token slots per
     sequence are given pages (for later appends) without being drawn.
     ``two_level`` calibrates the per-tensor scales of the NVFP4 planes
-    (NVFP4_G16's K and V, K8V4's V).
+    (NVFP4_G16's K and V, K8V4's V).  ``H_q``/``H_kv`` override the head
+    counts (other query-group shapes on the same recipe).
     """
     cfg = CONFIGS[config]
     fmt_id = FORMAT_IDS[fmt] if isinstance(fmt, str) else int(fmt)
     B = cfg["B"] if B is None else B
     n_q = cfg["n_q"] if n_q is None else n_q
-    D, P, H_q, H_kv = cfg["D"], cfg["P"], cfg["H_q"], cfg["H_kv"]
+    D, P = cfg["D"], cfg["P"]
+    H_q = cfg["H_q"] if H_q is None else H_q
+    H_kv = cfg["H_kv"] if H_kv is None else H_kv
     rng = np.random.default_rng(_seed(config))
     special = rng.choice(D, size=4, replace=False)
     if lengths is None:
