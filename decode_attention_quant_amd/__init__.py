@@ -26,7 +26,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too sm
 
 EXPORTS = [
     "kvq_page_bytes", "kvq_quantize_append", "kvq_decode_workspace_size", "kvq_decode_workspace_size_for",
-    "kvq_decode_attention",
+    "kvq_decode_attention", "kvq_decode_attention_noalloc",
     "kvq_decode_split", "kvq_decode_combine", "kvq_decode_plan", "kvq_dequant_page", "kvq_status_string",
     "kvq_decode_step", "kvq_decode_step_split", "kvq_prefill_attention",
 ]
@@ -62,6 +62,7 @@ def library():
             "kvq_decode_workspace_size": [D, I32, I32, I32, I32, ctypes.POINTER(SZ)],
             "kvq_decode_workspace_size_for": [D, I32, I32, I32, I32, I32, ctypes.POINTER(SZ)],
             "kvq_decode_attention": [D, P, P, I32, I32, I32, P, I32, P, F, P, P, P, SZ, P],
+            "kvq_decode_attention_noalloc": [D, P, P, I32, I32, I32, P, I32, P, F, P, P, P],
             "kvq_decode_split": [D, P, P, I32, I32, I32, P, I32, P, F, I32, I32, P, P, P, SZ, P],
             "kvq_decode_step": [D, P, P, P, P, I32, I32, I32, P, I32, P, F, P, P, P, SZ, P],
             "kvq_decode_step_split": [D, P, P, P, P, I32, I32, I32, P, I32, P, F, I32, I32, P, P, P, SZ, P],
@@ -246,6 +247,21 @@ def decode_attention(d, pool, q, block_table, seq_lens, softmax_scale, out=None,
         float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)),
         "kvq_decode_attention")
     return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # KVQ_NOALLOC_SCRATCH_BYTES
+
+
+def decode_attention_noalloc(d, pool, q, block_table, seq_lens, softmax_scale, out, lse=None, stream=None):
+    """decode_attention with the library's own device scratch as the workspace
+    (the caller allocates nothing but out/lse, which it passes in)."""
+    B, n_q, H_q, max_pages = _need_decode(d, pool, q, block_table, seq_lens, out, lse)
+    if out is None:
+        raise ValueError("out must be given")
+    _placed(pool=pool, q=q, block_table=block_table, seq_lens=seq_lens, out=out, lse=lse)
+    _check(library().kvq_decode_attention_noalloc(
+        ctypes.byref(d), _ptr(pool), _ptr(q), B, n_q, H_q, _ptr(block_table), max_pages, _ptr(seq_lens),
+        float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream)), "kvq_decode_attention_noalloc")
 
 
 def decode_step(d, pool, k_new, v_new, q, block_table, seq_lens, softmax_scale, out=None, lse=None, workspace=None,

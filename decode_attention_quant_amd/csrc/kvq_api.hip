@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/kvq.h"
 #include "kvq_format.hpp"
 #include "kvq_internal.hpp"
@@ -117,6 +119,34 @@ DecodeArgs base_args(const kvq_cache_desc* d, const Plan& p, int32_t batch, int3
 }
 
 kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
+
+}  // namespace
+
+// The workspace of kvq_decode_attention_noalloc: a file-scope device array
+// that every GPU the library runs on holds until the process ends.  In host
+// code its name is a host-side stand-in, not a device address; kernels get
+// the address hipGetSymbolAddress gives for the current device, resolved
+// once per device and kept below.
+static __device__ __align__(256) uint8_t scratch[KVQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[MAX_DEVICES] = {};
+
+// The current device's address of `scratch` (nullptr on a HIP error).
+void* scratch_on_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
 
 }  // namespace
 
@@ -241,6 +271,23 @@ kvq_status kvq_decode_attention(const kvq_cache_desc* desc, const void* pool, co
                                 float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return decode_run(desc, pool, q_bf16, batch, n_q, num_q_heads, block_table, max_pages_per_seq, seq_lens,
                     softmax_scale, 0, true, true, true, out, lse, workspace, workspace_bytes, stream);
+}
+
+kvq_status kvq_decode_attention_noalloc(const kvq_cache_desc* desc, const void* pool, const void* q_bf16,
+                                        int32_t batch, int32_t n_q, int32_t num_q_heads, const int32_t* block_table,
+                                        int32_t max_pages_per_seq, const int32_t* seq_lens, float softmax_scale,
+                                        float* out, float* lse, hipStream_t stream) {
+  kvq_status st = check_decode_shape(desc, batch, n_q, num_q_heads, max_pages_per_seq);
+  if (st != KVQ_OK) return st;
+  if (batch == 0) return KVQ_OK;
+  Plan p;
+  st = make_plan(desc, batch, n_q, num_q_heads, max_pages_per_seq, 0, &p);
+  if (st != KVQ_OK) return st;
+  if (p.total() > (size_t)KVQ_NOALLOC_SCRATCH_BYTES) return KVQ_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = scratch_on_current_device();
+  if (ws == nullptr) return KVQ_ERR_HIP;
+  return decode_run(desc, pool, q_bf16, batch, n_q, num_q_heads, block_table, max_pages_per_seq, seq_lens,
+                    softmax_scale, 0, true, true, true, out, lse, ws, (size_t)KVQ_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 kvq_status kvq_decode_step(const kvq_cache_desc* desc, void* pool, const void* k_new_bf16, const void* v_new_bf16,

@@ -191,6 +191,29 @@ kvq_status kvq_decode_attention(const kvq_cache_desc* desc, const void* pool,
                                 float softmax_scale, float* out, float* lse,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* kvq_decode_attention for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, and harnesses that
+ * forbid allocation.  The workspace is a device array of
+ * KVQ_NOALLOC_SCRATCH_BYTES inside the library (each GPU the library runs
+ * on holds its own copy until the process ends); the caller still passes
+ * the inputs and outputs.  The call allocates and frees nothing.  Its
+ * first call on a device, with that device current, looks the array's
+ * address up on that device (hipGetSymbolAddress) and keeps it.
+ * Arguments, results and errors are those of kvq_decode_attention; a
+ * problem whose planned workspace (kvq_decode_workspace_size) exceeds
+ * KVQ_NOALLOC_SCRATCH_BYTES returns KVQ_ERR_WORKSPACE_TOO_SMALL and
+ * enqueues nothing.  Every call on one GPU shares that GPU's array, so calls
+ * that overlap on one GPU (on different streams, or from several threads
+ * without ordering) race and must not be made; calls ordered on one stream
+ * are fine (nothing in the array needs clearing between them). */
+#define KVQ_NOALLOC_SCRATCH_BYTES (64 << 20)
+kvq_status kvq_decode_attention_noalloc(const kvq_cache_desc* desc, const void* pool,
+                                        const void* q_bf16, int32_t batch, int32_t n_q,
+                                        int32_t num_q_heads, const int32_t* block_table,
+                                        int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                        float softmax_scale, float* out, float* lse,
+                                        hipStream_t stream);
+
 /* One decode step with the append fused in (the decode-step variant of the
  * write path followed by attention; NInfer guide: every generated token
  * enters the cache through its codec and then attends over the whole

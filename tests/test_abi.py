@@ -149,6 +149,11 @@ def _header_signatures():
     return sigs
 
 
+def test_noalloc_scratch_size_matches_the_header():
+    m = re.search(r"#define KVQ_NOALLOC_SCRATCH_BYTES \((\d+) << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == kvq.NOALLOC_SCRATCH_BYTES
+
+
 def test_boundary_calls_have_the_survey_signatures():
     sigs = _header_signatures()
     for name, params in SURVEY_SIGNATURES.items():
