@@ -418,21 +418,26 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
       if constexpr (T::RING) __builtin_amdgcn_s_barrier();
       else __syncthreads();
       // 8 consecutive elements d0 .. d0 + 7 of this lane's row r
-      // xr[k][e] = element 32 k + 8 g + e of this lane's row r (all at once)
+      // xr[k][e] = element 32 k + 8 g + e of this lane's row r (all at once).
+      // Packed (at most 8 rows): lanes c16 and c16 + 8 both take row c16 % 8;
+      // the first gives the query's first piece, the second its second.
+      const int qr = T::PACK ? (c16 & 7) : r;
+      const bool qrow_ok = qr < Rt;
       float xr[8][8];
       if constexpr (T::RING) {
-        lds_get_8x8(qrow_a(r) + 32 * g, xr);
+        lds_get_8x8(qrow_a(qr) + 32 * g, xr);
       } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) xr[k][e] = sm_o[r * D + 32 * k + 8 * g + e];
+          for (int e = 0; e < 8; ++e) xr[k][e] = sm_o[qr * D + 32 * k + 8 * g + e];
       }
       float am = 0.f;
-      if (row_ok) {
-        if constexpr (T::RING) am = lds_get1(qexp_a + 4 * r);
-        else am = qexp[r];
+      if (qrow_ok) {
+        if constexpr (T::RING) am = lds_get1(qexp_a + 4 * qr);
+        else am = qexp[qr];
       }
+      const bool second_piece = T::PACK && (c16 & 8) != 0;
       if constexpr (T::QI8) {
         // q' ~ (c1 + c2 / 254) / inv, int8 c1 = RN(q' inv), c2 = RN(254 (q' inv - c1)),
         // inv = 127 / max|q'|: error below max|q'| / 64516 per element
@@ -445,14 +450,22 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
           // j < 8 at 64 kk + 8 g + j, else at 64 kk + 32 + 8 g + (j - 8)
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
-            const float v = row_ok ? (j < 8 ? xr[2 * kk][j] : xr[2 * kk + 1][j - 8]) * inv : 0.f;
+            const float v = qrow_ok ? (j < 8 ? xr[2 * kk][j] : xr[2 * kk + 1][j - 8]) * inv : 0.f;
             const float c1 = fmaxf(fminf(rintf(v), 127.f), -127.f);
             const float c2 = fmaxf(fminf(rintf((v - c1) * 254.0f), 127.f), -127.f);
-            w1[j >> 2] |= ((uint32_t)(int)c1 & 0xFFu) << (8 * (j & 3));
-            w2[j >> 2] |= ((uint32_t)(int)c2 & 0xFFu) << (8 * (j & 3));
+            if constexpr (T::PACK) {  // this lane's piece only (a per-element select)
+              w1[j >> 2] |= ((uint32_t)(int)(second_piece ? c2 : c1) & 0xFFu) << (8 * (j & 3));
+            } else {
+              w1[j >> 2] |= ((uint32_t)(int)c1 & 0xFFu) << (8 * (j & 3));
+              w2[j >> 2] |= ((uint32_t)(int)c2 & 0xFFu) << (8 * (j & 3));
+            }
           }
-          qv[2 * kk] = make_uint4(w1[0], w1[1], w1[2], w1[3]);
-          qv[2 * kk + 1] = make_uint4(w2[0], w2[1], w2[2], w2[3]);
+          if constexpr (T::PACK) {
+            qv[kk] = make_uint4(w1[0], w1[1], w1[2], w1[3]);
+          } else {
+            qv[2 * kk] = make_uint4(w1[0], w1[1], w1[2], w1[3]);
+            qv[2 * kk + 1] = make_uint4(w2[0], w2[1], w2[2], w2[3]);
+          }
         }
       } else {
         // f16 hi + lo of q' * 2^(8 - e), e = exponent of max|q'|: max in
@@ -464,12 +477,19 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
           f16x8 qh16, ql16;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float v = row_ok ? ldexpf(xr[kk][e], 8 - ex) : 0.f;
+            const float v = qrow_ok ? ldexpf(xr[kk][e], 8 - ex) : 0.f;
             qh16[e] = (_Float16)v;
             ql16[e] = (_Float16)(v - (float)qh16[e]);
           }
-          qv[2 * kk] = bitcast<uint4>(qh16);
-          qv[2 * kk + 1] = bitcast<uint4>(ql16);
+          if constexpr (T::PACK) {  // this lane's piece only (a per-element select)
+            f16x8 mine;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) mine[e] = second_piece ? ql16[e] : qh16[e];
+            qv[kk] = bitcast<uint4>(mine);
+          } else {
+            qv[2 * kk] = bitcast<uint4>(qh16);
+            qv[2 * kk + 1] = bitcast<uint4>(ql16);
+          }
         }
       }
       // the other first blocks, once the query no longer needs the wave
@@ -513,8 +533,9 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
 #pragma unroll
       for (int e = 0; e < 4; ++e) sc[e] = (t0 + 4 * g + e <= limit) ? S[e] * crow : NEG_INF;
     };
-    auto pv_phase = [&](Buf<FMT, D>& buf, int jb, const float (&sc)[4]) {
-      const int t0 = 16 * jb;
+    // Online softmax of one block's scores: rescale l and O (and the p of a
+    // block held for a paired product) past the slack, then p = 2^(s - m).
+    auto softmax_phase = [&](const float (&sc)[4], float (&p)[4], float (&p_held)[4]) {
       const float bm = max_over_g(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
       // The running maximum only has to bound the scores loosely: with it up
       // to RESCALE_SLACK below the true one, p <= 2^RESCALE_SLACK, which f16 P
@@ -532,17 +553,22 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
         for (int nt = 0; nt < T::NT; ++nt)
 #pragma unroll
           for (int e = 0; e < 4; ++e) O[nt][e] *= ce[e];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p_held[e] *= corr;  // this lane's row, like l
         m_run = m_new;
       }
       // a row that has seen no visible key yet has m_run = -inf and only
       // -inf scores: subtract 0 instead so that exp2 gives 0, not NaN
       const float m_use = (m_run == NEG_INF) ? 0.f : m_run;
-      float p[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         p[e] = fast_exp2(sc[e] - m_use);
         l_run += p[e];
       }
+    };
+    // O += P . V of one block (16 tokens: 16x16x16 products)
+    auto pv_single = [&](Buf<FMT, D>& buf, int jb, const float (&p)[4]) {
+      const int t0 = 16 * jb;
       const f16x4 P = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
       if (__builtin_expect(t0 + 16 > L, 0)) clear_tail<FMT, D>(buf, L - t0, g);  // only the last block
       // keep the compiler from hoisting every V conversion ahead of the
@@ -551,6 +577,27 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
       for (int nt = 0; nt < T::NT; ++nt) {
         if ((nt & 3) == 0) __builtin_amdgcn_sched_barrier(0);
         O[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(P, v_operand<FMT, D>(buf, nt, lane), O[nt], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto pv_phase = [&](Buf<FMT, D>& buf, int jb, const float (&sc)[4]) {
+      float p[4], none[4] = {0.f, 0.f, 0.f, 0.f};
+      softmax_phase(sc, p, none);
+      pv_single(buf, jb, p);
+    };
+    // O += P . V of two blocks at once with 16x16x32 products: k-slots
+    // 8 g .. 8 g + 3 are tokens 4 g .. 4 g + 3 of the first block and
+    // 8 g + 4 .. 8 g + 7 the same tokens of the second, in P (A operand) as
+    // in V (B operand).  One product costs what a 16x16x16 one does.
+    auto pv_pair = [&](const float (&p0)[4], Buf<FMT, D>& b0, const float (&p1)[4], Buf<FMT, D>& b1) {
+      const f16x8 P = {(_Float16)p0[0], (_Float16)p0[1], (_Float16)p0[2], (_Float16)p0[3],
+                       (_Float16)p1[0], (_Float16)p1[1], (_Float16)p1[2], (_Float16)p1[3]};
+#pragma unroll
+      for (int nt = 0; nt < T::NT; ++nt) {
+        if ((nt & 3) == 0) __builtin_amdgcn_sched_barrier(0);
+        const f16x4 v0 = v_operand<FMT, D>(b0, nt, lane), v1 = v_operand<FMT, D>(b1, nt, lane);
+        const f16x8 V = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(P, V, O[nt], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -572,23 +619,69 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
         // hide its stalls.  Stepping the priority down as a wave progresses
         // lets the one behind catch up, so the two finish close together.
         const int q1 = nk >> 2, q2 = nk >> 1, q3 = nk - (nk >> 2);
-        for (int k = 0; k < nk; ++k) {
-          // stage st - 1 (block k - 1) has been read: refill it with block k + S - 1
+        auto pace = [&](int k) {
+          if (k == q1) __builtin_amdgcn_s_setprio(2);
+          if (k == q2) __builtin_amdgcn_s_setprio(1);
+          if (k == q3) __builtin_amdgcn_s_setprio(0);
+        };
+        // refill the stage block k - 1 left with block k + S - 1, wait for
+        // block k; returns its stage
+        auto arrive = [&](int k) -> uint32_t {
           if (k + S - 1 < nk) {
             const int sn = st == 0 ? S - 1 : st - 1;
             stage_block<FMT, D>(ring0 + sn * T::STAGE, head0, geo, bt_row, j + 4 * (S - 1), lane);
           }
           wait_staged<T::NDMA, S>(min(S - 1, nk - 1 - k));
-          const uint32_t stg = ring0 + st * T::STAGE;
-          read_stage_k<FMT, D>(A, stg, lane);
-          qk_phase(A, j, sc);
-          read_stage_v<FMT, D>(A, stg, lane);
-          pv_phase(A, j, sc);
+          return ring0 + st * T::STAGE;
+        };
+        auto advance = [&]() {
           j += 4;
           st = st + 1 == S ? 0 : st + 1;
-          if (k == q1) __builtin_amdgcn_s_setprio(2);
-          if (k == q2) __builtin_amdgcn_s_setprio(1);
-          if (k == q3) __builtin_amdgcn_s_setprio(0);
+        };
+        if constexpr (T::PV_PAIR) {
+          // blocks in pairs: the first one's p and V operands wait in
+          // registers (its stage is refilled meanwhile) for the second
+          Buf<FMT, D> H;
+          float ph[4], p[4];
+          int k = 0;
+          for (; k + 1 < nk; k += 2) {
+            uint32_t stg = arrive(k);
+            read_stage_k<FMT, D>(A, stg, lane);
+            qk_phase(A, j, sc);
+            read_stage_v<FMT, D>(H, stg, lane);
+            float none[4] = {0.f, 0.f, 0.f, 0.f};
+            softmax_phase(sc, ph, none);
+            if (__builtin_expect(16 * j + 16 > L, 0)) clear_tail<FMT, D>(H, L - 16 * j, g);
+            advance();
+            pace(k);
+            stg = arrive(k + 1);
+            read_stage_k<FMT, D>(A, stg, lane);
+            qk_phase(A, j, sc);
+            read_stage_v<FMT, D>(A, stg, lane);
+            softmax_phase(sc, p, ph);
+            if (__builtin_expect(16 * j + 16 > L, 0)) clear_tail<FMT, D>(A, L - 16 * j, g);
+            pv_pair(ph, H, p, A);
+            advance();
+            pace(k + 1);
+          }
+          if (k < nk) {  // an odd last block
+            const uint32_t stg = arrive(k);
+            read_stage_k<FMT, D>(A, stg, lane);
+            qk_phase(A, j, sc);
+            read_stage_v<FMT, D>(A, stg, lane);
+            pv_phase(A, j, sc);
+            advance();
+          }
+        } else {
+          for (int k = 0; k < nk; ++k) {
+            const uint32_t stg = arrive(k);
+            read_stage_k<FMT, D>(A, stg, lane);
+            qk_phase(A, j, sc);
+            read_stage_v<FMT, D>(A, stg, lane);
+            pv_phase(A, j, sc);
+            advance();
+            pace(k);
+          }
         }
         // a wave with no blocks here still has its first copies in flight
         // (clamped to a valid block); they must land before the merge
@@ -824,6 +917,14 @@ size_t decode_split_lds_bytes(const Geometry& geo, int B, int R) {
 
 hipError_t decode_split_occupancy(const Geometry& geo, int B, int R, int* blocks_per_cu) {
   const size_t lds = decode_split_lds_bytes(geo, B, R);
+  if (R <= PACK_MAX_ROWS) {
+#define KVQ_OCC_PACKED(F, DD)                                                                                      \
+  if (geo.fmt == F && geo.D == DD)                                                                                 \
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, decode_split_kernel<F | VARIANT_PACK, DD, false>, \
+                                                        256, lds);
+    KVQ_FOR_EACH_PACKED(KVQ_OCC_PACKED)
+#undef KVQ_OCC_PACKED
+  }
 #define KVQ_OCC_CASE(F, DD)                                                                        \
   if (geo.fmt == F && geo.D == DD)                                                                 \
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, decode_split_kernel<F, DD, false>, \
@@ -851,6 +952,21 @@ hipError_t launch_decode_split(const Geometry& geo, const DecodeArgs& a, hipStre
     KVQ_QMX_CASE(128) KVQ_QMX_CASE(256)
 #undef KVQ_QMX_CASE
     return hipErrorInvalidValue;
+  }
+  // at most 8 rows: the packed kernel (same LDS layout, one tile)
+  if (a.R <= PACK_MAX_ROWS) {
+#define KVQ_PACKED_CASE(F, DD)                                                                                \
+  if (geo.fmt == F && geo.D == DD) {                                                                          \
+    if (a.pool_w != nullptr)                                                                                  \
+      hipLaunchKernelGGL((decode_split_kernel<F | VARIANT_PACK, DD, true>), dim3(a.nwg, 1), dim3(256), lds, stream, \
+                         geo, a);                                                                             \
+    else                                                                                                      \
+      hipLaunchKernelGGL((decode_split_kernel<F | VARIANT_PACK, DD, false>), dim3(a.nwg, 1), dim3(256), lds, stream, \
+                         geo, a);                                                                             \
+    return hipGetLastError();                                                                                 \
+  }
+    KVQ_FOR_EACH_PACKED(KVQ_PACKED_CASE)
+#undef KVQ_PACKED_CASE
   }
 #define KVQ_SPLIT_CASE(F, DD)                                                                                 \
   if (geo.fmt == F && geo.D == DD) {                                                                          \

@@ -18,6 +18,11 @@ namespace kvq {
   X(F_FP8_TENSOR, 256) X(F_MXFP8, 128) X(F_MXFP8, 256) X(F_INT8_G64, 256) X(F_NVFP4_G16, 256)   \
   X(F_K8V4, 256) X(F_MXFP4, 256)
 
+// The (format, head_dim) pairs whose query goes to the matrix cores in two
+// pieces, which have a packed kernel for at most 8 rows (VARIANT_PACK).
+#define KVQ_FOR_EACH_PACKED(X) X(F_INT8_G64, 256) X(F_NVFP4_G16, 256) X(F_MXFP4, 256)
+constexpr int PACK_MAX_ROWS = 8;
+
 template <int FMT, int D>
 struct DT {
   static constexpr int KC = k_codec(FMT), VC = v_codec(FMT);
@@ -29,9 +34,14 @@ struct DT {
   // Q.K on the block-scaled fp8 MFMA, q rounded to MXFP8 (MXFP8 cache only)
   static constexpr bool QMX = (FMT & VARIANT_QMX) != 0;
   static_assert(!QMX || KC == C_E4MX, "the query-MXFP8 variant reads an MXFP8 cache");
+  // At most 8 query rows: the query's two pieces share one operand, piece 1
+  // in columns 0-7 and piece 2 in columns 8-15 (one lane holds one of them)
+  static constexpr bool PACK = (FMT & VARIANT_PACK) != 0;
+  static_assert(!PACK || QI8 || QF16, "only a query in two pieces is packed");
   static constexpr int KSTEPS = D / 32;
   static constexpr int QSTEPS = QMX ? D / 128 : QI8 ? D / 64 : D / 32;  // MFMA k-steps of Q.K
-  static constexpr int QPIECES = (QI8 || QF16 || QMX) ? 2 : 1;  // QMX: 32 fp8 codes = two 16-byte pieces
+  // 16-byte query pieces per k-step and lane (QMX: 32 fp8 codes = two pieces)
+  static constexpr int QPIECES = PACK ? 1 : (QI8 || QF16 || QMX) ? 2 : 1;
   // Bytes of one 16-token block in each plane, and their place in an LDS
   // stage (the four plane regions back to back).
   static constexpr int KB = code_block_bytes(KC, D), KSB = scale_block_bytes(KC, D);
@@ -59,6 +69,12 @@ struct DT {
   // P.V is done.
   static constexpr bool DOUBLE_BUF = D == 128 || FMT == F_FP8_ROW || FMT == F_FP8_TENSOR;
   static constexpr int NT = D / 16;
+  // P.V over pairs of ring blocks with 16x16x32 products (half the products
+  // of one block at a time); the first block's V operands wait in registers.
+  // For 4-bit V, whose loops are bound by instruction issue (measured: 0-3%
+  // faster there, no change for the 8-bit formats); not where the query takes
+  // two operand pieces of its own (unpacked), which would spill.
+  static constexpr bool PV_PAIR = RING && VBITS == 4 && (QPIECES == 1 || QMX);
   static constexpr int KCH = D * KBITS / 512;                       // 16-B K chunks per lane per block
   static constexpr int VCH = VBITS * NT / 32;                       // 16-B V chunks per lane per block
   // (QMX: one scale byte per 128-value MFMA, one word each)
@@ -587,23 +603,45 @@ __device__ __forceinline__ f32x4 qk_block(const Buf<FMT, D>& buf, const Q& qo, i
     // one fp16 scale per 64 values = one 16-byte chunk = one int8 k-step:
     // the raw codes are the A operand; q = coarse + fine / 254 (int8 each)
     const i32x4 izero = {0, 0, 0, 0};
+    if constexpr (T::PACK) {
+      // columns 0-7 hold the coarse digits, 8-15 the fine ones: weigh this
+      // lane's sums by 254 or 1, then add the other half's (lane c ^ 8)
+      const float w = (lane & 8) ? 1.0f : 254.0f;
 #pragma unroll
-    for (int grp = 0; grp < T::KCH; ++grp) {
-      const i32x4 kc = bitcast<i32x4>(buf.k[grp]);
-      const i32x4 a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(kc, bitcast<i32x4>(qo.get(grp, 0)), izero, 0, 0, 0);
-      const i32x4 a2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(kc, bitcast<i32x4>(qo.get(grp, 1)), izero, 0, 0, 0);
+      for (int grp = 0; grp < T::KCH; ++grp) {
+        const i32x4 a = __builtin_amdgcn_mfma_i32_16x16x64_i8(bitcast<i32x4>(buf.k[grp]),
+                                                             bitcast<i32x4>(qo.get(grp, 0)), izero, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int hw = e * 4 + grp;  // halfword of token 4g+e, group grp
+          const float sc = f16_bits_to_f32((buf.ks[hw >> 1] >> (16 * (hw & 1))) & 0xFFFFu);
+          S[e] += (float)a[e] * sc;  // |a| <= 64*127*127: exact in fp32
+        }
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int hw = e * 4 + grp;  // halfword of token 4g+e, group grp
-        const float sc = f16_bits_to_f32((buf.ks[hw >> 1] >> (16 * (hw & 1))) & 0xFFFFu);
-        S[e] += (float)(a1[e] * 254 + a2[e]) * sc;  // |a1| <= 64*127*127: no int32 overflow
+        S[e] *= w;
+        S[e] += quad_swap<ROW_ROR8>(S[e]);
+      }
+    } else {
+#pragma unroll
+      for (int grp = 0; grp < T::KCH; ++grp) {
+        const i32x4 kc = bitcast<i32x4>(buf.k[grp]);
+        const i32x4 a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(kc, bitcast<i32x4>(qo.get(grp, 0)), izero, 0, 0, 0);
+        const i32x4 a2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(kc, bitcast<i32x4>(qo.get(grp, 1)), izero, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int hw = e * 4 + grp;  // halfword of token 4g+e, group grp
+          const float sc = f16_bits_to_f32((buf.ks[hw >> 1] >> (16 * (hw & 1))) & 0xFFFFu);
+          S[e] += (float)(a1[e] * 254 + a2[e]) * sc;  // |a1| <= 64*127*127: no int32 overflow
+        }
       }
     }
   } else if constexpr (T::KC == C_E2G16) {
     // E2M1 x UE4M3 is exact in f16: fold the group scale into the operand.
     // lane (g, t): k-step kk covers d in [32kk + 8g, +8) -> group 2kk + g/2
     const int gb = (lane >> 5) & 1;
-    f32x4 Slo = zero;
+    f32x4 S1 = zero;
 #pragma unroll
     for (int i = 0; i < T::KCH; ++i) {
 #pragma unroll
@@ -614,27 +652,46 @@ __device__ __forceinline__ f32x4 qk_block(const Buf<FMT, D>& buf, const Q& qo, i
         const _Float16 s = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)sb, 1.0f, false)[0];
         f16x8 a = e2m1x8_f16(word(buf.k[i], hh));
         a *= s;
-        // hi and lo parts of q in separate chains
-        S = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bitcast<f16x8>(qo.get(kk, 0)), S, 0, 0, 0);
-        Slo = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bitcast<f16x8>(qo.get(kk, 1)), Slo, 0, 0, 0);
+        if constexpr (T::PACK) {
+          // hi (columns 0-7) and lo (8-15) in one product; two chains by k-step
+          if (hh & 1) S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bitcast<f16x8>(qo.get(kk, 0)), S1, 0, 0, 0);
+          else S = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bitcast<f16x8>(qo.get(kk, 0)), S, 0, 0, 0);
+        } else {
+          // hi and lo parts of q in separate chains
+          S = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bitcast<f16x8>(qo.get(kk, 0)), S, 0, 0, 0);
+          S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bitcast<f16x8>(qo.get(kk, 1)), S1, 0, 0, 0);
+        }
       }
     }
-    S += Slo;
+    S += S1;
+    if constexpr (T::PACK) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[e] += quad_swap<ROW_ROR8>(S[e]);  // hi + lo of row c16 % 8
+    }
   } else if constexpr (T::KC == C_E2MX) {
     // one UE8M0 per 32 values = per k-step, of the lane's token (lane % 16),
     // applied by the conversion itself; q' as f16 hi + lo as for NVFP4
-    f32x4 Slo = zero;
+    f32x4 S1 = zero;
 #pragma unroll
     for (int i = 0; i < T::KCH; ++i) {
 #pragma unroll
       for (int hh = 0; hh < 4; ++hh) {
         const int kk = 4 * i + hh;
         const f16x8 a = e2m1x8_f16_mx(word(buf.k[i], hh), (buf.ks[kk >> 2] >> (8 * (kk & 3))) & 0xFFu);
-        S = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bitcast<f16x8>(qo.get(kk, 0)), S, 0, 0, 0);
-        Slo = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bitcast<f16x8>(qo.get(kk, 1)), Slo, 0, 0, 0);
+        if constexpr (T::PACK) {
+          if (hh & 1) S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bitcast<f16x8>(qo.get(kk, 0)), S1, 0, 0, 0);
+          else S = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bitcast<f16x8>(qo.get(kk, 0)), S, 0, 0, 0);
+        } else {
+          S = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bitcast<f16x8>(qo.get(kk, 0)), S, 0, 0, 0);
+          S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bitcast<f16x8>(qo.get(kk, 1)), S1, 0, 0, 0);
+        }
       }
     }
-    S += Slo;
+    S += S1;
+    if constexpr (T::PACK) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[e] += quad_swap<ROW_ROR8>(S[e]);
+    }
   }
   return S;
 }

@@ -66,11 +66,17 @@ enum Format : int {
   F_MXFP4 = 7, F_COUNT = 8
 };
 
-// Kernel variant tag (a template argument, never a descriptor's format):
+// Kernel variant tags (template arguments, never a descriptor's format):
 // F_MXFP8 | VARIANT_QMX is the MXFP8 cache read with the query rounded to
-// MXFP8 too and Q.K on the block-scaled fp8 matrix cores.  The format
-// predicates below look at the format bits only.
+// MXFP8 too and Q.K on the block-scaled fp8 matrix cores.  VARIANT_PACK
+// (formats whose query goes to the matrix cores in two pieces: INT8-G64's
+// two int8 digits, the f16 hi + lo of NVFP4 and MXFP4) is the kernel for at
+// most 8 query rows per kv head, which puts both pieces into one 16-column
+// operand (piece 1 in columns 0-7, piece 2 in columns 8-15) and so needs one
+// Q.K product per k-step instead of two.  The format predicates below look
+// at the format bits only.
 constexpr int VARIANT_QMX = 0x100;
+constexpr int VARIANT_PACK = 0x200;
 KVQ_HD constexpr int base_format(int f) { return f & 0xFF; }
 
 KVQ_HD constexpr int k_codec(int f) {
