@@ -127,13 +127,17 @@ class Setup:
         self.kv_bytes = int(c.seq_lens.astype(np.int64).sum()) * c.H_kv * self.bpt
         torch.cuda.synchronize()
 
-    def step(self, stream, ev=None, fused=True):
+    def step(self, stream, ev=None, fused=True, phases=False):
         """One decode step: append the new tokens, attend, reduce.  Fused: the
         two launches kvq_decode_step makes (the split kernel stores the new
-        tokens), timed apart; else quantize-append and the two launches of
-        kvq_decode_attention."""
+        tokens); else quantize-append and the two launches of
+        kvq_decode_attention.  Events: ev[0] before and ev[3] after the step,
+        and with phases=True also ev[1], ev[2] between its launches (each
+        recorded event costs the stream a few microseconds, so a step is
+        timed without them and its phases in a series of their own)."""
         c = self.case
         rec = (lambda i: ev[i].record(stream)) if ev is not None else (lambda i: None)
+        inner = rec if phases else (lambda i: None)
         rec(0)
         if fused:
             kvq.decode_step_split(self.desc, self.pool, self.k_new, self.v_new, self.q, self.bt, self.sl,
@@ -142,10 +146,10 @@ class Setup:
         else:
             kvq.quantize_append(self.desc, self.pool, self.k_new.view(-1, c.H_kv, c.D),
                                 self.v_new.view(-1, c.H_kv, c.D), self.slot_new, stream=stream)
-            rec(1)
+            inner(1)
             kvq.decode_split(self.desc, self.pool, self.q, self.bt, self.sl, c.softmax_scale, self.ws,
                              flags=self.flags, out=self.out, lse=self.lse, stream=stream)
-        rec(2)
+        inner(2)
         kvq.decode_combine(self.desc, c.B, c.n_q, c.H_q, c.max_pages, self.sl, self.ws, self.out, self.lse,
                            flags=self.flags, stream=stream)
         rec(3)
@@ -195,8 +199,9 @@ def _stats(x):
             "p90": float(np.percentile(x, 90))}
 
 
-def time_steps(s, steps, warmup, stream, probe=None, fused=True):
-    """Per-step HIP-event times (ms) of the step and of its launches.
+def time_steps(s, steps, warmup, stream, probe=None, fused=True, phases=False):
+    """Per-step HIP-event times (ms) of the step (events at its ends only),
+    or with phases=True of its launches (events between them too).
 
     With a probe, its cache-evicting read runs before each step, outside
     the step's events; the wall time between the first and last step then
@@ -207,12 +212,12 @@ def time_steps(s, steps, warmup, stream, probe=None, fused=True):
     gc.collect()
     gc.disable()
     try:
-        return _time_steps(s, steps, warmup, stream, probe, fused)
+        return _time_steps(s, steps, warmup, stream, probe, fused, phases)
     finally:
         gc.enable()
 
 
-def _time_steps(s, steps, warmup, stream, probe, fused):
+def _time_steps(s, steps, warmup, stream, probe, fused, phases):
     with torch.cuda.stream(stream):
         for _ in range(warmup):
             if probe is not None:
@@ -226,19 +231,17 @@ def _time_steps(s, steps, warmup, stream, probe, fused):
         for i in range(steps):
             if probe is not None:
                 probe.flush(stream)
-            s.step(stream, evs[i], fused=fused)
+            s.step(stream, evs[i], fused=fused, phases=phases)
         t1.record(stream)
         torch.cuda.synchronize()
-    t = {
-        "wall": t0.elapsed_time(t1) / steps,
-        "step": _stats([e[0].elapsed_time(e[3]) for e in evs]),
-        "combine": _stats([e[2].elapsed_time(e[3]) for e in evs]),
-    }
-    if fused:
-        t["split"] = _stats([e[0].elapsed_time(e[2]) for e in evs])
-    else:
-        t["append"] = _stats([e[0].elapsed_time(e[1]) for e in evs])
-        t["split"] = _stats([e[1].elapsed_time(e[2]) for e in evs])
+    t = {"wall": t0.elapsed_time(t1) / steps, "step": _stats([e[0].elapsed_time(e[3]) for e in evs])}
+    if phases:
+        t["combine"] = _stats([e[2].elapsed_time(e[3]) for e in evs])
+        if fused:
+            t["split"] = _stats([e[0].elapsed_time(e[2]) for e in evs])
+        else:
+            t["append"] = _stats([e[0].elapsed_time(e[1]) for e in evs])
+            t["split"] = _stats([e[1].elapsed_time(e[2]) for e in evs])
     return t
 
 
@@ -469,10 +472,14 @@ def run_workload(name, formats, args, stream, flush):
             time_steps(s, 3, 1, stream, flush, fused=fused)
         t = time_steps(s, args.steps, args.warmup, stream, flush, fused=False)
         tf = time_steps(s, args.steps, args.warmup, stream, flush, fused=True)
+        # the launches of each step apart (events between them), for the
+        # split kernel's own time and the breakdown
+        tp = time_steps(s, args.steps, args.warmup, stream, flush, fused=False, phases=True)
+        tpf = time_steps(s, args.steps, args.warmup, stream, flush, fused=True, phases=True)
         ms = t["step"]["mean"] if flush is not None else t["wall"]
         ms_f = tf["step"]["mean"] if flush is not None else tf["wall"]
         c = s.case
-        split_ms = t["split"]["mean"]
+        split_ms = tp["split"]["mean"]
         achieved = s.kv_bytes / (split_ms * 1e-3) / 1e9
         fmt_base = parse_label(fmt)[0]
         res = {
@@ -484,7 +491,9 @@ def run_workload(name, formats, args, stream, flush):
             "kv_bytes": s.kv_bytes,
             "bytes_per_token": s.bpt,
             "new_tokens_per_step": c.B * c.n_q,
-            "split_kernel_ms": t["split"], "combine_ms": t["combine"], "step_append_ms": t["append"],
+            "split_kernel_ms": tp["split"], "combine_ms": tp["combine"], "step_append_ms": tp["append"],
+            "phase_times_note": "split_kernel_ms, combine_ms and step_append_ms come from a series with events "
+                                "between the launches; the step times have events at their ends only",
             "split_workgroups": s.nwg, "partial_slots": s.slots,
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": achieved / HBM_PEAK_GBS,
@@ -494,16 +503,16 @@ def run_workload(name, formats, args, stream, flush):
                 "GB_per_s": s.kv_bytes / (ms_f * 1e-3) / 1e9,
                 "pct_of_hbm_peak": 100.0 * s.kv_bytes / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS,
                 "ms_per_step": ms_f, "step_ms": tf["step"],
-                "split_kernel_ms": tf["split"], "combine_ms": tf["combine"]},
+                "split_kernel_ms": tpf["split"], "combine_ms": tpf["combine"]},
         }
         per[fmt] = res
-        print("[bench] %s %s: %.1f GB/s (%.1f%% of peak), step %.3f ms = append %.3f + split %.3f (p10 %.3f p90 "
-              "%.3f, %.1f%% of peak) + combine %.3f | fused step %.1f GB/s: %.3f ms = split storing the new tokens "
-              "%.3f + combine %.3f" % (
-                  name, fmt, res["GB_per_s"], res["pct_of_hbm_peak"], ms, t["append"]["mean"],
-                  split_ms, t["split"]["p10"], t["split"]["p90"], 100 * achieved / HBM_PEAK_GBS,
-                  t["combine"]["mean"], res["fused_step"]["GB_per_s"], ms_f, tf["split"]["mean"],
-                  tf["combine"]["mean"]),
+        print("[bench] %s %s: %.1f GB/s (%.1f%% of peak), step %.3f ms (launches apart: append %.3f, split %.3f "
+              "(p10 %.3f p90 %.3f, %.1f%% of peak), combine %.3f) | fused step %.1f GB/s: %.3f ms (apart: split "
+              "storing the new tokens %.3f, combine %.3f)" % (
+                  name, fmt, res["GB_per_s"], res["pct_of_hbm_peak"], ms, tp["append"]["mean"],
+                  split_ms, tp["split"]["p10"], tp["split"]["p90"], 100 * achieved / HBM_PEAK_GBS,
+                  tp["combine"]["mean"], res["fused_step"]["GB_per_s"], ms_f, tpf["split"]["mean"],
+                  tpf["combine"]["mean"]),
               file=sys.stderr, flush=True)
         if primary is None:
             primary = s
