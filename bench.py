@@ -31,10 +31,11 @@ comes from committed HBM byte counters, only while the kernel sources still
 hash to what was profiled.  ``cpu_baseline`` times the CPU oracle on a
 bounded sample of the same workload.
 
-    python bench.py --summarize-counters FETCH_DIR WRITE_DIR --bench-json FILE
+    python bench.py --summarize-counters FETCH_DIR WRITE_DIR BENCH_JSON [FETCH_DIR WRITE_DIR BENCH_JSON ...]
 
-turns two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE)
-into that traffic record: per-dispatch KiB of the split kernel, scaled by
+turns pairs of rocprofv3 --pmc runs of this script (FETCH_SIZE, then
+WRITE_SIZE, each on one workload and format, with that run's JSON line) into
+a list of traffic records: per-dispatch KiB of the split kernel, scaled by
 what the same counters read for the probe's copy kernel of known size.
 """
 
@@ -92,6 +93,26 @@ def parse_label(label):
     ('MXFP8/QMX') whether decode runs in the query-MXFP8 mode."""
     fmt, _, mod = label.partition("/")
     return fmt, mod == "2L", mod == "QMX"
+
+
+# formats whose split kernel has a packed variant for at most 8 query rows
+# per kv head (G * n_q), by head_dim; the library picks it by itself
+PACKED_SPLIT = {"INT8_G64": 256, "NVFP4_G16": 256, "MXFP4": 256}
+PACK_MAX_ROWS = 8
+VARIANT_QMX, VARIANT_PACK = 0x100, 0x200
+
+
+def split_kernel_name(label, D, rows, fused=False):
+    """The decode_split_kernel instantiation the library launches for one
+    workload: the format id with its variant bits, the head dim, and
+    whether the step's append is fused in."""
+    fmt, _, qmx = parse_label(label)
+    v = kvq.FORMATS[fmt]
+    if qmx:
+        v |= VARIANT_QMX
+    elif PACKED_SPLIT.get(fmt) == D and rows <= PACK_MAX_ROWS:
+        v |= VARIANT_PACK
+    return "decode_split_kernel<%d, %d, %s>" % (v, D, "true" if fused else "false")
 
 
 def kv_bytes_per_token(d):
@@ -353,16 +374,18 @@ def kernel_sources_sha():
 
 
 def recorded_traffic(workload, fmt):
-    """HBM bytes per split-kernel launch from the committed counter summary,
-    or None when it is for another workload or the split kernel's sources
-    changed since."""
+    """HBM bytes per split-kernel launch from the committed counter
+    summaries, or None when none covers this workload and format or the
+    split kernel's sources changed since they were taken."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as fh:
-        t = json.load(fh)
-    if t.get("sources_sha256") != kernel_sources_sha() or t.get("workload") != workload or t.get("kv_dtype") != fmt:
-        return None
-    return t["traffic_bytes_per_launch"]
+        records = json.load(fh)
+    sha = kernel_sources_sha()
+    for t in records if isinstance(records, list) else [records]:
+        if t.get("sources_sha256") == sha and t.get("workload") == workload and t.get("kv_dtype") == fmt:
+            return t["traffic_bytes_per_launch"]
+    return None
 
 
 def _counter_means(folder, counter):
@@ -397,7 +420,8 @@ def summarize_counters(fetch_dir, write_dir, bench_json):
             raise SystemExit("expected one kernel matching %r, found %s" % (needle, [k for k, _ in hits]))
         return hits[0]
 
-    split_name = "decode_split_kernel<%d, %d, false>" % (kvq.FORMATS[fmt], line["config"]["head_dim"])
+    cfg = line["config"]
+    split_name = split_kernel_name(fmt, cfg["head_dim"], cfg["num_q_heads"] // cfg["num_kv_heads"] * cfg["n_q"])
     kname, (f_kib, n_f) = pick(fetch, split_name)
     _, (w_kib, n_w) = pick(write, split_name)
     _, (cf_kib, _) = pick(fetch, "kvq_probe::copy_kernel")
@@ -497,8 +521,9 @@ def run_workload(name, formats, args, stream, flush):
             "split_workgroups": s.nwg, "partial_slots": s.slots,
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": achieved / HBM_PEAK_GBS,
-                         "kernel": "decode_split_kernel<%d, %d, false> (%s)" % (kvq.FORMATS[fmt_base], c.D, fmt),
-                         "kernel_ms": split_ms, "algorithmic_bytes_per_launch": s.kv_bytes},
+                         "kernel": "%s (%s)" % (split_kernel_name(fmt, c.D, c.H_q // c.H_kv * c.n_q), fmt),
+                         "kernel_ms": split_ms, "algorithmic_bytes_per_launch": s.kv_bytes,
+                         "traffic": recorded_traffic(name, fmt)},
             "fused_step": {
                 "GB_per_s": s.kv_bytes / (ms_f * 1e-3) / 1e9,
                 "pct_of_hbm_peak": 100.0 * s.kv_bytes / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -539,11 +564,14 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill attention measurement")
     ap.add_argument("--no-flush", action="store_true", help="time steps back to back, caches warm")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
-    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
-    ap.add_argument("--bench-json")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR_OR_JSON",
+                    help="FETCH_DIR WRITE_DIR BENCH_JSON triples")
     args = ap.parse_args()
     if args.summarize_counters:
-        print(json.dumps(summarize_counters(*args.summarize_counters, args.bench_json), indent=1))
+        a = args.summarize_counters
+        if len(a) % 3:
+            ap.error("--summarize-counters takes FETCH_DIR WRITE_DIR BENCH_JSON triples")
+        print(json.dumps([summarize_counters(*a[i:i + 3]) for i in range(0, len(a), 3)], indent=1))
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build runs the hot path on a single device and has no "
@@ -601,7 +629,7 @@ def main():
                    "split_workgroups": s.nwg, "cache_flush_between_steps": flush is not None},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(head, fmt),
-                     "kernel": "decode_split_kernel<%d, %d, false> (%s)" % (kvq.FORMATS[fmt], c.D, fmt),
+                     "kernel": "%s (%s)" % (split_kernel_name(fmt, c.D, c.H_q // c.H_kv * c.n_q), fmt),
                      "kernel_ms": split_ms,
                      "algorithmic_bytes_per_launch": s.kv_bytes,
                      "measured_streaming_read_GBs": read_gbs, "frac_of_measured_read": achieved / read_gbs,
