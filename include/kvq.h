@@ -183,7 +183,14 @@ kvq_status kvq_decode_workspace_size_for(const kvq_cache_desc* desc, int32_t bat
  * attends to positions 0..that one (causal among the new tokens); query
  * head h reads kv head h / (num_q_heads / num_kv_heads).  A query with no
  * visible key gets out = 0 and lse = -inf.  Results are deterministic for a
- * given device. */
+ * given device.
+ * Value range: V is expanded to fp16 with its scale applied before the
+ * P.V products, so the values written must satisfy |V| < 32768 for
+ * INT8_G64, FP8_ROW, MXFP8 and MXFP4 (every decoded value then stays below
+ * 33,000, inside fp16's range); BF16 stores V as fp16 (the format itself
+ * overflows past 65504), and NVFP4_G16, K8V4 and FP8_TENSOR apply their
+ * tensor scale to the output, so any finite V is fine there.  Past that
+ * range results may be infinite or NaN. */
 kvq_status kvq_decode_attention(const kvq_cache_desc* desc, const void* pool,
                                 const void* q_bf16, int32_t batch, int32_t n_q,
                                 int32_t num_q_heads, const int32_t* block_table,

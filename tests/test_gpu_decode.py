@@ -93,6 +93,29 @@ def test_query_row_shapes(cfg, fmt, n_q, H_q, H_kv):
         assert_lse_close(l2.cpu().numpy(), ref_lse, "%s nwg=%d" % (W_name(c), nwg))
 
 
+@pytest.mark.parametrize("fmt,cfg", [("INT8_G64", 2), ("FP8_ROW", 2), ("MXFP8", 5), ("MXFP4", 3), ("BF16", 1),
+                                     ("NVFP4_G16", 3), ("K8V4", 4)])
+def test_values_at_the_edge_of_the_supported_range(fmt, cfg):
+    """V up to just below 2^15 in magnitude (the supported range of the
+    formats whose V is expanded to fp16 with its scale, include/kvq.h):
+    every decoded value stays inside fp16 and the outputs match the oracle.
+    V is the recipe's N(0, 1) draw times S = 12000, so outputs are compared
+    after dividing by S: the tolerance's absolute term is set for unit-scale
+    values, and the relative errors of the path do not depend on the scale."""
+    c = W.make_case(cfg, fmt, device="cpu", B=2, lengths=[700, 130])
+    v = (c.v.float() * 12000.0).clamp(-32512.0, 32512.0)
+    v[::97, :, ::17] = 32512.0   # the largest bf16 below 2^15, spread over tokens and dims
+    v[5::97, :, 3::19] = -32512.0
+    c.v = v.to(torch.bfloat16)
+    assert float(c.v.float().abs().max()) < 32768.0
+    bl = build(c)
+    out, lse = run_decode(bl)
+    ref, ref_lse = oracle_attention(bl)
+    assert np.all(np.isfinite(out))
+    assert_close(out / 12000.0, ref / 12000.0, "large V " + W_name(c))
+    assert_lse_close(lse, ref_lse, "large V " + W_name(c))
+
+
 def test_fp8_tensor_unit_scale():
     c = W.make_case(2, "FP8_TENSOR", device="cpu", B=2, lengths=[300, 90], calibrate_tensor_scale=False)
     assert c.k_scale == 1.0 and c.v_scale == 1.0
