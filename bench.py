@@ -100,6 +100,9 @@ def parse_label(label):
 PACKED_SPLIT = {"INT8_G64": 256, "NVFP4_G16": 256, "MXFP4": 256}
 PACK_MAX_ROWS = 8
 VARIANT_QMX, VARIANT_PACK = 0x100, 0x200
+# formats whose chunked prefill runs on the 32-row kernel (K exact in bf16,
+# one query piece); the others keep the 16-row kernel
+WIDE_PREFILL = ("BF16", "FP8_ROW", "FP8_TENSOR", "MXFP8", "K8V4")
 
 
 def split_kernel_name(label, D, rows, fused=False):
@@ -348,8 +351,9 @@ def prefill_bench(stream, probe, chunk=APPEND_CHUNK, fmt="K8V4", reps=3):
            "kv_dtype": fmt, "query_tokens": int(c.B * chunk), "attention_flops": flops,
            "ms": mean, "ms_runs": ms, "TFLOP_per_s": tflops,
            "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                        "frac": tflops / MFMA_PEAK_TFLOPS, "kernel": "prefill_kernel<%d, %d> (%s)" % (
-                            kvq.FORMATS[fmt], c.D, fmt)},
+                        "frac": tflops / MFMA_PEAK_TFLOPS, "kernel": "%s<%d, %d> (%s)" % (
+                            "prefill_wide_kernel" if fmt in WIDE_PREFILL else "prefill_kernel", kvq.FORMATS[fmt],
+                            c.D, fmt)},
            "kv_bytes_per_call": kv_bytes, "row_tiles": int(c.B * c.H_kv * ((6 * chunk + 63) // 64))}
     print("[bench] prefill %s: %d query tokens over %.2f GB of cache in %.2f ms, %.0f TFLOP/s (%.1f%% of %.0f)" % (
         fmt, c.B * chunk, kv_bytes / 1e9, mean, tflops, 100 * tflops / MFMA_PEAK_TFLOPS, MFMA_PEAK_TFLOPS),
