@@ -367,8 +367,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(Geometry geo, DecodeArg
 // register 8 m + i of S^T holds token 16 m + 8 (l / 32) + i, which is then
 // already the P^T operand of the P.V product over tokens 16 m .. 16 m + 15.
 // The V^T operand (dims x tokens) comes from a buffer the workgroup fills
-// once per 32-token step: [block m][dim d][16 tokens] f16, the two 16-byte
-// halves of a row swapped when bit 2 of d is set (no bank conflicts).
+// once per 32-token step: [block m][half h][dim d][tokens 8 h .. 8 h + 7]
+// f16, so that the 32 lanes of a half read 512 consecutive bytes.
 //
 // Pipeline: a ring of S stages of two 16-token blocks; wave 0 copies, one
 // barrier per step publishes a stage, after which all 256 threads expand
@@ -386,13 +386,21 @@ template <int FMT, int D>
 struct WT {
   using T = DT<FMT, D>;
   static constexpr int STAGE = 2 * T::STAGE;           // one 32-token step
-  static constexpr int NDMA = 2 * T::NDMA;
+  // copies per step of the waves that copy K codes, and of the others
+  static constexpr int NK_DMA = (T::KB + 1023) / 1024;
+  static constexpr int NR_DMA = (T::KSB + 1023) / 1024 + (T::VB + 1023) / 1024 + (T::VSB + 1023) / 1024;
   static constexpr bool VSH = T::VC != C_F16;          // V codes expanded into the shared buffer
-  static constexpr int VBUF = VSH ? 2 * D * 32 : 0;    // [2 blocks][D][16 tokens] f16
+  static constexpr int VSTEP = VSH ? 2 * D * 32 : 0;   // one step: [2 blocks][2 halves][D][8 tokens] f16
   static constexpr int BUDGET = 78 * 1024;             // two workgroups per CU
+  // Where a ring of 3 stages fits beside two V buffers, step k + 1's V is
+  // expanded during step k (one barrier per step); otherwise one buffer,
+  // filled at the top of the step and published by a second barrier.
+  static constexpr bool VDB = VSH && (BUDGET - 2 * VSTEP) / STAGE >= 3;
+  static constexpr int VBUF = VDB ? 2 * VSTEP : VSTEP;
   static constexpr int FIT = (BUDGET - VBUF) / STAGE;
   static constexpr int S = FIT > 4 ? 4 : FIT;
   static_assert(S >= 2, "a step is read while the next one is in flight");
+  static_assert(!VDB || S >= 3, "step k + 1 is expanded while step k + 2 is in flight");
   static constexpr int LDS = S * STAGE + VBUF;
   static constexpr int NT = D / 32;                    // 32-dim n-tiles of O^T
   static constexpr int KS = D / 16;                    // k-steps of Q.K
@@ -436,19 +444,19 @@ __device__ __forceinline__ uint32_t lds_read4b(uint32_t addr) {
   asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(r) : "v"(addr) : "memory");
   return r;
 }
-// Eight 8-byte writes at addr + 512 i, waiting for them.
+// Eight 8-byte writes at addr + 256 i, waiting for them.
 __device__ __forceinline__ void lds_write8x8(uint32_t addr, const uint2 (&v)[8]) {
-  asm volatile("ds_write_b64 %0, %1\n\tds_write_b64 %0, %2 offset:512\n\tds_write_b64 %0, %3 offset:1024\n\t"
-               "ds_write_b64 %0, %4 offset:1536\n\tds_write_b64 %0, %5 offset:2048\n\t"
-               "ds_write_b64 %0, %6 offset:2560\n\tds_write_b64 %0, %7 offset:3072\n\t"
-               "ds_write_b64 %0, %8 offset:3584\n\ts_waitcnt lgkmcnt(0)"
+  asm volatile("ds_write_b64 %0, %1\n\tds_write_b64 %0, %2 offset:256\n\tds_write_b64 %0, %3 offset:512\n\t"
+               "ds_write_b64 %0, %4 offset:768\n\tds_write_b64 %0, %5 offset:1024\n\t"
+               "ds_write_b64 %0, %6 offset:1280\n\tds_write_b64 %0, %7 offset:1536\n\t"
+               "ds_write_b64 %0, %8 offset:1792\n\ts_waitcnt lgkmcnt(0)"
                : : "v"(addr), "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7])
                : "memory");
 }
-// Four 8-byte writes at addr + 512 i.
+// Four 8-byte writes at addr + 256 i.
 __device__ __forceinline__ void lds_write4x8(uint32_t addr, const uint2 (&v)[4]) {
-  asm volatile("ds_write_b64 %0, %1\n\tds_write_b64 %0, %2 offset:512\n\tds_write_b64 %0, %3 offset:1024\n\t"
-               "ds_write_b64 %0, %4 offset:1536\n\ts_waitcnt lgkmcnt(0)"
+  asm volatile("ds_write_b64 %0, %1\n\tds_write_b64 %0, %2 offset:256\n\tds_write_b64 %0, %3 offset:512\n\t"
+               "ds_write_b64 %0, %4 offset:768\n\ts_waitcnt lgkmcnt(0)"
                : : "v"(addr), "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]) : "memory");
 }
 
@@ -496,7 +504,8 @@ __device__ __forceinline__ void expand_v_step(uint32_t stg, uint32_t vbuf, int t
         out[jj].y = p0 + 2 >= L ? 0u : (p0 + 3 >= L ? (out[jj].y & 0xFFFFu) : out[jj].y);
       }
     }
-    const uint32_t dst = vbuf + m * D * 32 + c * 4096 + n * 32 + (((g >> 1) ^ ((n >> 2) & 1)) * 16) + (g & 1) * 8;
+    // dims 16 (8c + jj) + n, tokens 4g .. 4g + 3 = half g / 2, bytes 8 (g % 2) ..
+    const uint32_t dst = vbuf + m * D * 32 + (g >> 1) * D * 16 + (128 * c + n) * 16 + (g & 1) * 8;
     lds_write8x8(dst, out);
   } else {
     // 8-bit codes: thread (m, c, g, n) per 16-byte chunk c of column n, tokens
@@ -548,7 +557,7 @@ __device__ __forceinline__ void expand_v_step(uint32_t stg, uint32_t vbuf, int t
           out[jj].y = p0 + 2 >= L ? 0u : (p0 + 3 >= L ? (out[jj].y & 0xFFFFu) : out[jj].y);
         }
       }
-      const uint32_t dst = vbuf + m * D * 32 + c * 2048 + n * 32 + (((g >> 1) ^ ((n >> 2) & 1)) * 16) + (g & 1) * 8;
+      const uint32_t dst = vbuf + m * D * 32 + (g >> 1) * D * 16 + (64 * c + n) * 16 + (g & 1) * 8;
       lds_write4x8(dst, out);
     }
   }
@@ -612,9 +621,26 @@ __global__ __launch_bounds__(256, 2) void prefill_wide_kernel(Geometry geo, Deco
 
   const uint8_t* head0 = a.pool + (int64_t)h * geo.head_bytes;
   const cint32* bt_row = as_const(a.block_table) + (int64_t)b * a.max_pages;
-  auto stage_step = [&](int k, uint32_t dst) {
-    stage_block<FMT, D, CPOL_REUSE>(dst, head0, geo, bt_row, 2 * k, lane);
-    stage_block<FMT, D, CPOL_REUSE>(dst + T::STAGE, head0, geo, bt_row, min(2 * k + 1, last_blk), lane);
+  // A step's copies are spread over the four waves: wave w takes token block
+  // w % 2 of the step, its K codes (w < 2) or its K scales, V codes and V
+  // scales (w >= 2); each wave waits for its own copies before the barrier
+  // that publishes the step.
+  auto stage_part = [&](int k, uint32_t dst) {
+    const BlockAddr ba = block_addr(head0, geo, bt_row, (wave & 1) ? min(2 * k + 1, last_blk) : 2 * k);
+    const uint32_t d = dst + (wave & 1) * T::STAGE;
+    if (wave < 2) {
+      copy_plane<T::KB, CPOL_REUSE>(d + T::SK, ba.hb + geo.off_kc + (int64_t)ba.bip * T::KB, lane);
+    } else {
+      if constexpr (T::KSB > 0)
+        copy_plane<T::KSB, CPOL_REUSE>(d + T::SKS, ba.hb + geo.off_ks + (int64_t)ba.bip * T::KSB, lane);
+      copy_plane<T::VB, CPOL_REUSE>(d + T::SV, ba.hb + geo.off_vc + (int64_t)ba.bip * T::VB, lane);
+      if constexpr (T::VSB > 0)
+        copy_plane<T::VSB, CPOL_REUSE>(d + T::SVS, ba.hb + geo.off_vs + (int64_t)ba.bip * T::VSB, lane);
+    }
+  };
+  auto wait_part = [&](int after) {
+    if (wave < 2) wait_staged<W::NK_DMA, W::S>(after);
+    else wait_staged<W::NR_DMA, W::S>(after);
   };
 
   f32x16 O[W::NT];
@@ -625,24 +651,45 @@ __global__ __launch_bounds__(256, 2) void prefill_wide_kernel(Geometry geo, Deco
   float m_run = NEG_INF, l_run = 0.f;
 
   constexpr int S = W::S;
-  if (wave == 0) {
 #pragma unroll
-    for (int k = 0; k < S - 1; ++k)
-      if (k < nk) stage_step(k, ring0 + k * W::STAGE);
+  for (int k = 0; k < S - 1; ++k)
+    if (k < nk) stage_part(k, ring0 + k * W::STAGE);
+  if constexpr (W::VDB) {
+    if (nk > 0) {
+      wait_part(min(S - 2, nk - 1));
+      __syncthreads();
+      expand_v_step<FMT, D>(ring0, vbuf, 0, L, tid);
+    }
   }
   int st = 0;
   for (int k = 0; k < nk; ++k) {
-    if (wave == 0) wait_staged<W::NDMA, S>(min(S - 2, nk - 1 - k));
-    __syncthreads();  // step k landed; every wave is done with step k - 1 (its stage and the V buffer)
-    if (wave == 0 && k + S - 1 < nk) stage_step(k + S - 1, ring0 + ((st + S - 1) % S) * W::STAGE);
+    // With two V buffers the waves wait for step k + 1 (k landed before), else for step k.
+    if constexpr (W::VDB) {
+      if (k + 1 < nk) wait_part(min(S - 3, nk - 2 - k));
+    } else {
+      wait_part(min(S - 2, nk - 1 - k));
+    }
+    __builtin_amdgcn_s_setprio(0);
+    __syncthreads();  // the step(s) landed; every wave is done with step k - 1 (its stage and V buffer)
+    if (k + S - 1 < nk) stage_part(k + S - 1, ring0 + ((st + S - 1) % S) * W::STAGE);
     const uint32_t stg = ring0 + st * W::STAGE;
-    st = st + 1 == S ? 0 : st + 1;
+    const int st1 = st + 1 == S ? 0 : st + 1;
     const int t0 = 32 * k;
-    if constexpr (W::VSH) expand_v_step<FMT, D>(stg, vbuf, t0, L, tid);
+    uint32_t vcur = vbuf;  // the V buffer of step k
+    if constexpr (W::VDB) {
+      vcur = vbuf + (k & 1) * W::VSTEP;
+      if (k + 1 < nk) expand_v_step<FMT, D>(ring0 + st1 * W::STAGE, vbuf + ((k + 1) & 1) * W::VSTEP, t0 + 32, L, tid);
+    } else if constexpr (W::VSH) {
+      expand_v_step<FMT, D>(stg, vbuf, t0, L, tid);
+    }
+    st = st1;
 
     const bool active = has_rows && t0 <= wlim_hi;  // wave-uniform: some row sees a token of this step
     f16x8 P0, P1;
     if (active) {
+      // the products run at raised priority, the softmax and the expansion
+      // at the base one, so a SIMD's matrix core is fed first
+      __builtin_amdgcn_s_setprio(1);
       // ---- S^T = K Q^T (rows: tokens tau, columns: the wave's rows)
       f32x16 Sacc;
 #pragma unroll
@@ -681,6 +728,7 @@ __global__ __launch_bounds__(256, 2) void prefill_wide_kernel(Geometry geo, Deco
           }
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       // ---- scores in log2 units, causal limit (positions past L included)
       float sc[16];
       if constexpr (T::KC == C_E4ROW) {
@@ -734,15 +782,16 @@ __global__ __launch_bounds__(256, 2) void prefill_wide_kernel(Geometry geo, Deco
         P1[i] = (_Float16)p[8 + i];
       }
     }
-    if constexpr (W::VSH) __syncthreads();  // the V buffer is complete
+    if constexpr (W::VSH && !W::VDB) __syncthreads();  // the V buffer is complete
     if (active) {
+      __builtin_amdgcn_s_setprio(1);
       // ---- O^T += V^T P^T, two 16-token products per 32-dim n-tile
       if constexpr (W::VSH) {
-        const uint32_t vb = vbuf + c32 * 32 + ((hl ^ ((c32 >> 2) & 1)) * 16);
+        const uint32_t vb = vcur + hl * D * 16 + c32 * 16;
 #pragma unroll
         for (int nt = 0; nt < W::NT; nt += 2) {
           uint4 v4[4];
-          lds_read4<0, D * 32, 1024, 1024 + D * 32>(v4, vb + nt * 1024);
+          lds_read4<0, D * 32, 512, 512 + D * 32>(v4, vb + nt * 512);
           O[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bitcast<f16x8>(v4[0]), P0, O[nt], 0, 0, 0);
           O[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bitcast<f16x8>(v4[1]), P1, O[nt], 0, 0, 0);
           O[nt + 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bitcast<f16x8>(v4[2]), P0, O[nt + 1], 0, 0, 0);
