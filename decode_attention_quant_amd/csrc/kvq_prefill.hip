@@ -13,9 +13,13 @@
 // ring; one barrier per block publishes it and frees the stage read last;
 // every wave then runs the decode kernel's per-block code on it for its own
 // rows (K expanded exactly into matrix-core operands, Q.K, online softmax
-// with the lazy running maximum, P.V).  The work items are laid out so that
-// one unit's row tiles run on one XCD, whose L2 then serves the repeats, so
-// HBM sees a unit's cache about once per XCD.  Each wave finishes its own
+// with the lazy running maximum, P.V).  Work items (row tiles) go out in
+// unit-major order, one workgroup each; the hardware hands workgroups to the
+// 8 XCDs round robin, so every XCD gets every eighth tile of every unit and
+// the XCDs' shares stay even whatever the length mix, while the tiles of a
+// unit that one XCD runs side by side still share its L2.  (Keeping a unit's
+// tiles on one XCD left one XCD with 1.66 times the mean work on 64 mixed
+// lengths.)  Each wave finishes its own
 // rows: normalization, the inverse rotation of V for the rotated formats
 // (through LDS, 8 rows at a time), output and lse.
 #include <hip/hip_runtime.h>
@@ -50,11 +54,9 @@ __host__ __device__ constexpr size_t prefill_lds_bytes() {
   return PT<FMT, D>::HDR_FLOATS * sizeof(float) + (size_t)PT<FMT, D>::AREA;
 }
 
-// One work item = 64 rows (a row tile) of one unit; item wi runs on workgroup
-// n with wi = (n % 8) * chunk + n / 8, so the items of one unit, which are
-// consecutive, share an XCD (workgroups go to the 8 XCDs round robin).
+// One work item = 64 rows (a row tile) of one unit, item n on workgroup n.
 template <int FMT, int D>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(Geometry geo, DecodeArgs a, int tiles, int chunk) {
+__global__ __launch_bounds__(256, 2) void prefill_kernel(Geometry geo, DecodeArgs a, int tiles) {
   using T = DT<FMT, D>;
   using PP = PT<FMT, D>;
   constexpr float NEG_INF = -__builtin_inff();
@@ -63,9 +65,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(Geometry geo, DecodeArg
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, c16 = lane & 15;
-  const int n = blockIdx.x;
-  const int wi = (n & 7) * chunk + (n >> 3);
-  if (wi >= a.B * geo.H_kv * tiles) return;
+  const int wi = blockIdx.x;
   const int u = wi / tiles, tile = wi - u * tiles;
   const int b = u / geo.H_kv, h = u - b * geo.H_kv;
   const int L = as_const(a.seq_lens)[b];
@@ -576,7 +576,7 @@ __device__ __forceinline__ bf16x8 e4m3x8_bf16_mx(uint32_t w0, uint32_t w1, uint3
 }
 
 template <int FMT, int D>
-__global__ __launch_bounds__(256, 2) void prefill_wide_kernel(Geometry geo, DecodeArgs a, int tiles, int chunk) {
+__global__ __launch_bounds__(256, 2) void prefill_wide_kernel(Geometry geo, DecodeArgs a, int tiles) {
   using T = DT<FMT, D>;
   using W = WT<FMT, D>;
   constexpr float NEG_INF = -__builtin_inff();
@@ -585,9 +585,7 @@ __global__ __launch_bounds__(256, 2) void prefill_wide_kernel(Geometry geo, Deco
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, c32 = lane & 31;
-  const int wg = blockIdx.x;
-  const int wi = (wg & 7) * chunk + (wg >> 3);
-  if (wi >= a.B * geo.H_kv * tiles) return;
+  const int wi = blockIdx.x;  // item: 128 rows (a row tile) of one unit
   const int u = wi / tiles, tile = wi - u * tiles;
   const int b = u / geo.H_kv, h = u - b * geo.H_kv;
   const int L = as_const(a.seq_lens)[b];
@@ -872,18 +870,15 @@ hipError_t launch_prefill_t(const Geometry& geo, const DecodeArgs& a, hipStream_
     const int64_t tiles = (a.R + 127) / 128;
     const int64_t total = (int64_t)a.B * geo.H_kv * tiles;
     if (total == 0) return hipSuccess;
-    const int64_t chunk = (total + 7) / 8;
     constexpr size_t lds = WT<FMT, D>::LDS;
-    hipLaunchKernelGGL((prefill_wide_kernel<FMT, D>), dim3((unsigned)(8 * chunk)), dim3(256), lds, stream, geo, a,
-                       (int)tiles, (int)chunk);
+    hipLaunchKernelGGL((prefill_wide_kernel<FMT, D>), dim3((unsigned)total), dim3(256), lds, stream, geo, a,
+                       (int)tiles);
   } else {
     const int64_t tiles = (a.R + 63) / 64;
     const int64_t total = (int64_t)a.B * geo.H_kv * tiles;
     if (total == 0) return hipSuccess;
-    const int64_t chunk = (total + 7) / 8;
     constexpr size_t lds = prefill_lds_bytes<FMT, D>();
-    hipLaunchKernelGGL((prefill_kernel<FMT, D>), dim3((unsigned)(8 * chunk)), dim3(256), lds, stream, geo, a,
-                       (int)tiles, (int)chunk);
+    hipLaunchKernelGGL((prefill_kernel<FMT, D>), dim3((unsigned)total), dim3(256), lds, stream, geo, a, (int)tiles);
   }
   return hipGetLastError();
 }
