@@ -370,10 +370,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(Geometry geo, DecodeArg
 // once per 32-token step: [block m][half h][dim d][tokens 8 h .. 8 h + 7]
 // f16, so that the 32 lanes of a half read 512 consecutive bytes.
 //
-// Pipeline: a ring of S stages of two 16-token blocks; wave 0 copies, one
-// barrier per step publishes a stage, after which all 256 threads expand
-// the step's V codes into the buffer while each wave runs Q.K and the
-// softmax on its rows; a second barrier publishes the buffer for P.V.
+// Pipeline: a ring of S stages of two 16-token blocks, each step's copies
+// spread over the four waves; one barrier per step publishes a stage.  All
+// 256 threads expand V codes into the buffer: with two buffers (where a
+// 3-stage ring fits beside them) the next step's, during this one; with one
+// buffer this step's, published by a second barrier before P.V.
 
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
