@@ -63,9 +63,13 @@ constexpr int ROW_SHL4 = 0x104;  // lane i reads lane i + 4 of its row of 16
 constexpr int ROW_SHR4 = 0x114;  // lane i reads lane i - 4
 constexpr int ROW_ROR8 = 0x128;  // lane i reads lane (i + 8) mod 16
 
+// Every lane is written (full row and bank masks), so the move needs no
+// "old" value: mov_dpp leaves it undefined, where update_dpp with an old of
+// 0 would first put a zero into the destination, one more instruction per
+// exchange.
 template <int CTRL>
 __device__ __forceinline__ float quad_swap(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
 // The value of lane (i ^ M) of the same row of 16 lanes, M in {1, 2, 4, 8}.
@@ -77,7 +81,8 @@ __device__ __forceinline__ float lane_xor(float v) {
   else {
     static_assert(M == 4, "");
     // lanes 0-3 and 8-11 (banks 0, 2) read i + 4; lanes 4-7 and 12-15 read i - 4
-    const int lo = __builtin_amdgcn_update_dpp(0, __float_as_int(v), ROW_SHL4, 0xF, 0x5, false);
+    // (banks 1 and 3 of the first move are left undefined and overwritten)
+    const int lo = __builtin_amdgcn_mov_dpp(__float_as_int(v), ROW_SHL4, 0xF, 0x5, false);
     return __int_as_float(__builtin_amdgcn_update_dpp(lo, __float_as_int(v), ROW_SHR4, 0xF, 0xA, false));
   }
 }
