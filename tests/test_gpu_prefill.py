@@ -49,7 +49,8 @@ def oracle(c, bl, sl):
 
 
 # (config, format, cached lengths, chunk): G * chunk rows per kv head span
-# several 64-row tiles with a ragged last one; chunks start mid-block
+# several row tiles (64 rows on the 16-row kernel, 128 on the 32-row one)
+# with a ragged last one, and waves with no rows; chunks start mid-block
 CASES = [
     (1, "BF16", [300], 37),
     (1, "FP8_ROW", [300], 37),
@@ -60,6 +61,8 @@ CASES = [
     (4, "K8V4", [150, 400, 7], 29),
     (5, "MXFP8", [200, 61], 70),
     (5, "BF16", [200, 61], 70),
+    (5, "FP8_ROW", [200, 61], 70),      # head_dim 128 on the 32-row kernel, two V buffers
+    (5, "FP8_TENSOR", [131, 60], 67),
     (3, "MXFP4", [260, 33], 41),
 ]
 
