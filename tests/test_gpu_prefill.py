@@ -76,10 +76,13 @@ def test_prefill_matches_oracle(cfg, fmt, lens, chunk):
     assert_lse_close(lse, ref_lse, "prefill " + W_name(c))
 
 
-def test_prefill_short_and_empty_sequences():
+@pytest.mark.parametrize("cfg,fmt", [(3, "NVFP4_G16"), (4, "K8V4"), (1, "BF16")])
+def test_prefill_short_and_empty_sequences(cfg, fmt):
     """Sequences shorter than the chunk: early queries see nothing (out 0,
-    lse -inf); an empty cache before the chunk; one sequence of length 0."""
-    c, bl, sl = prefill_case(3, "NVFP4_G16", [0, 5, 90], 24)
+    lse -inf); an empty cache before the chunk; one sequence of length 0.
+    NVFP4 runs the 16-row kernel, K8V4 and BF16 the 32-row one (where whole
+    waves then see nothing in a step)."""
+    c, bl, sl = prefill_case(cfg, fmt, [0, 5, 90], 24)
     sl = sl.copy()
     sl[1] = 10   # only the first 10 of sequence 1's 29 positions: queries 0 .. 13 see nothing
     sl[0] = 0    # sequence 0 has nothing at all
