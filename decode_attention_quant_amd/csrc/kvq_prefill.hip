@@ -474,7 +474,9 @@ __device__ __forceinline__ void expand_v_step(uint32_t stg, uint32_t vbuf, int t
     static_assert(D == 256, "4-bit V planes are built for head_dim 256");
     // thread (m, c, g, n): 16-byte chunk c of column n, tokens 4g..4g+3, of block m:
     // dims 16 (8c + jj) + n for jj < 8
-    const int m = tid >> 7, c = (tid >> 6) & 1, g = (tid >> 4) & 3, n = tid & 15;
+    // (lane bit 0 and bit 5 give g, bits 1-4 give n: 16 lanes then write 128
+    // consecutive bytes of the buffer, the two 8-byte halves of 8 slots)
+    const int m = tid >> 7, c = (tid >> 6) & 1, g = (tid & 1) | ((tid >> 4) & 2), n = (tid >> 1) & 15;
     const uint32_t blk = stg + m * T::STAGE;
     const uint4 cw = lds_read16(blk + T::SV + c * 1024 + (16 * g + n) * 16);
     uint4 sw4[2];
@@ -516,7 +518,7 @@ __device__ __forceinline__ void expand_v_step(uint32_t stg, uint32_t vbuf, int t
 #pragma unroll
     for (int rep = 0; rep < REPS; ++rep) {
       const int ci = tid + 256 * rep;
-      const int m = ci / (64 * NCH), c = (ci >> 6) % NCH, g = (ci >> 4) & 3, n = ci & 15;
+      const int m = ci / (64 * NCH), c = (ci >> 6) % NCH, g = (ci & 1) | ((ci >> 4) & 2), n = (ci >> 1) & 15;
       const uint32_t blk = stg + m * T::STAGE;
       const uint4 cw = lds_read16(blk + T::SV + c * 1024 + (16 * g + n) * 16);
       const uint32_t cws[4] = {cw.x, cw.y, cw.z, cw.w};
