@@ -447,6 +447,18 @@ def summarize_counters(fetch_dir, write_dir, bench_json):
     }
 
 
+def host_cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None where it is absent)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(s, budget_s=10.0):
     """The oracle as it stands, on whole sequences of the same workload (all
     kv heads; its pool built untimed), timed per decode step: append the
@@ -478,7 +490,7 @@ def cpu_baseline(s, budget_s=10.0):
             break
     blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
     return {"value": nbytes / elapsed / 1e9, "unit": "GB/s", "cores": int(max(blas) if blas else 1),
-            "kind": "oracle",
+            "kind": "oracle", "host_cpu": host_cpu_model(), "host_logical_cpus": os.cpu_count(),
             "sample": "%d whole sequences (%d cached tokens x %d kv heads) of the same workload; one step each: "
                       "append the n_q newest tokens, then fp64 attention over all cached pages; %.1f s" % (
                           seqs, tokens, c.H_kv, elapsed)}
