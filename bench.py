@@ -578,6 +578,8 @@ def main():
                     help="formats of the prefill-chunk append measurement, or 'none'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill attention measurement")
+    ap.add_argument("--prefill-formats", default="K8V4",
+                    help="comma-separated formats of the chunked-prefill measurement (the first is the headline)")
     ap.add_argument("--no-flush", action="store_true", help="time steps back to back, caches warm")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--summarize-counters", nargs="+", metavar="DIR_OR_JSON",
@@ -625,7 +627,13 @@ def main():
     achieved = s.kv_bytes / (split_ms * 1e-3) / 1e9
     append_formats = [] if args.append_formats == "none" else args.append_formats.split(",")
     appends = append_chunk_bench(append_formats, stream, probe) if append_formats else {}
-    prefill = None if args.no_prefill else prefill_bench(stream, probe)
+    prefill = None
+    if not args.no_prefill:
+        pf_formats = [f for f in args.prefill_formats.split(",") if f]
+        runs = {f: prefill_bench(stream, probe, fmt=f) for f in pf_formats}
+        prefill = dict(runs[pf_formats[0]])
+        if len(pf_formats) > 1:
+            prefill["per_kv_dtype"] = runs
     line = {
         "metric": METRIC,
         "value": res["GB_per_s"],
