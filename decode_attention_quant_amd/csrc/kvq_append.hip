@@ -3,10 +3,13 @@
 // quantization guide, section on the five formats; TokenSpeed mxfp8 and
 // fp8_e4m3; Qwen FP8-KV article's per-tensor symmetric FP8).
 //
-// A wave takes one plane of 16 consecutive tokens of one kv head, so that
-// what it writes lies in a few long runs of the tile (tokens of a 16-slot
-// block are adjacent in it) and whole cache lines are written at once.  The
-// row encoders are in kvq_encode.hpp.
+// Two kernels.  For long runs of tokens (prefill chunks), a wave takes one
+// plane of 16 consecutive tokens of one kv head, so that what it writes lies
+// in a few long runs of the tile (tokens of a 16-slot block are adjacent in
+// it) and whole cache lines are written at once.  For a few tokens (a decode
+// step's one per sequence), a wave takes one (token, kv head) and holds each
+// row across all its lanes, so the time is a load, a short encode and the
+// stores.  The encoders are in kvq_encode.hpp.
 #include <hip/hip_runtime.h>
 
 #include "kvq_encode.hpp"
@@ -95,9 +98,38 @@ __global__ __launch_bounds__(256) void append_kernel(uint8_t* __restrict__ pool,
   else append_v_wave<FMT, D>(pool, v, T, slots, geo, v_scale, it >> 1, lane);
 }
 
+// Wave w of the grid encodes K and V of token w / H_kv, kv head w % H_kv.
+template <int FMT, int D>
+__global__ __launch_bounds__(256) void append_token_kernel(uint8_t* __restrict__ pool, const uint16_t* __restrict__ k,
+                                                           const uint16_t* __restrict__ v, int64_t T,
+                                                           const int32_t* __restrict__ slots, Geometry geo,
+                                                           float k_scale, float v_scale) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= T * geo.H_kv) return;  // whole waves
+  const int64_t token = item / geo.H_kv;
+  const int head = (int)(item - token * geo.H_kv);
+  enc::TokenRow<D> rk, rv;  // loaded before the slot, so the three loads overlap
+  enc::load_k_token<D>(rk, k + item * D, lane);
+  enc::load_v_token<D>(rv, v + item * D, lane);
+  const int slot = slots[token];
+  if (slot < 0) return;
+  enc::encode_k_token<FMT, D>(pool, rk, slot, geo, head, k_scale, lane);
+  enc::encode_v_token<FMT, D>(pool, rv, slot, geo, head, v_scale, lane);
+}
+
+// Calls of at most this many tokens take append_token_kernel.
+constexpr int64_t TOKEN_KERNEL_MAX_T = 256;
+
 template <int FMT, int D>
 hipError_t launch_append_t(uint8_t* pool, const uint16_t* k, const uint16_t* v, int64_t T, const int32_t* slots,
                            const Geometry& geo, float ks, float vs, hipStream_t stream) {
+  if (T <= TOKEN_KERNEL_MAX_T) {
+    const int64_t blocks = (T * geo.H_kv + 3) / 4;
+    hipLaunchKernelGGL((append_token_kernel<FMT, D>), dim3((unsigned)blocks), dim3(256), 0, stream, pool, k, v, T,
+                       slots, geo, ks, vs);
+    return hipGetLastError();
+  }
   const int64_t items = 2 * ((T + 15) / 16) * geo.H_kv;  // K and V of 16 tokens x 1 head each
   const int64_t blocks = (items + 3) / 4;
   hipLaunchKernelGGL((append_kernel<FMT, D>), dim3((unsigned)blocks), dim3(256), 0, stream, pool, k, v, T, slots,

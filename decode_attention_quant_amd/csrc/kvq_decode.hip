@@ -49,34 +49,55 @@ namespace kvq {
 
 // ----------------------------------------------------------- fused append
 
-// Encode and store the new tokens of sequence b, kv head h at positions
-// [plo, phi) (at most one 16-token block) with one wave: the K rows (a quad
-// per token), then the V rows (a row of 16 lanes per 4 tokens), with the
-// write path's own encoders, so the bytes are those quantize-append stores.
-// Input token i of sequence b is row b * n_q + i of k_new / v_new.
-template <int FMT, int D>
-__device__ __forceinline__ void append_new_tokens(const DecodeArgs& a, const Geometry& geo, int b, int h, int L,
-                                               int plo, int phi, int lane) {
-  const int pnew = L - a.n_q;          // position of new token 0
-  const int64_t tok0 = (int64_t)b * a.n_q;
-  const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
-  auto slot_of = [&](int64_t tok) -> int {
-    const int p = pnew + (int)(tok - tok0);
-    return p >= 0 ? bt[p / geo.P] * geo.P + p % geo.P : -1;
-  };
-  const int ilo = plo - pnew, ihi = phi - pnew;  // new-token indexes written here
-  {
-    const int q = lane & 3;
-    const int i = ilo + (lane >> 2);  // a whole quad shares it
-    if (i < ihi) {
-      const int64_t tok = tok0 + i;
-      uint32_t raw[D / 8];
-      enc::load_k_row<D>(raw, a.k_new + (tok * geo.H_kv + h) * D + q * (D / 4));
-      enc::encode_k_row<base_format(FMT), D>(a.pool_w, raw, slot_of(tok), geo, h, a.enc_k_scale, q);
-    }
+// The new tokens of sequence b, kv head h at positions [plo, phi) (at most
+// one 16-token block; input token i of sequence b is row b * n_q + i of
+// k_new / v_new) are encoded one token at a time by the whole wave, with the
+// write path's single-token encoders, so the bytes are those quantize-append
+// stores.  The raw rows of the first TB tokens are loaded at the segment's
+// start, so that their latency overlaps the query's and the first blocks'.
+template <int D>
+struct NewRows {
+  static constexpr int TB = D == 256 ? 2 : 4;
+  enc::TokenRow<D> k[TB], v[TB];
+};
+
+__device__ __forceinline__ int64_t new_row(const DecodeArgs& a, const Geometry& geo, int b, int h, int i) {
+  return (((int64_t)b * a.n_q + i) * geo.H_kv + h) * geo.D;
+}
+
+template <int D>
+__device__ __forceinline__ void load_new_rows(NewRows<D>& nr, const DecodeArgs& a, const Geometry& geo, int b, int h,
+                                              int L, int plo, int phi, int lane) {
+  const int ilo = plo - (L - a.n_q), ihi = phi - (L - a.n_q);
+#pragma unroll
+  for (int u = 0; u < NewRows<D>::TB; ++u) {
+    const int64_t row = new_row(a, geo, b, h, min(ilo + u, ihi - 1));  // issued on every path
+    enc::load_k_token<D>(nr.k[u], a.k_new + row, lane);
+    enc::load_v_token<D>(nr.v[u], a.v_new + row, lane);
   }
-  enc::v_row_group<base_format(FMT), D>(a.pool_w, a.v_new, slot_of, geo, a.enc_v_scale, h, lane & 15,
-                           tok0 + ilo + 4 * (lane >> 4), tok0 + ilo, tok0 + ihi);
+}
+
+template <int FMT, int D>
+__device__ __forceinline__ void store_new_tokens(const NewRows<D>& nr, const DecodeArgs& a, const Geometry& geo, int b,
+                                                 int h, int L, int plo, int phi, int lane) {
+  const int pnew = L - a.n_q;  // position of new token 0
+  const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
+  auto slot_at = [&](int p) -> int { return bt[p / geo.P] * geo.P + p % geo.P; };
+  auto put = [&](const enc::TokenRow<D>& rk, const enc::TokenRow<D>& rv, int p) {
+    const int slot = slot_at(p);
+    enc::encode_k_token<base_format(FMT), D>(a.pool_w, rk, slot, geo, h, a.enc_k_scale, lane);
+    enc::encode_v_token<base_format(FMT), D>(a.pool_w, rv, slot, geo, h, a.enc_v_scale, lane);
+  };
+#pragma unroll
+  for (int u = 0; u < NewRows<D>::TB; ++u)
+    if (plo + u < phi) put(nr.k[u], nr.v[u], plo + u);
+  for (int p = plo + NewRows<D>::TB; p < phi; ++p) {
+    enc::TokenRow<D> rk, rv;
+    const int64_t row = new_row(a, geo, b, h, p - pnew);
+    enc::load_k_token<D>(rk, a.k_new + row, lane);
+    enc::load_v_token<D>(rv, a.v_new + row, lane);
+    put(rk, rv, p);
+  }
 }
 
 // ----------------------------------------------------------- the kernel
@@ -212,10 +233,10 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
     //      touch only cache lines of the block's own code plane.  Loads and
     //      stores of a wave complete in order as far as the vector-memory
     //      counter goes, so a ring block staged at iteration k >= 1, issued
-    //      after the wait for block k - 1, needs no wait of its own.  A block
+    //      after the wait for block k - 1, needs no wait of its own.  The new
+    //      rows are loaded here, so that they arrive with the query.  A block
     //      staged at start-up is stored first and waited for; a block that
-    //      the ring stages later is stored once the first copies are out
-    //      (its loads then overlap theirs), just before the block loop.
+    //      the ring stages later is stored just before the block loop.
     int kmine = -1;  // this wave's index k of its block with new tokens
     int mlo = 0, mhi = 0;
     if constexpr (FUSED) {
@@ -229,8 +250,10 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
       }
     }
     const bool late_append = T::RING && kmine >= T::RING_S - 1;
+    NewRows<D> nr;
+    if (FUSED && kmine >= 0) load_new_rows<D>(nr, a, geo, b, h, L, mlo, mhi, lane);
     if (FUSED && kmine >= 0 && !late_append) {
-      append_new_tokens<FMT, D>(a, geo, b, h, L, mlo, mhi, lane);
+      store_new_tokens<FMT, D>(nr, a, geo, b, h, L, mlo, mhi, lane);
       wait_vmcnt<0>();
     }
 
@@ -515,7 +538,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
     }
 
     if (FUSED && late_append) {
-      append_new_tokens<FMT, D>(a, geo, b, h, L, mlo, mhi, lane);
+      store_new_tokens<FMT, D>(nr, a, geo, b, h, L, mlo, mhi, lane);
       if (kmine == T::RING_S - 1) wait_vmcnt<0>();  // staged by the first iteration's refill
     }
 

@@ -783,25 +783,6 @@ __device__ __forceinline__ f16x4 v_operand(const Buf<FMT, D>& buf, int nt, int l
 
 // ----------------------------------------------------------- 64-lane FWHT
 
-// One butterfly stage across lanes M apart: the lower lane of each pair
-// keeps x + partner and the upper one partner - x, each rounded once.
-// M <= 8 is a DPP permutation inside a row of 16 lanes; M = 16 and 32 use
-// the swap instructions, which leave the lower lane's value in result 0
-// and the upper lane's in result 1, in both lanes of the pair.
-template <int M>
-__device__ __forceinline__ float xlane_butterfly(float x, int lane) {
-  const float sg = (lane & M) ? -1.0f : 1.0f;
-  if constexpr (M <= 8) {
-    return __builtin_fmaf(sg, x, lane_xor<M>(x));
-  } else {
-    static_assert(M == 16 || M == 32, "");
-    const uint32_t v = bitcast<uint32_t>(x);
-    const auto s = M == 16 ? __builtin_amdgcn_permlane16_swap(v, v, false, false)
-                           : __builtin_amdgcn_permlane32_swap(v, v, false, false);
-    return __builtin_fmaf(sg, bitcast<float>((uint32_t)s[1]), bitcast<float>((uint32_t)s[0]));
-  }
-}
-
 // Unnormalized Hadamard of a 64*E vector, lane l holding elements
 // E*l .. E*l+E-1 (any fp32 order is fine on the read path).  No LDS: the
 // cross-lane stages are register permutations, so a transform costs a few

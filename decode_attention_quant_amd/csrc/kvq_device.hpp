@@ -92,4 +92,23 @@ __device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v) {
   return __float_as_uint(lane_xor<M>(__uint_as_float(v)));
 }
 
+// One butterfly stage across lanes M apart: the lower lane of each pair
+// keeps x + partner and the upper one partner - x, each rounded once.
+// M <= 8 is a DPP permutation inside a row of 16 lanes; M = 16 and 32 use
+// the swap instructions, which leave the lower lane's value in result 0
+// and the upper lane's in result 1, in both lanes of the pair.
+template <int M>
+__device__ __forceinline__ float xlane_butterfly(float x, int lane) {
+  const float sg = (lane & M) ? -1.0f : 1.0f;
+  if constexpr (M <= 8) {
+    return __builtin_fmaf(sg, x, lane_xor<M>(x));
+  } else {
+    static_assert(M == 16 || M == 32, "");
+    const uint32_t v = bitcast<uint32_t>(x);
+    const auto s = M == 16 ? __builtin_amdgcn_permlane16_swap(v, v, false, false)
+                           : __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return __builtin_fmaf(sg, bitcast<float>((uint32_t)s[1]), bitcast<float>((uint32_t)s[0]));
+  }
+}
+
 }  // namespace kvq

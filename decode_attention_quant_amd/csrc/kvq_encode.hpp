@@ -785,5 +785,272 @@ __device__ __forceinline__ void load_k_row(uint32_t (&raw)[D / 8], const uint16_
   }
 }
 
+
+// ---------------------------------------------------------- single tokens
+// One token's K or V row held by a whole wave, for appends of a few tokens
+// (a decode step adds one per sequence), where the rows above leave most
+// lanes idle and give each busy lane a long serial chain.  N = D / 64
+// elements per lane:
+//
+//   K: lane l holds d = N l .. N l + N - 1 (the row in order), so its codes
+//      are N consecutive values of one K tile row;
+//   V: lane l = 16 Q + n holds d = 16 (N Q + k) + n, k < N: column n of
+//      n-tiles N Q .. N Q + N - 1, so its codes sit in one V tile row.
+//
+// The rotation runs the stages h = 1, 2, ..., 128 in that order, each
+// pairing the same two elements with one rounding, and every other step is
+// elementwise or an exact maximum, so the stored bytes are those of the
+// row encoders above.  Every lane of the wave must take part.
+
+// Max over the L lanes (L a power of two <= 64) whose index differs only in
+// its low log2 L bits.
+template <int L>
+__device__ __forceinline__ float max_over_lanes_wave(float a) {
+  a = max_over_lanes<(L < 16 ? L : 16)>(a);
+  if constexpr (L >= 32) {
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+    a = fmaxf(__uint_as_float((uint32_t)s[0]), __uint_as_float((uint32_t)s[1]));
+  }
+  if constexpr (L >= 64) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+    a = fmaxf(__uint_as_float((uint32_t)s[0]), __uint_as_float((uint32_t)s[1]));
+  }
+  return a;
+}
+
+// Raw bf16 elements of one token row in the wave's K or V order, two per word.
+template <int D>
+struct TokenRow {
+  uint32_t w[D / 128];
+};
+
+template <int D>
+__device__ __forceinline__ void load_k_token(TokenRow<D>& r, const uint16_t* row, int lane) {
+  if constexpr (D == 256) {
+    const uint2 w = *reinterpret_cast<const uint2*>(row + 4 * lane);
+    r.w[0] = w.x;
+    r.w[1] = w.y;
+  } else {
+    static_assert(D == 128, "");
+    r.w[0] = *reinterpret_cast<const uint32_t*>(row + 2 * lane);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void load_v_token(TokenRow<D>& r, const uint16_t* row, int lane) {
+  constexpr int N = D / 64;
+  const uint16_t* p = row + 16 * N * (lane >> 4) + (lane & 15);
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) r.w[i] = (uint32_t)p[32 * i] | ((uint32_t)p[32 * i + 16] << 16);
+}
+
+template <int D>
+__device__ __forceinline__ void unpack_token(const TokenRow<D>& r, float (&x)[D / 64]) {
+#pragma unroll
+  for (int i = 0; i < D / 128; ++i) {
+    x[2 * i] = bf16_to_f32(r.w[i] & 0xFFFFu);
+    x[2 * i + 1] = bf16_to_f32(r.w[i] >> 16);
+  }
+}
+
+// Quotient of x by its group scale, as the row encoders take it.
+template <int C>
+__device__ __forceinline__ float token_quot(float x, float s, float r, uint32_t sbits, bool fast) {
+  if constexpr (mx_scaled(C)) return ldexpf(x, 127 - (int)sbits);
+  else if constexpr (C == C_E4TEN) return fast ? div_scale(x, s, r) : __fdiv_rn(x, s);
+  else return div_scale(x, s, r);
+}
+
+// The code of one quotient in the low BITS bits.
+template <int C>
+__device__ __forceinline__ uint32_t token_code(float q) {
+  if constexpr (C == C_I8G64) return i8_bits(q) & 0xFFu;
+  else if constexpr (codec_bits(C) == 8) return e4m3_pair<false>(0u, q, 0.0f) & 0xFFu;
+  else return e2m1_pair<0>(0u, q, 0.0f) & 0xFu;
+}
+
+// Encode one token's K row (TokenRow in K order) and store it at `slot`.
+template <int FMT, int D>
+__device__ __forceinline__ void encode_k_token(uint8_t* __restrict__ pool, const TokenRow<D>& raw, int slot,
+                                               const Geometry& geo, int head, float k_scale, int lane) {
+  constexpr int N = D / 64;
+  constexpr int C = k_codec(FMT);
+  constexpr int BITS = codec_bits(C);
+  const int64_t page = slot / geo.P;
+  const int off = slot - (int)(page * geo.P);
+  const int blk = off >> 4, t = off & 15;
+  uint8_t* head_base = pool + page * geo.page_bytes + (int64_t)head * geo.head_bytes;
+  uint8_t* codes = head_base + geo.off_kc + (int64_t)blk * geo.kcode_blk;
+  uint8_t* scales = head_base + geo.off_ks + (int64_t)blk * geo.kscale_blk;
+  const int d0 = N * lane;
+  uint8_t* dst = codes + k_code_byte(BITS, t, d0);
+  if constexpr (C == C_BF16) {  // K of BF16 is stored bit for bit
+    if constexpr (N == 4) *reinterpret_cast<uint2*>(dst) = make_uint2(raw.w[0], raw.w[1]);
+    else *reinterpret_cast<uint32_t*>(dst) = raw.w[0];
+    return;
+  } else {
+    float x[N];
+    unpack_token<D>(raw, x);
+    if constexpr (k_rotated(FMT)) {
+      static_assert(D == 256, "the rotation is 256-point");
+      // h = 1, 2 inside the lane, h = 4 .. 128 across lanes 1 .. 32 apart
+#pragma unroll
+      for (int h = 1; h < N; h <<= 1)
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+          if ((i & h) == 0) {
+            const float a = x[i], b = x[i + h];
+            x[i] = a + b;
+            x[i + h] = a - b;
+          }
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        x[i] = xlane_butterfly<1>(x[i], lane);
+        x[i] = xlane_butterfly<2>(x[i], lane);
+        x[i] = xlane_butterfly<4>(x[i], lane);
+        x[i] = xlane_butterfly<8>(x[i], lane);
+        x[i] = xlane_butterfly<16>(x[i], lane);
+        x[i] = xlane_butterfly<32>(x[i], lane);
+        x[i] *= 0.0625f;
+      }
+    }
+    if constexpr (C == C_E2G16) divide_by_tensor_scale(x, k_scale);
+    float s = k_scale, r = 0.0f;
+    uint32_t sbits = 0u;
+    bool fast = true, zero = false;
+    if constexpr (C == C_E4TEN) {
+      r = __fdiv_rn(1.0f, s);
+      fast = s >= 0x1p-30f && s <= 0x1p30f;  // uniform
+    } else {
+      constexpr int GS = codec_group(C) < 0 ? D : codec_group(C);
+      group_scale<C>(max_over_lanes_wave<GS / N>(abs_max<N>(x)), s, r, sbits);
+      zero = !mx_scaled(C) && !(s > 0.0f);
+      if ((d0 % GS) == 0) {  // the group's first lane stores its scale
+        constexpr int G = D / GS;
+        const int grp = d0 / GS;
+        if constexpr (scale_bytes(C) == 2) *reinterpret_cast<uint16_t*>(scales + (t * G + grp) * 2) = (uint16_t)sbits;
+        else scales[t * G + grp] = (uint8_t)sbits;
+      }
+    }
+    uint32_t w = 0u;
+#pragma unroll
+    for (int i = 0; i < N; ++i) w |= token_code<C>(token_quot<C>(x[i], s, r, sbits, fast)) << (BITS * i);
+    if (zero) w = 0u;
+    if constexpr (BITS * N == 32) *reinterpret_cast<uint32_t*>(dst) = w;
+    else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w;
+  }
+}
+
+// Encode one token's V row (TokenRow in V order) and store it at `slot`.
+// 8- and 16-bit codes share their tile words with the slab's other tokens
+// and are written byte- or halfword-wise; 4-bit codes share bytes with the
+// other token of their pair and are set with atomic and/or.
+template <int FMT, int D>
+__device__ __forceinline__ void encode_v_token(uint8_t* __restrict__ pool, const TokenRow<D>& raw, int slot,
+                                               const Geometry& geo, int head, float v_scale, int lane) {
+  constexpr int N = D / 64;
+  constexpr int C = v_codec(FMT);
+  constexpr int BITS = codec_bits(C);
+  const int Q = lane >> 4, n = lane & 15;
+  const int64_t page = slot / geo.P;
+  const int off = slot - (int)(page * geo.P);
+  const int blk = off >> 4, t = off & 15, gv = t >> 2, te = t & 3;
+  uint8_t* head_base = pool + page * geo.page_bytes + (int64_t)head * geo.head_bytes;
+  uint8_t* codes = head_base + geo.off_vc + (int64_t)blk * geo.vcode_blk;
+  uint8_t* scales = head_base + geo.off_vs + (int64_t)blk * geo.vscale_blk;
+  float x[N];
+  unpack_token<D>(raw, x);
+  if constexpr (v_rotated(FMT)) {
+    static_assert(D == 256, "the rotation is 256-point");
+    // h = 1 .. 8 across lanes 1 .. 8 apart, h = 16, 32 inside the lane,
+    // h = 64, 128 across lanes 16, 32 apart
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      x[i] = xlane_butterfly<1>(x[i], lane);
+      x[i] = xlane_butterfly<2>(x[i], lane);
+      x[i] = xlane_butterfly<4>(x[i], lane);
+      x[i] = xlane_butterfly<8>(x[i], lane);
+    }
+#pragma unroll
+    for (int h = 1; h < N; h <<= 1)
+#pragma unroll
+      for (int i = 0; i < N; ++i)
+        if ((i & h) == 0) {
+          const float a = x[i], b = x[i + h];
+          x[i] = a + b;
+          x[i + h] = a - b;
+        }
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      x[i] = xlane_butterfly<16>(x[i], lane);
+      x[i] = xlane_butterfly<32>(x[i], lane);
+      x[i] *= 0.0625f;
+    }
+  }
+  if constexpr (C == C_E2G16) divide_by_tensor_scale(x, v_scale);
+  uint32_t cd[N];  // code of element k in the low BITS bits
+  if constexpr (C == C_F16) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) cd[k] = f16_bits(x[k]);
+  } else if constexpr (C == C_E4TEN) {
+    const float s = v_scale, r = __fdiv_rn(1.0f, s);
+    const bool fast = s >= 0x1p-30f && s <= 0x1p30f;  // uniform
+#pragma unroll
+    for (int k = 0; k < N; ++k) cd[k] = token_code<C>(token_quot<C>(x[k], s, r, 0u, fast));
+  } else {
+    // a group is NTG whole n-tiles (a row: all of them): the lane's NTG
+    // elements of it, then the 16 (row: 64) lanes that hold its columns
+    constexpr int GS = codec_group(C) < 0 ? D : codec_group(C);
+    constexpr int NTG = GS / 16 < N ? GS / 16 : N;  // a group's elements in one lane
+    constexpr int GPL = N / NTG;                    // groups per lane
+    constexpr int G = D / GS;
+    uint32_t sb[GPL];
+#pragma unroll
+    for (int gl = 0; gl < GPL; ++gl) {
+      float am = abs_max<NTG>(x + gl * NTG);
+      am = GS == D ? max_over_lanes_wave<64>(am) : max_over_lanes_wave<16>(am);
+      float s, r;
+      group_scale<C>(am, s, r, sb[gl]);
+      const bool zero = !mx_scaled(C) && !(s > 0.0f);
+#pragma unroll
+      for (int k = gl * NTG; k < gl * NTG + NTG; ++k)
+        cd[k] = zero ? 0u : token_code<C>(token_quot<C>(x[k], s, r, sb[gl], true));
+    }
+    // lane n < GPL of each lane row stores the scale of its group n (a row
+    // scale: lane 0)
+    uint32_t mine = sb[0];
+#pragma unroll
+    for (int gl = 1; gl < GPL; ++gl) mine = n == gl ? sb[gl] : mine;
+    if (n < GPL && (GS < D || Q == 0)) {
+      const int grp = GS == D ? 0 : (N * Q) / NTG + n;
+      if constexpr (BITS == 4) scales[gv * 4 * G + grp * 4 + te] = (uint8_t)mine;
+      else if constexpr (scale_bytes(C) == 2) *reinterpret_cast<uint16_t*>(scales + (t * G + grp) * 2) = (uint16_t)mine;
+      else scales[t * G + grp] = (uint8_t)mine;
+    }
+  }
+  if constexpr (BITS == 4) {
+    // the lane's nibbles of n-tiles 4 Q + k (k < 4) lie in one 8-byte word of
+    // tile row gv * 16 + n, 16 bits apart
+    static_assert(N == 4, "4-bit V planes are 256 wide");
+    const int st = 8 * (te >> 1) + 4 * (te & 1);
+    uint64_t v = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v |= (uint64_t)cd[k] << (16 * k);
+    const uint64_t mask = 0x000F000F000F000Full << st;
+    unsigned long long* wp =
+        reinterpret_cast<unsigned long long*>(codes + (Q >> 1) * 1024 + (gv * 16 + n) * 16 + (Q & 1) * 8);
+    atomicAnd(wp, ~mask);
+    atomicOr(wp, v << st);
+  } else {
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      const int jt = N * Q + k;
+      if constexpr (BITS == 8) codes[(jt >> 2) * 1024 + (gv * 16 + n) * 16 + (jt & 3) * 4 + te] = (uint8_t)cd[k];
+      else *reinterpret_cast<uint16_t*>(codes + (jt >> 1) * 1024 + (gv * 16 + n) * 16 + (jt & 1) * 8 + 2 * te) =
+               (uint16_t)cd[k];
+    }
+  }
+}
+
 }  // namespace enc
 }  // namespace kvq

@@ -19,6 +19,13 @@ CASES = [
 ]
 
 
+# quantize_append takes its single-token kernel (a wave per token and kv
+# head) for calls of at most this many tokens and its 16-token row kernel
+# above; the tests below run on both sides of it.
+TOKEN_KERNEL_MAX_T = 256
+KERNELS = ["token", "rows"]
+
+
 def _mismatch(bl):
     got = bl.pool_gpu.cpu().numpy()
     ref = bl.pool_ref
@@ -26,9 +33,11 @@ def _mismatch(bl):
     return got, ref, diff
 
 
+@pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("fmt,cfg,_", CASES)
-def test_append_bytes_bit_exact(fmt, cfg, _):
-    lens = [130, 65, 7, 1]
+def test_append_bytes_bit_exact(fmt, cfg, _, kernel):
+    lens = [130, 65, 7, 1] if kernel == "token" else [330, 65, 7, 1]
+    assert (sum(lens) <= TOKEN_KERNEL_MAX_T) == (kernel == "token")
     c = W.make_case(cfg, fmt, device="cpu", B=4, lengths=lens)
     bl = build(c)
     got, ref, diff = _mismatch(bl)
@@ -81,24 +90,29 @@ def _adversarial_rows(D, rng):
     return np.stack(rows)
 
 
+@pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("fmt", ["INT8_G64", "FP8_ROW", "NVFP4_G16", "K8V4", "MXFP8", "FP8_TENSOR", "BF16", "MXFP4"])
-def test_append_adversarial_rows_bit_exact(fmt):
+def test_append_adversarial_rows_bit_exact(fmt, kernel):
     require_gpu()
     D, P, H = 256, 64, 2
     rng = np.random.default_rng(77)
     rows = _adversarial_rows(D, rng)
+    if kernel == "rows":  # the rows again, scaled by powers of two, past the single-token limit
+        rows = np.concatenate([rows * np.float32(2.0 ** (i % 5 - 2)) for i in range(27)])
     n = rows.shape[0]
+    assert (n <= TOKEN_KERNEL_MAX_T) == (kernel == "token")
     x = np.stack([rows, rows[::-1] * np.float32(0.5)], axis=1)  # [n][H][D]
     xt = torch.from_numpy(x).to(torch.bfloat16)
     k_scale = v_scale = 0.37
-    d = kvq.desc(fmt, D, P, H, 1, k_scale, v_scale)
+    pages = -(-n // P)
+    d = kvq.desc(fmt, D, P, H, pages, k_scale, v_scale)
     geo = OL.Geometry(W.FORMAT_IDS[fmt], D, P, H)
     slots = torch.arange(n, dtype=torch.int32)
     pool = kvq.alloc_pool(d)
-    note("append adversarial", fmt)
+    note("append adversarial", fmt, kernel)
     kvq.quantize_append(d, pool, xt.cuda(), xt.flip(0).contiguous().cuda(), slots.cuda())
     torch.cuda.synchronize()
-    ref = np.full(geo.page_bytes, 0xFF, np.uint8)
+    ref = np.full(pages * geo.page_bytes, 0xFF, np.uint8)
     OA.quantize_append(geo, ref, W.bf16_bits(xt), W.bf16_bits(xt.flip(0)), slots.numpy(), k_scale, v_scale)
     got = pool.cpu().numpy()
     diff = np.flatnonzero(got != ref)
@@ -149,12 +163,13 @@ def test_dequant_page_original_domain(fmt, cfg):
 
 @pytest.mark.parametrize("fmt,cfg", [("K8V4", 4), ("NVFP4_G16", 3), ("INT8_G64", 2), ("FP8_ROW", 2),
                                      ("FP8_TENSOR", 2), ("BF16", 1), ("MXFP8", 5), ("MXFP4", 3)])
-def test_append_chunks_at_any_offset(fmt, cfg):
+@pytest.mark.parametrize("chunk", [37, 75])
+def test_append_chunks_at_any_offset(fmt, cfg, chunk):
     """Prefill chunks appended after cached prefixes start at every alignment
     inside a 16-slot block and a 4-slot slab (consecutive slots, shifted),
-    the layout of the bench's prefill workload; the pool stays bit-exact."""
+    the layout of the bench's prefill workload; the pool stays bit-exact.
+    4 chunks of 37 tokens take the single-token kernel, of 75 the rows."""
     lens = [5, 70, 130, 3] if cfg != 5 else [5, 134, 66, 3]
-    chunk = 37
     c = W.make_case(cfg, fmt, device="cpu", B=4, lengths=lens, reserve=chunk)
     bl = build(c)
     k, v, slots = W.append_chunk(c, chunk)
@@ -172,14 +187,15 @@ def test_append_chunks_at_any_offset(fmt, cfg):
 
 @pytest.mark.parametrize("fmt,cfg", [("NVFP4_G16", 3), ("K8V4", 4), ("INT8_G64", 2), ("FP8_ROW", 2), ("MXFP8", 5),
                                      ("BF16", 1), ("MXFP4", 4)])
-def test_append_slots_in_random_order(fmt, cfg):
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_append_slots_in_random_order(fmt, cfg, kernel):
     """One call writes every slot of a few pages in random input order, so the
     tokens that share a slab (and, for 4-bit V, a byte) sit in different rows
     and waves and are stored concurrently, token by token."""
     require_gpu()
     c = W.make_case(cfg, fmt, device="cpu", B=1, lengths=[8])
     geo = OL.Geometry(c.fmt, c.D, c.P, c.H_kv)
-    num_pages = 4
+    num_pages = TOKEN_KERNEL_MAX_T // c.P + (kernel == "rows")
     d = kvq.desc(c.fmt, c.D, c.P, c.H_kv, num_pages, c.k_scale, c.v_scale)
     n = num_pages * c.P
     gen = torch.Generator().manual_seed(41)
@@ -187,7 +203,7 @@ def test_append_slots_in_random_order(fmt, cfg):
     v = torch.randn((n, c.H_kv, c.D), generator=gen).to(torch.bfloat16)
     slots = torch.as_tensor(np.random.default_rng(41).permutation(n).astype(np.int32))
     pool = kvq.alloc_pool(d, fill=0x5A)
-    note("append random order", fmt)
+    note("append random order", fmt, kernel)
     kvq.quantize_append(d, pool, k.cuda(), v.cuda(), slots.cuda())
     torch.cuda.synchronize()
     ref = np.full(num_pages * geo.page_bytes, 0x5A, np.uint8)

@@ -94,6 +94,19 @@ def test_fused_step_single_query_row(cfg, fmt, H_q, H_kv):
     check_step(c, bl, 1)
 
 
+@pytest.mark.parametrize("cfg,fmt,n_q,H_q,H_kv", [(3, "NVFP4_G16", 4, 4, 4), (4, "K8V4", 3, 4, 4),
+                                                  (2, "INT8_G64", 5, 2, 2), (5, "MXFP8", 8, None, None),
+                                                  (1, "BF16", 6, 2, 2)])
+def test_fused_step_many_new_tokens(cfg, fmt, n_q, H_q, H_kv):
+    """More new tokens per sequence than the kernel loads ahead (2 rows at
+    head_dim 256, 4 at 128): the rest are loaded and encoded one by one, and
+    the new tokens of a sequence may span two blocks (two owner waves)."""
+    c = W.make_case(cfg, fmt, device="cpu", B=3, lengths=[701, 126, 9], n_q=n_q, H_q=H_q, H_kv=H_kv, reserve=n_q)
+    assert (c.H_q // c.H_kv) * c.n_q <= 16
+    bl = build(c)
+    check_step(c, bl, n_q)
+
+
 def test_fused_step_rejects_more_than_one_row_tile():
     """G * n_q = 24 (24 / 4 GQA with 4 MTP tokens) takes two row tiles, so a
     block has two reading workgroups and the fused step is refused (the
