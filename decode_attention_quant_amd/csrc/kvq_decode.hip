@@ -416,11 +416,17 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
         }
       }
       const uint32_t qexp_a = (uint32_t)(uintptr_t)(void*)qexp;
-      auto qrow_a = [&](int row) -> uint32_t {  // LDS byte address of row `row` (ring formats)
+      // LDS byte address of row `row` (ring formats).  The rings' strides
+      // are multiples of 256 bytes, so rows placed 1 KB apart would put the
+      // 16 lanes that read 16 different rows at one offset into one bank;
+      // row r is shifted by 16 r bytes, and those lanes read 16 distinct
+      // 16-byte slots of every 256.
+      auto qrow_a = [&](int row) -> uint32_t {
         return (uint32_t)(uintptr_t)(void*)sm_o +
-               (uint32_t)((row & 3) * T::RING_S * T::STAGE + (T::RING_S - 1) * T::STAGE + (row >> 2) * D * 4);
+               (uint32_t)((row & 3) * T::RING_S * T::STAGE + (T::RING_S - 1) * T::STAGE + (row >> 2) * D * 4 +
+                          16 * row);
       };
-      if constexpr (T::RING) static_assert(T::STAGE >= 4 * D * 4, "four rows fit a stage");
+      if constexpr (T::RING) static_assert(T::STAGE >= 4 * D * 4 + 16 * 15, "four shifted rows fit a stage");
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = wave + 4 * i;  // rows past Rt hold values nobody reads
