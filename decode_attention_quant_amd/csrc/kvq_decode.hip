@@ -791,6 +791,14 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
 #pragma unroll
         for (int i = 0; i < E; ++i) xo[i] += sm_o[(ww * Rt + row) * D + E * lane + i];
       if (!direct) {
+        // the partial leaves in the original domain (the rotation is linear,
+        // so merging rotated-back partials equals rotating the merged one
+        // back), which lets the combine split a row across workgroups
+        if constexpr (T::VROT) {
+          fwht_wave<E>(xo, lane);
+#pragma unroll
+          for (int i = 0; i < E; ++i) xo[i] *= 0.0625f;
+        }
         const int64_t prow = (int64_t)(u + w) * a.R + rr2;
         float* op = a.ws_o + prow * D + E * lane;
 #pragma unroll
@@ -823,29 +831,35 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
 }
 
 // ----------------------------------------------------------- combine
-// One workgroup of NT = SG D / 4 threads per (unit, row); thread (g, c) owns
-// elements 4c .. 4c + 3 and merges partials g, g + SG, ...
-// with a running maximum, rescaling what it holds when the maximum grows
-// (the same log-sum-exp merge as the split kernel's); the groups then merge
-// through LDS.  Units finished by the split kernel (one workgroup,
+// One workgroup of SG x DL threads per (unit, row, column slice), DL =
+// D / (4 NS) threads per slice of D / NS columns; thread (g, c) owns columns
+// 4c .. 4c + 3 of the slice and merges partials g, g + SG, ... with a
+// running maximum, rescaling what it holds when the maximum grows (the same
+// log-sum-exp merge as the split kernel's); the groups then merge through
+// LDS.  The partials are already in the original domain, so a row's slices
+// are independent: a unit split many ways spreads its partials' bytes over
+// NS workgroups.  Units finished by the split kernel (one workgroup,
 // write_direct) are skipped; empty sequences get out = 0, lse = -inf.
 
-template <int D, bool VROT, int SG>
-__global__ __launch_bounds__(SG * D / 4) void decode_combine_kernel(DecodeArgs a, int H_kv) {
+template <int D, int SG, int NS>
+__global__ __launch_bounds__(SG * D / (4 * NS)) void decode_combine_kernel(DecodeArgs a, int H_kv) {
   constexpr float NEG_INF = -__builtin_inff();
-  constexpr int DL = D / 4;       // threads per partial row (4 elements each)
+  constexpr int DL = D / (4 * NS);  // threads per partial slice (4 columns each)
   __shared__ float4 sacc[SG][DL];
   __shared__ float sm[SG], sl[SG];
   const int tid = threadIdx.x, c = tid % DL, g = tid / DL;
-  const int u = (int)(blockIdx.x / (unsigned)a.R), rr = (int)(blockIdx.x - (unsigned)u * a.R);
+  const unsigned item = blockIdx.x / (unsigned)NS;
+  const int col0 = (int)(blockIdx.x - item * (unsigned)NS) * (D / NS) + 4 * c;
+  const int u = (int)(item / (unsigned)a.R), rr = (int)(item - (unsigned)u * a.R);
   const int b = u / H_kv, h = u - b * H_kv;
   const int qi = rr / a.G, qh = h * a.G + (rr - qi * a.G);
   const int64_t orow = ((int64_t)b * a.n_q + qi) * a.H_q + qh;
+  const bool lse_writer = col0 == 0;  // thread 0 of slice 0
   const int L = a.seq_lens[b];
   const int nb = (L + 15) >> 4;
   if (nb == 0) {
-    if (tid < DL) *reinterpret_cast<float4*>(a.out + orow * D + 4 * c) = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (a.lse != nullptr && tid == 0) a.lse[orow] = NEG_INF;
+    if (tid < DL) *reinterpret_cast<float4*>(a.out + orow * D + col0) = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (a.lse != nullptr && lse_writer && tid == 0) a.lse[orow] = NEG_INF;
     return;
   }
   const int total = a.ws_cum[a.B];
@@ -854,7 +868,7 @@ __global__ __launch_bounds__(SG * D / 4) void decode_combine_kernel(DecodeArgs a
   const int wa = start / per, wb = (start + nb - 1) / per;
   if (wa == wb && a.write_direct) return;
   const float* ml = a.ws_ml + ((int64_t)(u + wa) * a.R + rr) * 2;
-  const float* po = a.ws_o + ((int64_t)(u + wa) * a.R + rr) * D + 4 * c;
+  const float* po = a.ws_o + ((int64_t)(u + wa) * a.R + rr) * D + col0;
   const int nseg = wb - wa + 1;
   const int64_t sml = (int64_t)a.R * 2, so = (int64_t)a.R * D;  // slot strides
 
@@ -922,15 +936,9 @@ __global__ __launch_bounds__(SG * D / 4) void decode_combine_kernel(DecodeArgs a
     A.x += w * v.x; A.y += w * v.y; A.z += w * v.z; A.w += w * v.w;
   }
   const float inv = Lt > 0.f ? a.v_out_scale / Lt : 0.f;
-  float xv[4] = {A.x * inv, A.y * inv, A.z * inv, A.w * inv};
-  if constexpr (VROT) {
-    static_assert(D == 256, "the rotation is 256-point");
-    fwht_wave<4>(xv, c);  // the 64 threads of group 0 are one wave holding the row
-#pragma unroll
-    for (int i = 0; i < 4; ++i) xv[i] *= 0.0625f;
-  }
-  *reinterpret_cast<float4*>(a.out + orow * D + 4 * c) = make_float4(xv[0], xv[1], xv[2], xv[3]);
-  if (a.lse != nullptr && tid == 0) a.lse[orow] = Lt > 0.f ? (M + __log2f(Lt)) * 0.69314718055994531f : NEG_INF;
+  *reinterpret_cast<float4*>(a.out + orow * D + col0) = make_float4(A.x * inv, A.y * inv, A.z * inv, A.w * inv);
+  if (a.lse != nullptr && lse_writer && tid == 0)
+    a.lse[orow] = Lt > 0.f ? (M + __log2f(Lt)) * 0.69314718055994531f : NEG_INF;
 }
 
 // ----------------------------------------------------------- launchers
@@ -1014,22 +1022,25 @@ hipError_t launch_decode_combine(const Geometry& geo, const DecodeArgs& a, hipSt
   const int64_t units = (int64_t)a.B * geo.H_kv;
   const int64_t rows = units * a.R;
   if (rows == 0) return hipSuccess;
-  const bool vrot = v_rotated(geo.fmt);
-  // partials merged side by side: about the partials per unit, 1 .. 16
+  // about the partials per unit: up to 16 merged side by side in one
+  // workgroup per row; more (a few long sequences over the whole grid) in
+  // 16 or 32 groups per 64-column slice, so that a row's partials are read
+  // by D / 64 workgroups
   const int64_t expect = a.nwg / units + 1;
-  const int sg = expect >= 16 ? 16 : expect >= 8 ? 8 : expect >= 4 ? 4 : expect >= 2 ? 2 : 1;
-#define KVQ_COMBINE(DD, VR)                                                                               \
-  switch (sg) {                                                                                           \
-    case 16: hipLaunchKernelGGL((decode_combine_kernel<DD, VR, 16>), dim3((unsigned)rows), dim3(4 * DD), 0, stream, a, geo.H_kv); break; \
-    case 8: hipLaunchKernelGGL((decode_combine_kernel<DD, VR, 8>), dim3((unsigned)rows), dim3(2 * DD), 0, stream, a, geo.H_kv); break; \
-    case 4: hipLaunchKernelGGL((decode_combine_kernel<DD, VR, 4>), dim3((unsigned)rows), dim3(DD), 0, stream, a, geo.H_kv); break; \
-    case 2: hipLaunchKernelGGL((decode_combine_kernel<DD, VR, 2>), dim3((unsigned)rows), dim3(DD / 2), 0, stream, a, geo.H_kv); break; \
-    default: hipLaunchKernelGGL((decode_combine_kernel<DD, VR, 1>), dim3((unsigned)rows), dim3(DD / 4), 0, stream, a, geo.H_kv); break; \
-  }
-  if (geo.D == 256 && vrot) KVQ_COMBINE(256, true)
-  else if (geo.D == 256) KVQ_COMBINE(256, false)
-  else if (geo.D == 128 && !vrot) KVQ_COMBINE(128, false)
+#define KVQ_COMBINE(DD, SG, NS)                                                                        \
+  hipLaunchKernelGGL((decode_combine_kernel<DD, SG, NS>), dim3((unsigned)(rows * NS)), dim3(SG * DD / (4 * NS)), 0, \
+                     stream, a, geo.H_kv)
+#define KVQ_COMBINE_D(DD)                                                           \
+  if (expect >= 32) KVQ_COMBINE(DD, 32, DD / 64);                                   \
+  else if (expect >= 16) KVQ_COMBINE(DD, 16, DD / 64);                              \
+  else if (expect >= 8) KVQ_COMBINE(DD, 8, 1);                                      \
+  else if (expect >= 4) KVQ_COMBINE(DD, 4, 1);                                      \
+  else if (expect >= 2) KVQ_COMBINE(DD, 2, 1);                                      \
+  else KVQ_COMBINE(DD, 1, 1);
+  if (geo.D == 256) { KVQ_COMBINE_D(256) }
+  else if (geo.D == 128) { KVQ_COMBINE_D(128) }
   else return hipErrorInvalidValue;
+#undef KVQ_COMBINE_D
 #undef KVQ_COMBINE
   return hipGetLastError();
 }

@@ -261,10 +261,11 @@ kvq_status kvq_decode_step(const kvq_cache_desc* desc, void* pool, const void* k
  *   [slots][rows][head_dim]; slots = batch * num_kv_heads + num_workgroups,
  *   rows = G * n_q.  m is the running maximum in base-2 units of the scaled
  *   score, l the softmax denominator relative to it, o the unnormalized
- *   output (still rotated for NVFP4_G16 and K8V4).
- * kvq_decode_combine merges each unit's partials, normalizes, undoes the
- * rotation and writes out / lse exactly as kvq_decode_attention does; pass
- * the same num_workgroups (0 = planned) and flags to both.
+ *   output in the original domain (the split phase rotates the partials of
+ *   rotated V planes back: NVFP4_G16, K8V4, MXFP4).
+ * kvq_decode_combine merges each unit's partials, normalizes and writes
+ * out / lse exactly as kvq_decode_attention does; pass the same
+ * num_workgroups (0 = planned) and flags to both.
  * flags & KVQ_SPLIT_WRITE_WHOLE_UNITS: a unit held entirely by one split
  * workgroup is finished by the split phase (written to out / lse, which
  * kvq_decode_split then needs) and the combine skips it; this is what
