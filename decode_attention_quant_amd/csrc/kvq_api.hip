@@ -35,6 +35,7 @@ constexpr int MAX_BATCH = 4096;  // the split kernel keeps a per-sequence prefix
 
 struct Plan {
   int32_t R, tiles, units, nwg, slots;
+  int32_t cus, per_cu;  // the device's CUs and the split workgroups one holds (0: unknown)
   size_t cum_bytes, ml_bytes, o_bytes;
   size_t total() const { return cum_bytes + ml_bytes + o_bytes; }
 };
@@ -67,8 +68,17 @@ kvq_status make_plan(const kvq_cache_desc* d, int32_t batch, int32_t n_q, int32_
   p->tiles = (p->R + 15) / 16;
   p->units = batch * d->num_kv_heads;
   if (nwg_req < 0) return KVQ_ERR_INVALID_ARGUMENT;
+  p->cus = p->per_cu = 0;
   if (nwg_req > 0) {
     p->nwg = nwg_req;
+    int dev = 0, cus = 0, per_cu = 0;
+    const Geometry geo = make_geometry(d->format, d->head_dim, d->page_size, d->num_kv_heads);
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        decode_split_occupancy(geo, batch, p->R, &per_cu) == hipSuccess && cus > 0 && per_cu > 0) {
+      p->cus = cus;
+      p->per_cu = per_cu;
+    }
   } else {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess) return KVQ_ERR_HIP;
@@ -76,6 +86,8 @@ kvq_status make_plan(const kvq_cache_desc* d, int32_t batch, int32_t n_q, int32_
       return KVQ_ERR_HIP;
     const Geometry geo = make_geometry(d->format, d->head_dim, d->page_size, d->num_kv_heads);
     if (decode_split_occupancy(geo, batch, p->R, &per_cu) != hipSuccess || per_cu < 1) return KVQ_ERR_HIP;
+    p->cus = cus;
+    p->per_cu = per_cu;
     // Whole rounds of resident workgroups: one, or two when the cache can
     // hold more than 256 blocks per resident workgroup.  A partial last
     // round would run a few workgroups alone at the end (measured: a 640-
@@ -109,6 +121,12 @@ DecodeArgs base_args(const kvq_cache_desc* d, const Plan& p, int32_t batch, int3
   a.seq_lens = seq_lens;
   a.B = batch; a.n_q = n_q; a.H_q = H_q; a.G = H_q / d->num_kv_heads; a.R = p.R;
   a.max_pages = max_pages; a.nwg = p.nwg;
+  // a grid of one resident round only: with more rounds the two
+  // workgroups of a CU are best left staggered (pacing the first round's
+  // younger ones measured 1.5-2% slower for 16 rounds)
+  const bool one_round = p.per_cu >= 2 && (int64_t)p.nwg <= (int64_t)p.cus * p.per_cu;
+  a.pace_cus = one_round ? p.cus : 0;
+  a.pace_round = one_round ? p.cus * p.per_cu : 0;
   a.qk_scale = softmax_scale * 1.4426950408889634f * (k_tensor_scaled(d->format) ? d->k_scale : 1.0f);
   a.v_out_scale = v_tensor_scaled(d->format) ? d->v_scale : 1.0f;
   uint8_t* ws = static_cast<uint8_t*>(workspace);

@@ -647,7 +647,14 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
         // the other, which then runs its last blocks without a partner to
         // hide its stalls.  Stepping the priority down as a wave progresses
         // lets the one behind catch up, so the two finish close together.
-        const int q1 = nk >> 2, q2 = nk >> 1, q3 = nk - (nk >> 2);
+        // Even so the younger workgroup of a CU (dispatched once every CU
+        // has one) ended about 5 us after the older one at 1 x 262K tokens
+        // (per-wave clock stamps, every run alike); it steps down at 3/8,
+        // 5/8 and 7/8 of its blocks instead of 1/4, 1/2 and 3/4 (for grids
+        // of one resident round, whose dispatch order is known).
+        const bool young = (int)blockIdx.x >= a.pace_cus && (int)blockIdx.x < a.pace_round;
+        const int q1 = young ? (3 * nk) >> 3 : nk >> 2, q2 = young ? (5 * nk) >> 3 : nk >> 1,
+                  q3 = young ? (7 * nk) >> 3 : nk - (nk >> 2);
         auto pace = [&](int k) {
           if (k == q1) __builtin_amdgcn_s_setprio(2);
           if (k == q2) __builtin_amdgcn_s_setprio(1);
