@@ -401,10 +401,12 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
 #pragma unroll
         for (int i = 0; i < 4; ++i) qraw[i] = *reinterpret_cast<const uint2*>(qrow_ptr(i) + E * lane);
       }
+      // rows past Rt are neither transformed nor written: the lanes that
+      // would read them select 0 instead (qrow_ok below)
       float xq[4][E], amx[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        {
+        if (wave + 4 * i < Rt) {
           xq[i][0] = bf16_to_f32(qraw[i].x & 0xFFFFu); xq[i][1] = bf16_to_f32(qraw[i].x >> 16);
           xq[i][2] = bf16_to_f32(qraw[i].y & 0xFFFFu); xq[i][3] = bf16_to_f32(qraw[i].y >> 16);
           fwht_wave<E>(xq[i], lane);
@@ -429,8 +431,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
       if constexpr (T::RING) static_assert(T::STAGE >= 4 * D * 4 + 16 * 15, "four shifted rows fit a stage");
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = wave + 4 * i;  // rows past Rt hold values nobody reads
-        {
+        const int row = wave + 4 * i;
+        if (row < Rt) {
           if constexpr (T::RING) {
             lds_put4(qrow_a(row) + 16 * lane, xq[i][0], xq[i][1], xq[i][2], xq[i][3]);
             if (lane == 0) lds_put1(qexp_a + 4 * row, amx[i]);
