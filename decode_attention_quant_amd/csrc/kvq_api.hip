@@ -88,24 +88,20 @@ kvq_status make_plan(const kvq_cache_desc* d, int32_t batch, int32_t n_q, int32_
     if (decode_split_occupancy(geo, batch, p->R, &per_cu) != hipSuccess || per_cu < 1) return KVQ_ERR_HIP;
     p->cus = cus;
     p->per_cu = per_cu;
-    // Whole rounds of resident workgroups: one, or two when the cache can
-    // hold more than 256 blocks per resident workgroup.  A partial last
-    // round would run a few workgroups alone at the end (measured: a 640-
-    // workgroup grid on 512 slots spent a third of its time on the last
-    // 128), and many rounds pay each workgroup's start-up and merge again.
-    // Many short units (at most 256 blocks, at least one per resident
-    // workgroup) get one workgroup each instead: a range that is exactly
-    // one unit is a single segment (measured 1.4% faster for 8192 units of
-    // 256 blocks than 1024 workgroups of 8 units).
+    // One round of resident workgroups.  A partial last round would run a
+    // few workgroups alone at the end (measured: a 640-workgroup grid on
+    // 512 slots spent a third of its time on the last 128), and every
+    // further round pays each workgroup's start-up and merge again
+    // (measured: two rounds for 32 sequences of 8K-32K tokens were 4-6%
+    // slower than one, 1.3% for 64 of 1K-128K).  Many short units (at most
+    // 256 blocks, at least one per resident workgroup) get one workgroup
+    // each instead: a range that is exactly one unit is a single segment
+    // (measured 1.4% faster for 8192 units of 256 blocks than 1024
+    // workgroups of 8 units).
     const int64_t unit_blocks = ((int64_t)max_pages * d->page_size + 15) / 16;
-    const int64_t blocks_upper = (int64_t)p->units * unit_blocks;
     const int64_t resident = (int64_t)cus * per_cu;
-    if (unit_blocks <= 256 && p->units >= resident) {
-      p->nwg = p->units;
-    } else {
-      const int64_t rounds = blocks_upper > resident * 256 ? 2 : 1;
-      p->nwg = (int32_t)(resident * rounds);
-    }
+    if (unit_blocks <= 256 && p->units >= resident) p->nwg = p->units;
+    else p->nwg = (int32_t)resident;
   }
   if (p->nwg > (1 << 24) || p->tiles > 65535) return KVQ_ERR_UNSUPPORTED;
   p->slots = p->units + p->nwg;
@@ -121,10 +117,13 @@ DecodeArgs base_args(const kvq_cache_desc* d, const Plan& p, int32_t batch, int3
   a.seq_lens = seq_lens;
   a.B = batch; a.n_q = n_q; a.H_q = H_q; a.G = H_q / d->num_kv_heads; a.R = p.R;
   a.max_pages = max_pages; a.nwg = p.nwg;
-  // a grid of one resident round only: with more rounds the two
-  // workgroups of a CU are best left staggered (pacing the first round's
-  // younger ones measured 1.5-2% slower for 16 rounds)
-  const bool one_round = p.per_cu >= 2 && (int64_t)p.nwg <= (int64_t)p.cus * p.per_cu;
+  // a grid of one resident round whose units span at least 4 workgroups
+  // each on average: with more rounds the two workgroups of a CU are best
+  // left staggered (pacing the first round's younger ones measured 1.5-2%
+  // slower for 16 rounds), and where a workgroup holds several units
+  // (64 sequences of 1K-128K tokens) the bias measured 0.9% slower
+  const bool one_round = p.per_cu >= 2 && (int64_t)p.nwg <= (int64_t)p.cus * p.per_cu &&
+                         (int64_t)p.units * 4 <= (int64_t)p.nwg;
   a.pace_cus = one_round ? p.cus : 0;
   a.pace_round = one_round ? p.cus * p.per_cu : 0;
   a.qk_scale = softmax_scale * 1.4426950408889634f * (k_tensor_scaled(d->format) ? d->k_scale : 1.0f);

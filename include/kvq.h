@@ -327,9 +327,7 @@ kvq_status kvq_prefill_attention(const kvq_cache_desc* desc, const void* pool, c
  * per (sequence, kv head) unit when a unit holds at most 256 blocks of 16
  * tokens (max_pages_per_seq x page_size / 16) and there are at least as
  * many units as the device holds workgroups at once (CUs x resident
- * workgroups per CU); otherwise one whole round of resident workgroups, or
- * two rounds when the units hold more than 256 blocks per resident
- * workgroup. */
+ * workgroups per CU); otherwise one whole round of resident workgroups. */
 kvq_status kvq_decode_plan(const kvq_cache_desc* desc, int32_t batch, int32_t n_q,
                            int32_t num_q_heads, int32_t max_pages_per_seq,
                            int32_t* num_workgroups, int32_t* num_slots);
