@@ -363,9 +363,10 @@ def prefill_bench(stream, probe, chunk=APPEND_CHUNK, fmt="K8V4", reps=3):
     return res
 
 
-# the sources the split kernel is compiled from
+# the sources the split kernel is compiled from, and the planner that sizes
+# its grid (the partials' bytes depend on the workgroup count)
 SPLIT_SOURCES = ["kvq_decode.hip", "kvq_decode_core.hpp", "kvq_device.hpp", "kvq_encode.hpp", "kvq_format.hpp",
-                 "kvq_internal.hpp"]
+                 "kvq_internal.hpp", "kvq_api.hip"]
 
 
 def kernel_sources_sha():
