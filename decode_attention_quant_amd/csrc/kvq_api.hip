@@ -93,15 +93,9 @@ kvq_status make_plan(const kvq_cache_desc* d, int32_t batch, int32_t n_q, int32_
     // 512 slots spent a third of its time on the last 128), and every
     // further round pays each workgroup's start-up and merge again
     // (measured: two rounds for 32 sequences of 8K-32K tokens were 4-6%
-    // slower than one, 1.3% for 64 of 1K-128K).  Many short units (at most
-    // 256 blocks, at least one per resident workgroup) get one workgroup
-    // each instead: a range that is exactly one unit is a single segment
-    // (measured 1.4% faster for 8192 units of 256 blocks than 1024
-    // workgroups of 8 units).
-    const int64_t unit_blocks = ((int64_t)max_pages * d->page_size + 15) / 16;
-    const int64_t resident = (int64_t)cus * per_cu;
-    if (unit_blocks <= 256 && p->units >= resident) p->nwg = p->units;
-    else p->nwg = (int32_t)resident;
+    // slower than one, 1.3% for 64 of 1K-128K; one workgroup per unit for
+    // 8192 units of 256 blocks, 16 rounds, 1.2% slower than one round).
+    p->nwg = (int32_t)((int64_t)cus * per_cu);
   }
   if (p->nwg > (1 << 24) || p->tiles > 65535) return KVQ_ERR_UNSUPPORTED;
   p->slots = p->units + p->nwg;

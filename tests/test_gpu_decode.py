@@ -274,15 +274,13 @@ def test_scores_that_climb_and_jump(fmt, cfg):
     assert_lse_close(lse, ref_lse, "climbing scores " + W_name(c))
 
 
-def test_planned_grid_is_one_round_or_one_per_unit():
+def test_planned_grid_is_one_round():
     """The planner's grid: one round of resident workgroups (a multiple of
-    the CU count, whatever the cache's size), or one workgroup per unit for
-    many units of at most 256 blocks."""
+    the CU count), whatever the cache's size and its number of units."""
     require_gpu()
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     one, _ = kvq.decode_plan(kvq.desc(3, 256, 64, 4, 4097), 1, 1, 24, 4096)        # 4 units x 16384 blocks
     big, _ = kvq.decode_plan(kvq.desc(3, 256, 64, 4, 16385), 32, 1, 24, 512)       # 128 units x 2048 blocks
+    many, slots = kvq.decode_plan(kvq.desc(5, 128, 128, 32, 8193), 256, 4, 32, 32)  # 8192 units x 256 blocks
     assert one % cus == 0 and one // cus >= 1
-    assert big == one
-    per_unit, slots = kvq.decode_plan(kvq.desc(5, 128, 128, 32, 8193), 256, 4, 32, 32)  # 8192 units x 256 blocks
-    assert per_unit == 256 * 32 and slots == 2 * 256 * 32
+    assert big == one and many == one and slots == 256 * 32 + one
