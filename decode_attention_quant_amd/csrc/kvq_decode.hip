@@ -840,49 +840,46 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
 }
 
 // ----------------------------------------------------------- combine
-// One workgroup of SG x DL threads per (unit, row, column slice), DL =
-// D / (4 NS) threads per slice of D / NS columns; thread (g, c) owns columns
-// 4c .. 4c + 3 of the slice and merges partials g, g + SG, ... with a
-// running maximum, rescaling what it holds when the maximum grows (the same
-// log-sum-exp merge as the split kernel's); the groups then merge through
-// LDS.  The partials are already in the original domain, so a row's slices
-// are independent: a unit split many ways spreads its partials' bytes over
-// NS workgroups.  Units finished by the split kernel (one workgroup,
-// write_direct) are skipped; empty sequences get out = 0, lse = -inf.
+// A (unit, row) item's partials: those of workgroups wa .. wb, whose ranges
+// cover the unit's blocks.  Units finished by the split kernel (one
+// workgroup, write_direct) have nothing to merge; empty sequences get
+// out = 0, lse = -inf.
 
-template <int D, int SG, int NS>
-__global__ __launch_bounds__(SG * D / (4 * NS)) void decode_combine_kernel(DecodeArgs a, int H_kv) {
-  constexpr float NEG_INF = -__builtin_inff();
-  constexpr int DL = D / (4 * NS);  // threads per partial slice (4 columns each)
-  __shared__ float4 sacc[SG][DL];
-  __shared__ float sm[SG], sl[SG];
-  const int tid = threadIdx.x, c = tid % DL, g = tid / DL;
-  const unsigned item = blockIdx.x / (unsigned)NS;
-  const int col0 = (int)(blockIdx.x - item * (unsigned)NS) * (D / NS) + 4 * c;
+struct CombineItem {
+  int64_t orow;     // output row
+  int64_t slot;     // the first partial's slot row, (u + wa) * R + rr
+  int nseg;         // partials to merge; 0: empty sequence, -1: written by the split kernel
+};
+
+__device__ __forceinline__ CombineItem combine_item(const DecodeArgs& a, int H_kv, unsigned item) {
+  CombineItem it;
   const int u = (int)(item / (unsigned)a.R), rr = (int)(item - (unsigned)u * a.R);
   const int b = u / H_kv, h = u - b * H_kv;
   const int qi = rr / a.G, qh = h * a.G + (rr - qi * a.G);
-  const int64_t orow = ((int64_t)b * a.n_q + qi) * a.H_q + qh;
-  const bool lse_writer = col0 == 0;  // thread 0 of slice 0
-  const int L = a.seq_lens[b];
-  const int nb = (L + 15) >> 4;
+  it.orow = ((int64_t)b * a.n_q + qi) * a.H_q + qh;
+  const int nb = (a.seq_lens[b] + 15) >> 4;
   if (nb == 0) {
-    if (tid < DL) *reinterpret_cast<float4*>(a.out + orow * D + col0) = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (a.lse != nullptr && lse_writer && tid == 0) a.lse[orow] = NEG_INF;
-    return;
+    it.slot = 0;
+    it.nseg = 0;
+    return it;
   }
-  const int total = a.ws_cum[a.B];
-  const int per = blocks_per_workgroup(total, a.nwg);
+  const int per = blocks_per_workgroup(a.ws_cum[a.B], a.nwg);
   const int start = a.ws_cum[b] + h * nb;
   const int wa = start / per, wb = (start + nb - 1) / per;
-  if (wa == wb && a.write_direct) return;
-  const float* ml = a.ws_ml + ((int64_t)(u + wa) * a.R + rr) * 2;
-  const float* po = a.ws_o + ((int64_t)(u + wa) * a.R + rr) * D + col0;
-  const int nseg = wb - wa + 1;
-  const int64_t sml = (int64_t)a.R * 2, so = (int64_t)a.R * D;  // slot strides
+  it.slot = (int64_t)(u + wa) * a.R + rr;
+  it.nseg = wa == wb && a.write_direct ? -1 : wb - wa + 1;
+  return it;
+}
 
-  float m = NEG_INF, l = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+// Merges partials g, g + SG, ... < nseg of 4 columns into (m, l, acc) with
+// a running maximum, rescaling what is held when the maximum grows (the
+// same log-sum-exp merge as the split kernel's).  Up to KF partials are in
+// flight per thread: their loads go out together, so a unit split many
+// ways costs about one memory round trip, not one per partial.
+template <int SG>
+__device__ __forceinline__ void merge_partials(const float* ml, const float* po, int nseg, int g, int64_t sml,
+                                               int64_t so, float& m, float& l, float4& acc) {
+  constexpr float NEG_INF = -__builtin_inff();
   auto take = [&](float ms, float ls, float4 o) {
     if (ms == NEG_INF) return;  // a partial that saw no visible key
     if (ms > m) {
@@ -895,9 +892,6 @@ __global__ __launch_bounds__(SG * D / (4 * NS)) void decode_combine_kernel(Decod
     l += w * ls;
     acc.x += w * o.x; acc.y += w * o.y; acc.z += w * o.z; acc.w += w * o.w;
   };
-  // up to KF partials in flight per thread: their loads go out together, so
-  // a unit split many ways costs about one memory round trip, not one per
-  // partial
   constexpr int KF = 8;
   int s = g;
   for (; s + (KF - 1) * SG < nseg; s += KF * SG) {
@@ -912,21 +906,49 @@ __global__ __launch_bounds__(SG * D / (4 * NS)) void decode_combine_kernel(Decod
 #pragma unroll
     for (int i = 0; i < KF; ++i) take(ms[i], ls[i], os[i]);
   }
-  {
-    float ms[KF - 1], ls[KF - 1];
-    float4 os[KF - 1];
+  float ms[KF - 1], ls[KF - 1];
+  float4 os[KF - 1];
 #pragma unroll
-    for (int i = 0; i < KF - 1; ++i) {
-      if (s + i * SG < nseg) {
-        ms[i] = ml[(s + i * SG) * sml];
-        ls[i] = ml[(s + i * SG) * sml + 1];
-        os[i] = *reinterpret_cast<const float4*>(po + (s + i * SG) * so);
-      }
+  for (int i = 0; i < KF - 1; ++i) {
+    if (s + i * SG < nseg) {
+      ms[i] = ml[(s + i * SG) * sml];
+      ls[i] = ml[(s + i * SG) * sml + 1];
+      os[i] = *reinterpret_cast<const float4*>(po + (s + i * SG) * so);
     }
-#pragma unroll
-    for (int i = 0; i < KF - 1; ++i)
-      if (s + i * SG < nseg) take(ms[i], ls[i], os[i]);
   }
+#pragma unroll
+  for (int i = 0; i < KF - 1; ++i)
+    if (s + i * SG < nseg) take(ms[i], ls[i], os[i]);
+}
+
+// One workgroup of SG x DL threads per (unit, row, column slice), DL =
+// D / (4 NS) threads per slice of D / NS columns; thread (g, c) owns columns
+// 4c .. 4c + 3 of the slice and merges partials g, g + SG, ...; the groups
+// then merge through LDS.  The partials are already in the original domain,
+// so a row's slices are independent: a unit split many ways spreads its
+// partials' bytes over NS workgroups.
+
+template <int D, int SG, int NS>
+__global__ __launch_bounds__(SG * D / (4 * NS)) void decode_combine_kernel(DecodeArgs a, int H_kv) {
+  constexpr float NEG_INF = -__builtin_inff();
+  constexpr int DL = D / (4 * NS);  // threads per partial slice (4 columns each)
+  __shared__ float4 sacc[SG][DL];
+  __shared__ float sm[SG], sl[SG];
+  const int tid = threadIdx.x, c = tid % DL, g = tid / DL;
+  const unsigned item = blockIdx.x / (unsigned)NS;
+  const int col0 = (int)(blockIdx.x - item * (unsigned)NS) * (D / NS) + 4 * c;
+  const bool lse_writer = col0 == 0;  // thread 0 of slice 0
+  const CombineItem it = combine_item(a, H_kv, item);
+  if (it.nseg == 0) {
+    if (tid < DL) *reinterpret_cast<float4*>(a.out + it.orow * D + col0) = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (a.lse != nullptr && lse_writer && tid == 0) a.lse[it.orow] = NEG_INF;
+    return;
+  }
+  if (it.nseg < 0) return;
+  float m = NEG_INF, l = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  merge_partials<SG>(a.ws_ml + it.slot * 2, a.ws_o + it.slot * D + col0, it.nseg, g, (int64_t)a.R * 2,
+                     (int64_t)a.R * D, m, l, acc);
 
   sacc[g][c] = acc;
   if (c == 0) { sm[g] = m; sl[g] = l; }
@@ -945,9 +967,39 @@ __global__ __launch_bounds__(SG * D / (4 * NS)) void decode_combine_kernel(Decod
     A.x += w * v.x; A.y += w * v.y; A.z += w * v.z; A.w += w * v.w;
   }
   const float inv = Lt > 0.f ? a.v_out_scale / Lt : 0.f;
-  *reinterpret_cast<float4*>(a.out + orow * D + col0) = make_float4(A.x * inv, A.y * inv, A.z * inv, A.w * inv);
+  *reinterpret_cast<float4*>(a.out + it.orow * D + col0) = make_float4(A.x * inv, A.y * inv, A.z * inv, A.w * inv);
   if (a.lse != nullptr && lse_writer && tid == 0)
-    a.lse[orow] = Lt > 0.f ? (M + __log2f(Lt)) * 0.69314718055994531f : NEG_INF;
+    a.lse[it.orow] = Lt > 0.f ? (M + __log2f(Lt)) * 0.69314718055994531f : NEG_INF;
+}
+
+// Fewer than two partials per unit on average (many units, most finished
+// by the split kernel): 256 threads take 1024 / D rows, one group of D / 4
+// threads per row merging its partials alone, so the launch is not one
+// small workgroup per row.  The result equals decode_combine_kernel's with
+// SG = NS = 1 bit for bit.
+
+template <int D>
+__global__ __launch_bounds__(256) void decode_combine_rows_kernel(DecodeArgs a, int H_kv, int64_t rows) {
+  constexpr float NEG_INF = -__builtin_inff();
+  constexpr int DL = D / 4, RW = 256 / DL;
+  const int tid = threadIdx.x, c = tid % DL;
+  const int64_t item = (int64_t)blockIdx.x * RW + tid / DL;
+  if (item >= rows) return;
+  const CombineItem it = combine_item(a, H_kv, (unsigned)item);
+  float4* out = reinterpret_cast<float4*>(a.out + it.orow * D + 4 * c);
+  if (it.nseg == 0) {
+    *out = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (a.lse != nullptr && c == 0) a.lse[it.orow] = NEG_INF;
+    return;
+  }
+  if (it.nseg < 0) return;
+  float m = NEG_INF, l = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  merge_partials<1>(a.ws_ml + it.slot * 2, a.ws_o + it.slot * D + 4 * c, it.nseg, 0, (int64_t)a.R * 2,
+                    (int64_t)a.R * D, m, l, acc);
+  const float inv = l > 0.f ? a.v_out_scale / l : 0.f;
+  *out = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  if (a.lse != nullptr && c == 0) a.lse[it.orow] = l > 0.f ? (m + __log2f(l)) * 0.69314718055994531f : NEG_INF;
 }
 
 // ----------------------------------------------------------- launchers
@@ -1031,10 +1083,10 @@ hipError_t launch_decode_combine(const Geometry& geo, const DecodeArgs& a, hipSt
   const int64_t units = (int64_t)a.B * geo.H_kv;
   const int64_t rows = units * a.R;
   if (rows == 0) return hipSuccess;
-  // about the partials per unit: up to 16 merged side by side in one
-  // workgroup per row; more (a few long sequences over the whole grid) in
-  // 16 or 32 groups per 64-column slice, so that a row's partials are read
-  // by D / 64 workgroups
+  // about the partials per unit: under 2, several rows per workgroup; up to
+  // 16 merged side by side in one workgroup per row; more (a few long
+  // sequences over the whole grid) in 16 or 32 groups per 64-column slice,
+  // so that a row's partials are read by D / 64 workgroups
   const int64_t expect = a.nwg / units + 1;
 #define KVQ_COMBINE(DD, SG, NS)                                                                        \
   hipLaunchKernelGGL((decode_combine_kernel<DD, SG, NS>), dim3((unsigned)(rows * NS)), dim3(SG * DD / (4 * NS)), 0, \
@@ -1045,7 +1097,8 @@ hipError_t launch_decode_combine(const Geometry& geo, const DecodeArgs& a, hipSt
   else if (expect >= 8) KVQ_COMBINE(DD, 8, 1);                                      \
   else if (expect >= 4) KVQ_COMBINE(DD, 4, 1);                                      \
   else if (expect >= 2) KVQ_COMBINE(DD, 2, 1);                                      \
-  else KVQ_COMBINE(DD, 1, 1);
+  else hipLaunchKernelGGL((decode_combine_rows_kernel<DD>), dim3((unsigned)((rows + 1024 / DD - 1) / (1024 / DD))), \
+                          dim3(256), 0, stream, a, geo.H_kv, rows);
   if (geo.D == 256) { KVQ_COMBINE_D(256) }
   else if (geo.D == 128) { KVQ_COMBINE_D(128) }
   else return hipErrorInvalidValue;
