@@ -42,6 +42,14 @@ struct Plan {
 
 size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
+// What a split workgroup's visit to a further unit costs, in 16-token
+// blocks: the query set-up, the ring's refill and the merge again (measured
+// by clock stamps: 5 us more for workgroups of two units on 32 sequences of
+// 8K-32K tokens, 7-12 us on 64 of 1K-128K in K8V4).  With 24 such blocks
+// between units those splits ran 1.3-1.7% faster; ranges that line up with
+// the units (one 262K sequence) stay as they were.
+constexpr int32_t SEG_COST = 24;
+
 kvq_status check_decode_shape(const kvq_cache_desc* d, int32_t batch, int32_t n_q, int32_t H_q, int32_t max_pages) {
   kvq_status st = check_desc(d);
   if (st != KVQ_OK) return st;
@@ -52,16 +60,14 @@ kvq_status check_decode_shape(const kvq_cache_desc* d, int32_t batch, int32_t n_
   if ((int64_t)max_pages * d->page_size >= ((int64_t)1 << 31) / 16) return KVQ_ERR_UNSUPPORTED;
   // the flat block range and the combine grid stay within int32
   const int64_t units = (int64_t)batch * d->num_kv_heads;
-  if (units * ((int64_t)max_pages * d->page_size / 16) > INT32_MAX) return KVQ_ERR_UNSUPPORTED;
+  if (units * ((int64_t)max_pages * d->page_size / 16 + SEG_COST) > INT32_MAX) return KVQ_ERR_UNSUPPORTED;
   if (units * (H_q / d->num_kv_heads) * n_q > INT32_MAX) return KVQ_ERR_UNSUPPORTED;
   return KVQ_OK;
 }
 
-// num_workgroups = 0: one split workgroup per ~256 token blocks (4096
-// tokens) of the largest problem the arguments allow, and at least as many
-// as fit on the device at once.  Sequences shorter than max_pages leave
-// the trailing workgroups empty (the kernel keeps >= 128 blocks per range).
-// A positive value forces that count.
+// num_workgroups = 0: one round of the workgroups the device holds at
+// once; a positive value forces that count.  Short problems leave some of
+// them empty (the kernel keeps ranges of at least 16-128 blocks).
 kvq_status make_plan(const kvq_cache_desc* d, int32_t batch, int32_t n_q, int32_t H_q, int32_t max_pages,
                      int32_t nwg_req, Plan* p) {
   p->R = (H_q / d->num_kv_heads) * n_q;
@@ -111,6 +117,7 @@ DecodeArgs base_args(const kvq_cache_desc* d, const Plan& p, int32_t batch, int3
   a.seq_lens = seq_lens;
   a.B = batch; a.n_q = n_q; a.H_q = H_q; a.G = H_q / d->num_kv_heads; a.R = p.R;
   a.max_pages = max_pages; a.nwg = p.nwg;
+  a.seg_cost = SEG_COST;
   // a grid of one resident round whose units span at least 4 workgroups
   // each on average: with more rounds the two workgroups of a CU are best
   // left staggered (pacing the first round's younger ones measured 1.5-2%

@@ -8,8 +8,9 @@
 //
 // Schedule (stream-K): the 16-token blocks of every (sequence b, kv head h)
 // unit, u = b * H_kv + h, form one flat range; workgroup x of the grid
-// (x, row tile) takes an equal slice of it (at least 128 blocks), so every
-// workgroup streams the same number of bytes whatever the length mix.  A
+// (x, row tile) takes an equal slice of it, counting a fixed cost for each
+// further unit a slice reaches into, so every workgroup streams about the
+// same number of bytes whatever the length mix.  A
 // unit wholly inside one slice is finished in place (normalized, V rotated
 // back, lse written); a unit cut by slice ends leaves one partial (m, l, o)
 // per slice for decode_combine_kernel.  The rows of a workgroup are the
@@ -102,16 +103,55 @@ __device__ __forceinline__ void store_new_tokens(const NewRows<D>& nr, const Dec
 
 // ----------------------------------------------------------- the kernel
 
-// Blocks per split workgroup: an equal share of the T blocks, but at least
-// ceil(T / 256) clamped to [16, 128], so that when the sequences are shorter
-// than the grid was sized for, about 256 workgroups (one per CU) get longer
-// ranges and the rest find theirs empty, instead of every range shrinking
-// to a few blocks that each leave a partial result.
-__host__ __device__ __forceinline__ int blocks_per_workgroup(int total, int nwg) {
-  const int per = (total + nwg - 1) / nwg;
-  int lo = (total + 255) / 256;
+// The split ranges.  The blocks of all units u = b * H_kv + h in order,
+// with c = DecodeArgs::seg_cost more between one unit and the next, form a
+// line of C = T + c (units - 1) cost positions: a workgroup pays a
+// segment's start-up and merge again for each further unit it visits, so
+// one whose range crosses into the next unit takes about c blocks fewer.
+// Block i of unit (b, h) sits at cost cum[b] + h * nb + c * (b * H_kv + h)
+// + i.  Workgroup w of the `ways` that get work holds the costs
+// [floor(w C / ways), floor((w + 1) C / ways)): exact shares, so that ranges
+// that would line up with the units (c = 0, equal units) still do, the
+// drift staying inside the c positions between two units.
+
+// Workgroups that get work: all of them, unless that leaves fewer than
+// clamp(C / 256, 16, 128) positions each (sequences much shorter than the
+// grid was sized for): then about 256 longer ranges, and the rest empty.
+__host__ __device__ __forceinline__ int split_ways(int64_t C, int nwg) {
+  int64_t lo = (C + 255) / 256;
   lo = lo < 16 ? 16 : (lo > 128 ? 128 : lo);
-  return per > lo ? per : lo;
+  const int64_t ways = (C + lo - 1) / lo;
+  return ways < 1 ? 1 : (ways < nwg ? (int)ways : nwg);
+}
+
+// The first cost position of workgroup w (C for w >= ways).
+__host__ __device__ __forceinline__ int64_t split_range_start(int64_t C, int ways, int w) {
+  return w >= ways ? C : (int64_t)w * C / ways;
+}
+
+// The workgroup that holds cost position y (0 <= y < C).
+__host__ __device__ __forceinline__ int split_range_of(int64_t C, int ways, int64_t y) {
+  return (int)(((y + 1) * ways - 1) / C);
+}
+
+// The blocks at cost positions below y (cum: the prefix table in LDS).
+__device__ __forceinline__ int blocks_before_cost(const int* cum, const int32_t* seq_lens, int B, int H_kv, int c,
+                                                  int64_t y) {
+  // with c positions before every unit, unit 0's too, unit (b, h) spans
+  // [s, s + c + nb), s = cum[b] + c * H_kv * b + h * (nb + c)
+  y += c;
+  const int64_t cb = (int64_t)c * H_kv;
+  if (y >= cum[B] + cb * B) return cum[B];
+  int lo = 0, hi = B;  // cost(lo) <= y < cost(hi), cost(b) = cum[b] + c * H_kv * b
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cum[mid] + cb * mid <= y) lo = mid; else hi = mid;
+  }
+  const int nb = (as_const(seq_lens)[lo] + 15) >> 4;  // nb + c > 0: sequence lo spans y
+  const int r = (int)(y - (cum[lo] + cb * lo));
+  const int h = r / (nb + c);
+  const int off = r - h * (nb + c) - c;
+  return cum[lo] + h * nb + (off > 0 ? off : 0);
 }
 
 // LDS layout of the split kernel: prefix table int [B + 1] (rounded to 16),
@@ -199,9 +239,11 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(Geometry geo, Deco
   const int total = cum[a.B];
   if (w == 0 && rt == 0)
     for (int i = threadIdx.x; i <= a.B; i += 256) a.ws_cum[i] = cum[i];
-  const int per = blocks_per_workgroup(total, a.nwg);
-  int x = w * per;
-  const int x_end = min(total, x + per);
+  const int units = a.B * geo.H_kv;
+  const int64_t C = total + (int64_t)a.seg_cost * (units > 1 ? units - 1 : 0);
+  const int ways = split_ways(C, a.nwg);
+  int x = blocks_before_cost(cum, a.seq_lens, a.B, geo.H_kv, a.seg_cost, split_range_start(C, ways, w));
+  const int x_end = blocks_before_cost(cum, a.seq_lens, a.B, geo.H_kv, a.seg_cost, split_range_start(C, ways, w + 1));
 
   while (x < x_end) {
     // ---- the unit that holds flat block x: b = last index with cum[b] <= x
@@ -863,9 +905,11 @@ __device__ __forceinline__ CombineItem combine_item(const DecodeArgs& a, int H_k
     it.nseg = 0;
     return it;
   }
-  const int per = blocks_per_workgroup(a.ws_cum[a.B], a.nwg);
-  const int start = a.ws_cum[b] + h * nb;
-  const int wa = start / per, wb = (start + nb - 1) / per;
+  const int c = a.seg_cost, units = a.B * H_kv;
+  const int64_t C = a.ws_cum[a.B] + (int64_t)c * (units > 1 ? units - 1 : 0);
+  const int ways = split_ways(C, a.nwg);
+  const int64_t start = a.ws_cum[b] + h * nb + (int64_t)c * u;  // cost position of the unit's block 0
+  const int wa = split_range_of(C, ways, start), wb = split_range_of(C, ways, start + nb - 1);
   it.slot = (int64_t)(u + wa) * a.R + rr;
   it.nseg = wa == wb && a.write_direct ? -1 : wb - wa + 1;
   return it;

@@ -25,6 +25,7 @@ struct DecodeArgs {
   int32_t B, n_q, H_q, G, R;  // G = H_q / H_kv, R = G * n_q rows per kv head
   int32_t max_pages;
   int32_t nwg;                // workgroups of the split kernel
+  int32_t seg_cost;           // blocks each unit adds to the cost the split ranges share equally
   float qk_scale;             // softmax_scale * log2(e) (* k_scale for FP8_TENSOR)
   float v_out_scale;          // v_scale for FP8_TENSOR, else 1
   int32_t* ws_cum;            // [B + 1]: H_kv * (blocks of sequences 0..b-1), written by workgroup 0

@@ -249,9 +249,14 @@ kvq_status kvq_decode_step(const kvq_cache_desc* desc, void* pool, const void* k
  * sequence's pages) or time them apart.
  *
  * Schedule: the 16-token blocks of all (sequence b, kv head h) units, in
- * unit order u = b * num_kv_heads + h, form one range of T blocks;
- * split workgroup w takes blocks [w * per, (w + 1) * per),
- * per = max(ceil(T / num_workgroups), min(max(ceil(T / 256), 16), 128)).
+ * unit order u = b * num_kv_heads + h, with 24 positions between one unit
+ * and the next (what a workgroup's visit to a further unit costs), form a
+ * line of C = T + 24 (units - 1) positions, T the blocks: block i of unit u
+ * sits at position cum_u + 24 u + i, cum_u the blocks of the units before u.
+ * Of the ways = min(num_workgroups, ceil(C / lo)) split workgroups that get
+ * work, lo = min(max(ceil(C / 256), 16), 128), workgroup w takes the blocks
+ * at positions [floor(w C / ways), floor((w + 1) C / ways)); the others
+ * take none.
  * kvq_decode_split writes, for every unit u and every workgroup w that
  * covers part of it, one partial per row r = i * G + j
  * (query token i, j-th query head of the group) into slot u + w:

@@ -176,6 +176,75 @@ def test_workgroup_sweep_and_phases(fmt, cfg):
             assert_lse_close(lse.cpu().numpy(), ref_lse, "%s nwg=%d flags=%d" % (fmt, nwg, flags))
 
 
+def merge_documented_partials(ws, c, nwg, seg_cost=24):
+    """Merge the split phase's partials as kvq.h documents them: the schedule
+    (units' blocks with seg_cost positions between units, exact shares over
+    the workgroups that get work), slot u + w per (unit, workgroup), and the
+    (m, l, o) layout of the workspace."""
+    B, H, D = c.B, c.H_kv, c.D
+    G = c.H_q // H
+    R = G * c.n_q
+    units = B * H
+    slots = units + nwg
+    a256 = lambda n: (n + 255) // 256 * 256
+    raw = ws.cpu().numpy()
+    cum = raw[: 4 * (B + 1)].view(np.int32)
+    o_ml = a256(4 * (B + 1))
+    ml = raw[o_ml: o_ml + 8 * slots * R].view(np.float32).reshape(slots, R, 2)
+    o_o = o_ml + a256(8 * slots * R)
+    o = raw[o_o: o_o + 4 * slots * R * D].view(np.float32).reshape(slots, R, D)
+    T = int(cum[B])
+    C = T + seg_cost * max(units - 1, 0)
+    lo = min(max((C + 255) // 256, 16), 128)
+    ways = max(1, min((C + lo - 1) // lo, nwg))
+    owner = lambda y: ((y + 1) * ways - 1) // C
+    out = np.zeros((B, c.n_q, c.H_q, D))
+    lse = np.full((B, c.n_q, c.H_q), -np.inf)
+    for b in range(B):
+        nb = (int(c.seq_lens[b]) + 15) // 16
+        assert cum[b] == H * sum((int(L) + 15) // 16 for L in c.seq_lens[:b])
+        for h in range(H):
+            if nb == 0:
+                continue
+            u = b * H + h
+            start = int(cum[b]) + h * nb + seg_cost * u
+            ws_ = range(owner(start), owner(start + nb - 1) + 1)
+            for r in range(R):
+                m = np.array([ml[u + w, r, 0] for w in ws_], np.float64)
+                l = np.array([ml[u + w, r, 1] for w in ws_], np.float64)
+                ov = np.array([o[u + w, r] for w in ws_], np.float64)
+                M = m.max()
+                f = np.where(np.isneginf(m), 0.0, np.exp2(m - M))
+                L = (f * l).sum()
+                i, j = divmod(r, G)
+                out[b, i, h * G + j] = (f[:, None] * ov).sum(0) / L
+                lse[b, i, h * G + j] = (M + np.log2(L)) * np.log(2.0)
+    return out, lse
+
+
+@pytest.mark.parametrize("fmt,cfg,lens", [("K8V4", 4, [900, 450, 77, 0, 1]), ("MXFP8", 5, [1100, 450, 77])])
+def test_partials_follow_the_documented_schedule(fmt, cfg, lens):
+    """The partials a caller may merge itself sit where the header says:
+    merged here by that description alone (numpy), they give the oracle's
+    attention, for forced and planned workgroup counts.  (Formats without a
+    per-tensor V scale, which the combine applies when it normalizes.)"""
+    c = W.make_case(cfg, fmt, device="cpu", B=len(lens), lengths=lens)
+    bl = build(c)
+    ref, ref_lse = oracle_attention(bl)
+    q = c.q.cuda()
+    planned, _ = kvq.decode_plan(bl.desc, c.B, c.n_q, c.H_q, c.max_pages)
+    for nwg in (1, 5, 37, 333, 0):
+        ws = kvq.alloc_workspace(kvq.workspace_size(bl.desc, c.B, c.n_q, c.H_q, c.max_pages, nwg))
+        ws.fill_(0xFF)
+        note("documented partials", fmt, "nwg", nwg)
+        kvq.decode_split(bl.desc, bl.pool_gpu, q, bl.bt, bl.sl, c.softmax_scale, ws, num_workgroups=nwg, flags=0)
+        torch.cuda.synchronize()
+        out, lse = merge_documented_partials(ws, c, nwg or planned)
+        live = np.asarray(c.seq_lens) > 0
+        assert_close(out[live], ref[live], "%s nwg=%d" % (fmt, nwg))
+        assert_lse_close(lse[live], ref_lse[live], "%s nwg=%d" % (fmt, nwg))
+
+
 @pytest.mark.parametrize("fmt,cfg", [("K8V4", 4), ("FP8_ROW", 2)])
 def test_deterministic_and_permutation_invariant(fmt, cfg):
     lens = [700, 300, 65]
