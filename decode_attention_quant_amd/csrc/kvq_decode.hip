@@ -899,16 +899,19 @@ __device__ __forceinline__ CombineItem combine_item(const DecodeArgs& a, int H_k
   const int b = u / H_kv, h = u - b * H_kv;
   const int qi = rr / a.G, qh = h * a.G + (rr - qi * a.G);
   it.orow = ((int64_t)b * a.n_q + qi) * a.H_q + qh;
-  const int nb = (a.seq_lens[b] + 15) >> 4;
+  // the sequence's blocks come from the split kernel's prefix table, so the
+  // three loads go out together instead of one after seq_lens[b]
+  const int cb = a.ws_cum[b], cb1 = a.ws_cum[b + 1], total = a.ws_cum[a.B];
+  const int nb = (cb1 - cb) / H_kv;
   if (nb == 0) {
     it.slot = 0;
     it.nseg = 0;
     return it;
   }
   const int c = a.seg_cost, units = a.B * H_kv;
-  const int64_t C = a.ws_cum[a.B] + (int64_t)c * (units > 1 ? units - 1 : 0);
+  const int64_t C = total + (int64_t)c * (units > 1 ? units - 1 : 0);
   const int ways = split_ways(C, a.nwg);
-  const int64_t start = a.ws_cum[b] + h * nb + (int64_t)c * u;  // cost position of the unit's block 0
+  const int64_t start = cb + h * nb + (int64_t)c * u;  // cost position of the unit's block 0
   const int wa = split_range_of(C, ways, start), wb = split_range_of(C, ways, start + nb - 1);
   it.slot = (int64_t)(u + wa) * a.R + rr;
   it.nseg = wa == wb && a.write_direct ? -1 : wb - wa + 1;

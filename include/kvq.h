@@ -270,7 +270,9 @@ kvq_status kvq_decode_step(const kvq_cache_desc* desc, void* pool, const void* k
  *   rotated V planes back: NVFP4_G16, K8V4, MXFP4).
  * kvq_decode_combine merges each unit's partials, normalizes and writes
  * out / lse exactly as kvq_decode_attention does; pass the same
- * num_workgroups (0 = planned) and flags to both.
+ * num_workgroups (0 = planned) and flags to both.  It takes the sequences'
+ * block counts from the workspace's cum table, which the split phase
+ * wrote, so seq_lens must be the split's.
  * flags & KVQ_SPLIT_WRITE_WHOLE_UNITS: a unit held entirely by one split
  * workgroup is finished by the split phase (written to out / lse, which
  * kvq_decode_split then needs) and the combine skips it; this is what
