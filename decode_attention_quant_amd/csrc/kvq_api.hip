@@ -67,7 +67,7 @@ kvq_status check_decode_shape(const kvq_cache_desc* d, int32_t batch, int32_t n_
 
 // num_workgroups = 0: one round of the workgroups the device holds at
 // once; a positive value forces that count.  Short problems leave some of
-// them empty (the kernel keeps ranges of at least 16-128 blocks).
+// them empty (the kernel keeps ranges of at least 4-128 blocks).
 kvq_status make_plan(const kvq_cache_desc* d, int32_t batch, int32_t n_q, int32_t H_q, int32_t max_pages,
                      int32_t nwg_req, Plan* p) {
   p->R = (H_q / d->num_kv_heads) * n_q;

@@ -254,7 +254,7 @@ kvq_status kvq_decode_step(const kvq_cache_desc* desc, void* pool, const void* k
  * line of C = T + 24 (units - 1) positions, T the blocks: block i of unit u
  * sits at position cum_u + 24 u + i, cum_u the blocks of the units before u.
  * Of the ways = min(num_workgroups, ceil(C / lo)) split workgroups that get
- * work, lo = min(max(ceil(C / 256), 16), 128), workgroup w takes the blocks
+ * work, lo = min(max(ceil(C / 256), 4), 128), workgroup w takes the blocks
  * at positions [floor(w C / ways), floor((w + 1) C / ways)); the others
  * take none.
  * kvq_decode_split writes, for every unit u and every workgroup w that

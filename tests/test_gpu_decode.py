@@ -195,7 +195,7 @@ def merge_documented_partials(ws, c, nwg, seg_cost=24):
     o = raw[o_o: o_o + 4 * slots * R * D].view(np.float32).reshape(slots, R, D)
     T = int(cum[B])
     C = T + seg_cost * max(units - 1, 0)
-    lo = min(max((C + 255) // 256, 16), 128)
+    lo = min(max((C + 255) // 256, 4), 128)
     ways = max(1, min((C + lo - 1) // lo, nwg))
     owner = lambda y: ((y + 1) * ways - 1) // C
     out = np.zeros((B, c.n_q, c.H_q, D))
