@@ -27,6 +27,7 @@ CASES = [
     (2, "FP8_ROW"),
     (2, "FP8_TENSOR"),
     (3, "NVFP4_G16"),
+    (3, "NVFP4_G16/2L"),  # calibrated per-tensor second-level scales
     (3, "MXFP4"),
     ("3b", "NVFP4_G16"),
     (4, "K8V4"),
@@ -74,10 +75,11 @@ def oracle_unit(c, geo, pool, b, h, q_mxfp8=False):
     return OA.attend(q, K, V, c.softmax_scale, c.n_q)
 
 
-def run_full(cfg, fmt, flags=0):
+def run_full(cfg, label, flags=0):
     require_gpu()
-    note("full-size case", cfg, fmt)
-    c = W.make_case(cfg, fmt, device="cuda")
+    note("full-size case", cfg, label)
+    fmt, _, mod = label.partition("/")
+    c = W.make_case(cfg, fmt, device="cuda", two_level=mod == "2L")
     geo = OL.Geometry(c.fmt, c.D, c.P, c.H_kv)
     d = kvq.desc(c.fmt, c.D, c.P, c.H_kv, c.num_pages, c.k_scale, c.v_scale)
     pool = kvq.alloc_pool(d)
