@@ -422,12 +422,22 @@ SPLIT_SOURCES = ["kvq_decode.hip", "kvq_decode_core.hpp", "kvq_device.hpp", "kvq
                  "kvq_internal.hpp", "kvq_api.hip"]
 
 
+def _code_only(text):
+    """C++ source without its comments and blank lines: an edit of the prose
+    alone leaves the recorded counters valid."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip())
+
+
 def kernel_sources_sha():
+    """SHA-256 of the split kernel's sources (code only, comments dropped)."""
     h = hashlib.sha256()
     for f in SPLIT_SOURCES:
         h.update(f.encode())
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()
 
 

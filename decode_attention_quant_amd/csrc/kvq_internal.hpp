@@ -11,8 +11,10 @@ namespace kvq {
 //
 // Work is scheduled stream-K style: the token blocks (16 tokens) of every
 // (sequence b, kv head h) unit, units in order u = b * H_kv + h, form one
-// flat range of T blocks; workgroup w of the split kernel takes blocks
-// [w * per, (w + 1) * per), per = ceil(T / nwg).  A unit wholly inside one
+// flat range of T blocks; workgroup w of the split kernel takes a
+// contiguous run of it, an equal share of a cost that adds seg_cost blocks
+// between one unit and the next (split_ways and blocks_before_cost in the
+// split kernel's source give the exact ranges).  A unit wholly inside one
 // workgroup's range can be finished there; a unit spread over workgroups
 // w_a..w_b leaves one partial (m, l, o) per workgroup, in slot u + w (the
 // pairs (u, w) visited form a monotone staircase, so u + w is unique), and
