@@ -13,6 +13,7 @@ import torch
 import decode_attention_quant_amd as kvq
 import workloads as W
 from _gpu_common import (assert_close, assert_lse_close, build, note, oracle_attention, require_gpu, W_name)
+import _schedule as S
 
 pytestmark = pytest.mark.gpu
 
@@ -176,7 +177,7 @@ def test_workgroup_sweep_and_phases(fmt, cfg):
             assert_lse_close(lse.cpu().numpy(), ref_lse, "%s nwg=%d flags=%d" % (fmt, nwg, flags))
 
 
-def merge_documented_partials(ws, c, nwg, seg_cost=24):
+def merge_documented_partials(ws, c, nwg, seg_cost=S.SEG_COST):
     """Merge the split phase's partials as kvq.h documents them: the schedule
     (units' blocks with seg_cost positions between units, exact shares over
     the workgroups that get work), slot u + w per (unit, workgroup), and the
@@ -195,9 +196,8 @@ def merge_documented_partials(ws, c, nwg, seg_cost=24):
     o = raw[o_o: o_o + 4 * slots * R * D].view(np.float32).reshape(slots, R, D)
     T = int(cum[B])
     C = T + seg_cost * max(units - 1, 0)
-    lo = min(max((C + 255) // 256, 4), 128)
-    ways = max(1, min((C + lo - 1) // lo, nwg))
-    owner = lambda y: ((y + 1) * ways - 1) // C
+    n = S.ways(C, nwg)
+    owner = lambda y: S.owner(C, n, y)
     out = np.zeros((B, c.n_q, c.H_q, D))
     lse = np.full((B, c.n_q, c.H_q), -np.inf)
     for b in range(B):
